@@ -1,0 +1,154 @@
+"""Thin torch-facing binding of libhq: the same entry points as include/hq.h.
+
+Each function only marshals arguments (tensor -> pointer, current HIP stream,
+optional output allocation with ``torch.empty``) and calls the C ABI; every
+step of the computation runs in the library's HIP kernels. Errors come back as
+``HQInvalidArgument`` (ValueError), ``HQUnsupportedDevice``
+(NotImplementedError) or ``HQLaunchError``.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (HQ_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANNEL, HQ_PER_TENSOR,
+                   HQ_PER_TOKEN, check, hq_ring, load)
+
+__all__ = [
+    "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
+    "hq_quantize_fp8", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
+    "hq_grouped_gemm_a8w8", "hq_last_error",
+]
+
+_XT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device, stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def hq_last_error() -> str:
+    return load().hq_last_error().decode(errors="replace")
+
+
+def hq_scale_count(gran: int, rows: int, cols: int) -> int:
+    return int(load().hq_scale_count(gran, rows, cols))
+
+
+def hq_quantize_workspace_bytes(gran: int, rows: int, cols: int) -> int:
+    return int(load().hq_quantize_workspace_bytes(gran, rows, cols))
+
+
+def hq_preshuffled_bytes(n: int, k: int) -> int:
+    return int(load().hq_preshuffled_bytes(n, k))
+
+
+class Ring:
+    """Device state of a delayed-scaling amax-history ring.
+
+    ``state`` is float32 [length + 2] = [hist | scale | counter], initialised to
+    hist = 0, scale = 1, counter = 0; ``flag`` is the sticky int32 non-finite flag.
+    """
+
+    def __init__(self, length: int = 16, margin: int = 0, device="cuda"):
+        self.length = int(length)
+        self.margin = int(margin)
+        self.state = torch.zeros(self.length + 2, dtype=torch.float32, device=device)
+        self.state[self.length] = 1.0
+        self.flag = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def c_struct(self, idx: int) -> hq_ring:
+        return hq_ring(self.state.data_ptr(), self.length, int(idx), self.margin, self.flag.data_ptr())
+
+
+def hq_quantize_fp8(x: torch.Tensor, fmt: int = HQ_E4M3, gran: int = HQ_PER_TOKEN, *,
+                    ring: Ring | None = None, ring_idx: int = 0, q=None, scale_out=None,
+                    amax_out=None, workspace=None, stream=None):
+    """Quantize a 2-D bf16/fp32 tensor; returns (q uint8, scale_out fp32, amax_out fp32)."""
+    if x.dtype not in _XT:
+        raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    x = x.contiguous()
+    rows, cols = x.shape
+    lib = load()
+    count = max(int(lib.hq_scale_count(gran, rows, cols)), 0)
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scale_out is None:
+        scale_out = torch.empty(count, dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty(count, dtype=torch.float32, device=dev)
+    need = int(lib.hq_quantize_workspace_bytes(gran, rows, cols))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ring_c = ctypes.byref(ring.c_struct(ring_idx)) if ring is not None else None
+    st = lib.hq_quantize_fp8(_ptr(x), _XT[x.dtype], rows, cols, fmt, gran, _ptr(q), _ptr(scale_out),
+                             _ptr(amax_out), ring_c, _ptr(workspace), ws_bytes, _stream(dev, stream))
+    check(st)
+    return q, scale_out, amax_out
+
+
+def hq_scale_ring_update(ring: Ring, amax: torch.Tensor, fmt: int = HQ_E4M3, ring_idx: int = 0,
+                         stream=None) -> None:
+    """Fold a device float32 amax scalar into the ring and publish the next scale."""
+    lib = load()
+    st = lib.hq_scale_ring_update(ctypes.byref(ring.c_struct(ring_idx)), _ptr(amax), fmt,
+                                  _stream(ring.state.device, stream))
+    check(st)
+
+
+def hq_preshuffle_weight(wq: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Pre-shuffle FP8 codes WQ [n, k] (uint8); returns the flat uint8 buffer."""
+    if wq.dim() != 2:
+        raise ValueError("wq must be 2-D [n, k]")
+    wq = wq.contiguous()
+    n, k = wq.shape
+    lib = load()
+    nbytes = int(lib.hq_preshuffled_bytes(n, k))
+    if out is None:
+        out = torch.empty(max(nbytes, 0), dtype=torch.uint8, device=wq.device)
+    check(lib.hq_preshuffle_weight(_ptr(wq), n, k, _ptr(out), _stream(wq.device, stream)))
+    return out
+
+
+def hq_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_scale: torch.Tensor,
+                 w_scale: torch.Tensor, n: int, out=None, stream=None) -> torch.Tensor:
+    """out[m, n] = bf16(x_scale[m] * w_scale[n] * sum_k XQ[m,k] WQ[n,k]); returns out."""
+    xq = xq.contiguous()
+    m, k = xq.shape
+    x_scale = x_scale.contiguous()
+    w_scale = w_scale.contiguous()
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    check(load().hq_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                              _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out),
+                              _stream(xq.device, stream)))
+    return out
+
+
+def hq_grouped_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
+                         x_scale: torch.Tensor, w_scale: torch.Tensor, group_offsets: torch.Tensor,
+                         num_experts: int, n: int, out=None, stream=None) -> torch.Tensor:
+    """Per-expert GEMM over row ranges [offsets[e], offsets[e+1]); returns out [T, n]."""
+    xq = xq.contiguous()
+    t, k = xq.shape
+    x_scale = x_scale.contiguous()
+    w_scale = w_scale.contiguous()
+    group_offsets = group_offsets.contiguous()
+    if out is None:
+        out = torch.empty((t, n), dtype=torch.bfloat16, device=xq.device)
+    check(load().hq_grouped_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                                      _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
+                                      int(num_experts), t, n, k, _ptr(out),
+                                      _stream(xq.device, stream)))
+    return out

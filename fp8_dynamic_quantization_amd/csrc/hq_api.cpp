@@ -1,0 +1,336 @@
+// C ABI of libhq: argument validation, the gfx950 gate and kernel dispatch.
+//
+// Order of checks (aiter PR "gemm_a8w8_bpreshuffle_out", Technical Details):
+// every argument check runs on the host before any launch and reports
+// HQ_ERR_INVALID_ARGUMENT; then the architecture check (gfx950 only, cached per
+// device under a mutex as AstrAI's ops.cu caches its capability check); empty
+// problems return HQ_OK without a launch. The memory-safety list of the
+// hip-quant README ("Memory Safety": checked narrowing, grid limits, empty
+// tensors) is applied to every entry point.
+#include "hq.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "hq_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hq_status fail(hq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hq_status ok() {
+  g_err.clear();
+  return HQ_OK;
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+// Returns the name pair of the first overlapping ranges, or nullptr.
+const char* find_overlap(const Range* r, int n, const char** other) {
+  for (int i = 0; i < n; ++i) {
+    if (!r[i].p || !r[i].bytes) continue;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(r[i].p), a1 = a0 + r[i].bytes;
+    for (int j = i + 1; j < n; ++j) {
+      if (!r[j].p || !r[j].bytes) continue;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(r[j].p), b1 = b0 + r[j].bytes;
+      if (a0 < b1 && b0 < a1) {
+        *other = r[j].name;
+        return r[i].name;
+      }
+    }
+  }
+  return nullptr;
+}
+
+// gfx950 gate for the current device, cached per device.
+hq_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(HQ_ERR_UNSUPPORTED_DEVICE, "no HIP device is available (libhq requires an MI355X / gfx950)");
+  }
+  static std::mutex mu;
+  static std::unordered_map<int, bool> cache;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) {
+      if (!it->second) return fail(HQ_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+      return HQ_OK;
+    }
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(HQ_ERR_UNSUPPORTED_DEVICE, "cannot query HIP device %d", dev);
+  }
+  const bool is950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                     (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    cache.emplace(dev, is950);
+  }
+  if (!is950) return fail(HQ_ERR_UNSUPPORTED_DEVICE, "device %d is %s, libhq requires gfx950", dev, prop.gcnArchName);
+  return HQ_OK;
+}
+
+hq_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HQ_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_fmt(int f) { return f == HQ_E4M3 || f == HQ_E5M2; }
+
+int64_t padded_bytes(int64_t n, int64_t k) { return ((n + 15) / 16 * 16) * ((k + 127) / 128 * 128); }
+
+hq_status check_ring(const hq_ring* ring) {
+  if (!ring->state) return fail(HQ_ERR_INVALID_ARGUMENT, "ring->state is NULL");
+  if (!aligned(ring->state, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "ring->state must be 4-byte aligned");
+  if (ring->len < 1 || ring->len > (1 << 20)) return fail(HQ_ERR_INVALID_ARGUMENT, "ring->len must be in [1, 2^20], got %d", ring->len);
+  if (ring->idx < 0 || ring->idx >= ring->len)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "ring->idx must be in [0, len), got %d (len %d)", ring->idx, ring->len);
+  if (ring->margin < -64 || ring->margin > 64)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "ring->margin must be in [-64, 64], got %d", ring->margin);
+  if (ring->nonfinite_flag && !aligned(ring->nonfinite_flag, 4))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "ring->nonfinite_flag must be 4-byte aligned");
+  return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hq_last_error(void) { return g_err.c_str(); }
+
+int64_t hq_scale_count(int gran, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return -1;
+  switch (gran) {
+    case HQ_PER_TENSOR: return 1;
+    case HQ_PER_TOKEN: return rows;
+    case HQ_PER_CHANNEL: return cols;
+    default: return -1;
+  }
+}
+
+size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || rows > kI32Max || cols > kI32Max) return 0;
+  switch (gran) {
+    case HQ_PER_TENSOR: return (size_t)hq::kMaxTensorPartials * 4;
+    case HQ_PER_TOKEN: return 0;
+    case HQ_PER_CHANNEL: return (size_t)hq::col_chunks((int)rows) * (size_t)cols * 4;
+    default: return 0;
+  }
+}
+
+int64_t hq_preshuffled_bytes(int64_t n, int64_t k) {
+  if (n < 0 || k < 0 || n > kI32Max || k > kI32Max) return -1;
+  return padded_bytes(n, k);
+}
+
+hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int fmt, int gran, uint8_t* q,
+                          float* scale_out, float* amax_out, const hq_ring* ring, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
+  if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
+  if (gran != HQ_PER_TENSOR && gran != HQ_PER_TOKEN && gran != HQ_PER_CHANNEL)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "unknown granularity %d", gran);
+  if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
+  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
+  if (ring) {
+    if (gran != HQ_PER_TENSOR) return fail(HQ_ERR_INVALID_ARGUMENT, "a delayed-scaling ring requires HQ_PER_TENSOR");
+    hq_status st = check_ring(ring);
+    if (st != HQ_OK) return st;
+  }
+  if (gran == HQ_PER_CHANNEL && hq::col_chunks((int)rows) > 65535)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "per-channel quantization supports at most %d rows", 65535 * hq::kColChunkRows);
+  if (rows == 0) return ok();
+  if (!x || !q || !scale_out) return fail(HQ_ERR_INVALID_ARGUMENT, "x, q and scale_out must be non-NULL");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "x and q must be 16-byte aligned");
+  if (!aligned(scale_out, 4) || (amax_out && !aligned(amax_out, 4)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scale_out and amax_out must be 4-byte aligned");
+  const size_t need = ring ? (size_t)hq::kMaxTensorPartials * 4 : hq_quantize_workspace_bytes(gran, rows, cols);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HQ_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                  workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "workspace must be 4-byte aligned");
+  }
+  const size_t numel = (size_t)rows * (size_t)cols;
+  const size_t nscale = (size_t)hq_scale_count(gran, rows, cols);
+  const Range rg[] = {
+      {x, numel * (xt == HQ_BF16 ? 2 : 4), "x"},
+      {q, numel, "q"},
+      {scale_out, nscale * 4, "scale_out"},
+      {amax_out, amax_out ? nscale * 4 : 0, "amax_out"},
+      {workspace, need, "workspace"},
+      {ring ? ring->state : nullptr, ring ? ((size_t)ring->len + 2) * 4 : 0, "ring->state"},
+      {ring ? ring->nonfinite_flag : nullptr, ring && ring->nonfinite_flag ? 4u : 0u, "ring->nonfinite_flag"},
+  };
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 7, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  hipError_t e;
+  if (ring) {
+    e = hq::launch_quant_delayed(x, xt, numel, fmt, q, scale_out, amax_out, ring->state, ring->len, ring->idx,
+                                 ring->margin, ring->nonfinite_flag, workspace, stream);
+  } else if (gran == HQ_PER_TOKEN) {
+    e = hq::launch_quant_rows(x, xt, (int)rows, (int)cols, fmt, q, scale_out, amax_out, stream);
+  } else if (gran == HQ_PER_TENSOR) {
+    e = hq::launch_quant_tensor(x, xt, numel, fmt, q, scale_out, amax_out, workspace, stream);
+  } else {
+    e = hq::launch_quant_cols(x, xt, (int)rows, (int)cols, fmt, q, scale_out, amax_out, workspace, stream);
+  }
+  return launched(e, "hq_quantize_fp8");
+}
+
+hq_status hq_scale_ring_update(const hq_ring* ring, const float* amax, int fmt, hipStream_t stream) {
+  if (!ring) return fail(HQ_ERR_INVALID_ARGUMENT, "ring is NULL");
+  if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
+  hq_status st = check_ring(ring);
+  if (st != HQ_OK) return st;
+  if (!amax || !aligned(amax, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "amax must be a non-NULL, 4-byte aligned device float");
+  const Range rg[] = {
+      {ring->state, ((size_t)ring->len + 2) * 4, "ring->state"},
+      {amax, 4, "amax"},
+      {ring->nonfinite_flag, ring->nonfinite_flag ? 4u : 0u, "ring->nonfinite_flag"},
+  };
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 3, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  return launched(hq::launch_ring_update(ring->state, ring->len, ring->idx, ring->margin, ring->nonfinite_flag, amax,
+                                         fmt, stream),
+                  "hq_scale_ring_update");
+}
+
+hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k, uint8_t* wq_pre, hipStream_t stream) {
+  if (n < 0 || n > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31), got %lld", (long long)n);
+  if (k < 16 || k > kI32Max || k % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16 below 2^31, got %lld", (long long)k);
+  if ((double)padded_bytes(n, k) / 16.0 / 256.0 > (double)kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "weight too large");
+  if (n == 0) return ok();
+  if (!wq || !wq_pre) return fail(HQ_ERR_INVALID_ARGUMENT, "wq and wq_pre must be non-NULL");
+  if (!aligned(wq, 16) || !aligned(wq_pre, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "wq and wq_pre must be 16-byte aligned");
+  const Range rg[] = {{wq, (size_t)n * (size_t)k, "wq"}, {wq_pre, (size_t)padded_bytes(n, k), "wq_pre"}};
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 2, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  return launched(hq::launch_preshuffle(wq, (int)n, (int)k, wq_pre, stream), "hq_preshuffle_weight");
+}
+
+static hq_status check_gemm_common(int xf, int wf, int64_t m, int64_t n, int64_t k) {
+  if (!valid_fmt(xf) || !valid_fmt(wf)) return fail(HQ_ERR_INVALID_ARGUMENT, "xf and wf must be HQ_E4M3 or HQ_E5M2");
+  if (m < 0 || m > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "m must be in [0, 2^31), got %lld", (long long)m);
+  if (n < 0 || n > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31), got %lld", (long long)n);
+  if (k < 16 || k > kI32Max || k % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16 below 2^31, got %lld", (long long)k);
+  if ((double)((m + 127) / 128) * (double)((n + 127) / 128) > 1.0e9)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "output too large for one launch");
+  return HQ_OK;
+}
+
+hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                       int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m, int64_t n,
+                       int64_t k, uint16_t* out, hipStream_t stream) {
+  hq_status st = check_gemm_common(xf, wf, m, n, k);
+  if (st != HQ_OK) return st;
+  if (x_scale_count != 1 && x_scale_count != m)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "x_scale_count must be 1 or m (%lld), got %lld", (long long)m, (long long)x_scale_count);
+  if (w_scale_count != 1 && w_scale_count != n)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "w_scale_count must be 1 or n (%lld), got %lld", (long long)n, (long long)w_scale_count);
+  if (m == 0 || n == 0) return ok();
+  if (!xq || !wq_pre || !x_scale || !w_scale || !out)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scale, w_scale and out must be non-NULL");
+  if (!aligned(xq, 16) || !aligned(wq_pre, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "xq and wq_pre must be 16-byte aligned");
+  if (!aligned(out, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+  const Range rg[] = {
+      {out, (size_t)m * (size_t)n * 2, "out"},
+      {xq, (size_t)m * (size_t)k, "xq"},
+      {wq_pre, (size_t)padded_bytes(n, k), "wq_pre"},
+      {x_scale, (size_t)x_scale_count * 4, "x_scale"},
+      {w_scale, (size_t)w_scale_count * 4, "w_scale"},
+  };
+  const char* other = nullptr;
+  const char* a = find_overlap(rg, 5, &other);
+  if (a && (strcmp(a, "out") == 0)) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
+  st = check_device();
+  if (st != HQ_OK) return st;
+  hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1};
+  (void)hipGetLastError();
+  return launched(hq::launch_gemm(g, xf, wf, stream), "hq_gemm_a8w8");
+}
+
+hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                               int64_t x_scale_count, const float* w_scale, int64_t w_scale_count,
+                               const int32_t* group_offsets, int32_t num_experts, int64_t total_rows, int64_t n,
+                               int64_t k, uint16_t* out, hipStream_t stream) {
+  hq_status st = check_gemm_common(xf, wf, total_rows, n, k);
+  if (st != HQ_OK) return st;
+  if (num_experts < 1 || num_experts > 1024)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "num_experts must be in [1, 1024], got %d", num_experts);
+  if (x_scale_count != 1 && x_scale_count != total_rows)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "x_scale_count must be 1 or total_rows (%lld), got %lld", (long long)total_rows,
+                (long long)x_scale_count);
+  if (w_scale_count != num_experts && w_scale_count != (int64_t)num_experts * n)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "w_scale_count must be num_experts or num_experts * n, got %lld",
+                (long long)w_scale_count);
+  if ((double)((total_rows + 127) / 128 + num_experts) * (double)((n + 127) / 128) > 1.0e9)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "output too large for one launch");
+  if (total_rows == 0 || n == 0) return ok();
+  if (!xq || !wq_pre || !x_scale || !w_scale || !group_offsets || !out)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scale, w_scale, group_offsets and out must be non-NULL");
+  if (!aligned(xq, 16) || !aligned(wq_pre, 16) || !aligned(out, 16))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre and out must be 16-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(group_offsets, 4))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scales and group_offsets must be 4-byte aligned");
+  const Range rg[] = {
+      {out, (size_t)total_rows * (size_t)n * 2, "out"},
+      {xq, (size_t)total_rows * (size_t)k, "xq"},
+      {wq_pre, (size_t)padded_bytes(n, k) * (size_t)num_experts, "wq_pre"},
+      {x_scale, (size_t)x_scale_count * 4, "x_scale"},
+      {w_scale, (size_t)w_scale_count * 4, "w_scale"},
+      {group_offsets, ((size_t)num_experts + 1) * 4, "group_offsets"},
+  };
+  const char* other = nullptr;
+  const char* a = find_overlap(rg, 6, &other);
+  if (a && strcmp(a, "out") == 0) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
+  st = check_device();
+  if (st != HQ_OK) return st;
+  hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)total_rows, (int)n, (int)k, x_scale_count != 1,
+                 w_scale_count != num_experts};
+  (void)hipGetLastError();
+  return launched(hq::launch_grouped_gemm(g, group_offsets, num_experts, xf, wf, stream), "hq_grouped_gemm_a8w8");
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Device-side helpers shared by the quantize and GEMM kernels of libhq (gfx950).
+//
+// FP8 formats (hip-quant README, "FP8 Formats (both APIs)"): E4M3 bias 7, max
+// 448, NaN only; E5M2 bias 15, max 57344, +-Inf/NaN. The cast used everywhere is
+// saturating round-to-nearest-even: the scaled value is clamped to +-fmax with
+// v_med3_f32 and converted with the gfx950 OCP conversion instructions
+// (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, round-to-nearest-even). Clamp + convert
+// equals the saturating RNE encoder on every non-NaN float32 input (checked
+// exhaustively over all 2^32 patterns on the device); NaN inputs, which the clamp
+// would turn into +-fmax, are patched to the canonical code 0x7F.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+constexpr int kE4M3 = 0;
+constexpr int kE5M2 = 1;
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+constexpr uint32_t kInfBits = 0x7f800000u;   // float32 +Inf; magnitudes >= this are non-finite
+constexpr float kScaleFloor = 1.17549435e-38f;  // 2^-126, smallest normal float32
+
+template <int FMT> struct Fp8Fmt;
+template <> struct Fp8Fmt<kE4M3> { static constexpr float kMax = 448.0f; };
+template <> struct Fp8Fmt<kE5M2> { static constexpr float kMax = 57344.0f; };
+
+__device__ __forceinline__ float clamp_fmax(float v, float fmax) {
+  return __builtin_amdgcn_fmed3f(v, -fmax, fmax);
+}
+
+// Two saturating RNE casts packed into 16-bit half `hi` of `old`.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
+  constexpr float F = Fp8Fmt<FMT>::kMax;
+  const float ca = clamp_fmax(a, F), cb = clamp_fmax(b, F);
+  if (FMT == kE4M3) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, (int)old, HI);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, (int)old, HI);
+}
+
+// Four floats -> four codes in one dword (element i in byte i).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  uint32_t w = cvt2<FMT, false>(a, b, 0u);
+  return cvt2<FMT, true>(c, d, w);
+}
+
+// Replace byte i of `codes` by 0x7F where element i is NaN.
+__device__ __forceinline__ uint32_t patch_nan4(uint32_t codes, float a, float b, float c, float d) {
+  const float v[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (v[i] != v[i]) codes = (codes & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+  return codes;
+}
+
+// ---- high-precision input vectors (16 bytes) ----------------------------------
+
+// Number of elements in a 16-byte vector of input type XT.
+template <int XT> struct VecTraits;
+template <> struct VecTraits<kBF16> { static constexpr int kElems = 8; };
+template <> struct VecTraits<kF32> { static constexpr int kElems = 4; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element i of a vector as float32 (exact widening).
+template <int XT>
+__device__ __forceinline__ float vec_elem(const uint4& v, int i) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (XT == kF32) return __uint_as_float(w[i]);
+  return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+}
+
+// Largest magnitude in the vector, as float32 bits, non-finite elements included
+// (a result >= kInfBits means the vector holds an Inf or NaN).
+template <int XT>
+__device__ __forceinline__ uint32_t vec_absmax_raw(const uint4& v) {
+  if (XT == kF32) {
+    const uint32_t a = max(v.x & 0x7fffffffu, v.y & 0x7fffffffu);
+    const uint32_t b = max(v.z & 0x7fffffffu, v.w & 0x7fffffffu);
+    return max(a, b);
+  }
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m0 = __builtin_bit_cast(us2, v.x & 0x7fff7fffu);
+  us2 m1 = __builtin_bit_cast(us2, v.y & 0x7fff7fffu);
+  us2 m2 = __builtin_bit_cast(us2, v.z & 0x7fff7fffu);
+  us2 m3 = __builtin_bit_cast(us2, v.w & 0x7fff7fffu);
+  us2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1), __builtin_elementwise_max(m2, m3));
+  return (uint32_t)max(m[0], m[1]) << 16;
+}
+
+// Largest magnitude over the finite elements only, as float32 bits.
+template <int XT>
+__device__ __forceinline__ uint32_t vec_absmax_finite(const uint4& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < VecTraits<XT>::kElems; ++i) {
+    const uint32_t a = __float_as_uint(vec_elem<XT>(v, i)) & 0x7fffffffu;
+    m = max(m, a < kInfBits ? a : 0u);
+  }
+  return m;
+}
+
+// Cast the vector's elements times r. Output: bytes in element order, in
+// `out[0 .. kElems/4 - 1]`. `patch` adds the NaN fix-up.
+template <int XT, int FMT>
+__device__ __forceinline__ void vec_cast(const uint4& v, float r, bool patch, uint32_t* out) {
+#pragma unroll
+  for (int d = 0; d < VecTraits<XT>::kElems / 4; ++d) {
+    const float a = vec_elem<XT>(v, 4 * d + 0) * r;
+    const float b = vec_elem<XT>(v, 4 * d + 1) * r;
+    const float c = vec_elem<XT>(v, 4 * d + 2) * r;
+    const float e = vec_elem<XT>(v, 4 * d + 3) * r;
+    uint32_t w = cvt4<FMT>(a, b, c, e);
+    if (patch) w = patch_nan4(w, a, b, c, e);
+    out[d] = w;
+  }
+}
+
+// Cast a whole vector; applies the NaN patch only when the vector holds a
+// non-finite element (raw >= kInfBits), so the common path is branch-free.
+template <int XT, int FMT>
+__device__ __forceinline__ void vec_cast_checked(const uint4& v, float r, uint32_t raw, uint32_t* out) {
+  if (raw >= kInfBits) vec_cast<XT, FMT>(v, r, true, out);
+  else vec_cast<XT, FMT>(v, r, false, out);
+}
+
+// ---- reductions ----------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Block-wide max of a uint32; every thread gets the result. `lds` needs
+// BLOCK/64 entries. Contains __syncthreads (all threads must call it).
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds) {
+  v = wave_max_u32(v);
+  if (BLOCK == 64) return v;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();  // lds may still be read by a previous call
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  uint32_t m = lds[0];
+#pragma unroll
+  for (int i = 1; i < BLOCK / 64; ++i) m = max(m, lds[i]);
+  return m;
+}
+
+// Dequant scale from an amax given as float32 bits: s = max(amax / fmax, 2^-126)
+// (correctly rounded float32 division).
+template <int FMT>
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return fmaxf(amax / Fp8Fmt<FMT>::kMax, kScaleFloor);
+}
+
+// ---- bf16 output ---------------------------------------------------------------
+
+// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > kInfBits) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace hq

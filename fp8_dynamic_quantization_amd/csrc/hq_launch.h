@@ -1,0 +1,49 @@
+// Internal launcher interface between the C ABI (hq_api.cpp) and the kernels.
+// All sizes here have been validated by the caller; launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hq {
+
+constexpr int kMaxTensorPartials = 1024;  // blocks of the per-tensor partial pass
+constexpr int kColChunkRows = 128;        // rows per partial in the per-column pass
+
+int tensor_partial_blocks(size_t nvec);   // partials written by the per-tensor passes
+int col_chunks(int rows);                 // partial rows of the per-column pass
+
+hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
+                             float* amax, hipStream_t st);
+hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
+                               float* amax, void* ws, hipStream_t st);
+hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
+                             float* amax, void* ws, hipStream_t st);
+hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
+                                float* amax, float* state, int len, int idx, int margin, int32_t* flag, void* ws,
+                                hipStream_t st);
+hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_t* flag, const float* amax,
+                              int fmt, hipStream_t st);
+
+hipError_t launch_preshuffle(const uint8_t* wq, int n, int k, uint8_t* out, hipStream_t st);
+
+struct GemmArgs {
+  const uint8_t* xq;      // [m, k] row-major
+  const uint8_t* wq_pre;  // pre-shuffled weight(s)
+  const float* x_scale;   // [1] or [m]
+  const float* w_scale;   // [1] or [n] (per expert in the grouped form)
+  uint16_t* out;          // bf16 [m, n]
+  int m, n, k;
+  int x_scale_per_row;    // 0: x_scale[0] for every row
+  int w_scale_per_col;    // 0: w_scale[0] (per expert) for every column
+};
+
+hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, hipStream_t st);
+
+// Grouped form: rows [offsets[e], offsets[e+1]) use expert e's weight at
+// wq_pre + e * preshuffled_bytes(n, k) and scales w_scale + e * (per_col ? n : 1).
+hipError_t launch_grouped_gemm(const GemmArgs& a, const int32_t* offsets, int experts, int xf, int wf,
+                               hipStream_t st);
+
+}  // namespace hq

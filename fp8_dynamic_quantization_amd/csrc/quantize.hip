@@ -1,0 +1,499 @@
+// Dynamic and delayed FP8 quantization kernels for gfx950.
+//
+// What is computed (the method statement; hip-quant README "Scale / amax
+// tracking" and "Training-path numerical guards"; fuel-ir quant_scale.rs for the
+// granularities): per group, amax = max |x| over finite x, s = max(amax/fmax,
+// 2^-126), r = 1/s, q = saturating RNE cast of fl32(x*r).
+//
+// Kernels (all read the input once from HBM with 16-byte vector loads):
+//   quant_rows       one workgroup per row ("per token"): the row is held in
+//                    registers between the amax reduction and the cast
+//   amax_partials +  per tensor: block partial maxima, then every block folds
+//   quant_tensor     the partials and casts its share (two launches)
+//   colmax_partials  per column ("per channel"): 256-column x 128-row tiles write
+//   + quant_cols     column partial maxima, then the cast pass folds them
+//   quant_delayed    per tensor with the scale taken from an amax-history ring;
+//                    a last-block epilogue folds the amax into the ring and
+//                    publishes the next scale (AstrAI ops.cu, commit "finalize fp8
+//                    scale rings inside quantize kernels": threadfence + counter
+//                    election, no extra launch)
+//   ring_update      the same ring fold as a one-thread launch
+//
+// Partial maxima are stored as float32 magnitude bits in bits 0..30 with bit 31
+// set when the block saw a non-finite element.
+#include "hq_device.h"
+#include "hq_launch.h"
+
+namespace hq {
+
+constexpr int kBlock = 256;
+constexpr int kUnroll = 4;  // vectors in flight per thread in the grid-stride kernels
+constexpr uint32_t kNonfiniteBit = 0x80000000u;
+
+// ---------------------------------------------------------------------------
+// per row
+// ---------------------------------------------------------------------------
+
+// NV > 0: each thread keeps up to NV vectors of the row in registers.
+// NV == 0: the row is streamed twice (first pass for amax, second for the cast).
+template <int XT, int FMT, int NV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
+    const uint4* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ amax_out, int vpr) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t red[BLOCK / 64];
+  const size_t row = blockIdx.x;
+  const uint4* xr = x + row * (size_t)vpr;
+  uint8_t* qr = q + row * (size_t)vpr * E;
+
+  uint4 v[NV > 0 ? NV : 1];
+  uint32_t raw[NV > 0 ? NV : 1];
+  uint32_t mx = 0;
+  if (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = threadIdx.x + j * BLOCK;
+      raw[j] = 0;
+      if (i < vpr) {
+        v[j] = xr[i];
+        raw[j] = vec_absmax_raw<XT>(v[j]);
+      }
+      mx = max(mx, raw[j]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < vpr; i += BLOCK) mx = max(mx, vec_absmax_raw<XT>(xr[i]));
+  }
+  mx = block_max_u32<BLOCK>(mx, red);
+  if (mx >= kInfBits) {  // the row holds an Inf/NaN: recompute over finite elements
+    uint32_t f = 0;
+    if (NV > 0) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        if (threadIdx.x + j * BLOCK < vpr) f = max(f, vec_absmax_finite<XT>(v[j]));
+    } else {
+      for (int i = threadIdx.x; i < vpr; i += BLOCK) f = max(f, vec_absmax_finite<XT>(xr[i]));
+    }
+    mx = block_max_u32<BLOCK>(f, red);
+  }
+  const float amax = __uint_as_float(mx);
+  const float s = scale_from_amax<FMT>(amax);
+  const float r = 1.0f / s;
+  if (threadIdx.x == 0) {
+    scale[row] = s;
+    if (amax_out) amax_out[row] = amax;
+  }
+  if (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = threadIdx.x + j * BLOCK;
+      if (i < vpr) {
+        uint32_t w[E / 4];
+        vec_cast_checked<XT, FMT>(v[j], r, raw[j], w);
+        if (E == 8) *reinterpret_cast<uint2*>(qr + (size_t)i * 8) = make_uint2(w[0], w[E / 4 - 1]);
+        else *reinterpret_cast<uint32_t*>(qr + (size_t)i * 4) = w[0];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < vpr; i += BLOCK) {
+      const uint4 vv = xr[i];
+      uint32_t w[E / 4];
+      vec_cast_checked<XT, FMT>(vv, r, vec_absmax_raw<XT>(vv), w);
+      if (E == 8) *reinterpret_cast<uint2*>(qr + (size_t)i * 8) = make_uint2(w[0], w[E / 4 - 1]);
+      else *reinterpret_cast<uint32_t*>(qr + (size_t)i * 4) = w[0];
+    }
+  }
+}
+
+template <int XT, int FMT>
+static hipError_t launch_rows_t(const void* x, int rows, int vpr, uint8_t* q, float* scale,
+                                float* amax, hipStream_t st) {
+  const uint4* xv = static_cast<const uint4*>(x);
+  const dim3 grid(rows);
+  if (vpr <= 64) {
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 1, 64>), grid, dim3(64), 0, st, xv, q, scale, amax, vpr);
+  } else if (vpr <= 256) {
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 1, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+  } else if (vpr <= 512) {
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 2, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+  } else if (vpr <= 1024) {
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 4, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+  } else if (vpr <= 2048) {
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 8, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+  } else {
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 0, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// per tensor (dynamic): partial maxima, then fold + cast
+// ---------------------------------------------------------------------------
+
+template <int XT>
+__global__ __launch_bounds__(kBlock) void amax_partials_kernel(const uint4* __restrict__ x, size_t nvec,
+                                                               uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kBlock / 64];
+  uint32_t raw = 0, fin = 0;
+  const size_t stride = (size_t)gridDim.x * kBlock * kUnroll;
+  for (size_t base = blockIdx.x * (size_t)kBlock * kUnroll + threadIdx.x; base < nvec; base += stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (base + u * kBlock < nvec) v[u] = x[base + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (base + u * kBlock < nvec) {
+        const uint32_t m = vec_absmax_raw<XT>(v[u]);
+        raw = max(raw, m);
+        fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
+      }
+    }
+  }
+  const uint32_t braw = block_max_u32<kBlock>(raw, red);
+  const uint32_t bfin = block_max_u32<kBlock>(fin, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = bfin | (braw >= kInfBits ? kNonfiniteBit : 0u);
+}
+
+// Fold `n` partials (every thread gets the finite amax bits and the flag).
+__device__ __forceinline__ uint32_t fold_partials(const uint32_t* __restrict__ partial, int n, uint32_t* red,
+                                                  bool* nonfinite) {
+  uint32_t m = 0, f = 0;
+  for (int i = threadIdx.x; i < n; i += kBlock) {
+    const uint32_t p = partial[i];
+    m = max(m, p & ~kNonfiniteBit);
+    f |= p & kNonfiniteBit;
+  }
+  m = block_max_u32<kBlock>(m, red);
+  f = block_max_u32<kBlock>(f, red);
+  *nonfinite = f != 0;
+  return m;
+}
+
+template <int XT, int FMT>
+__global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __restrict__ x, size_t nvec,
+                                                              const uint32_t* __restrict__ partial, int npart,
+                                                              uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                              float* __restrict__ amax_out) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t red[kBlock / 64];
+  bool nonfinite;
+  const float amax = __uint_as_float(fold_partials(partial, npart, red, &nonfinite));
+  const float s = scale_from_amax<FMT>(amax);
+  const float r = 1.0f / s;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    scale[0] = s;
+    if (amax_out) amax_out[0] = amax;
+  }
+  const size_t stride = (size_t)gridDim.x * kBlock * kUnroll;
+  for (size_t base = blockIdx.x * (size_t)kBlock * kUnroll + threadIdx.x; base < nvec; base += stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (base + u * kBlock < nvec) v[u] = x[base + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t i = base + u * kBlock;
+      if (i < nvec) {
+        uint32_t w[E / 4];
+        if (nonfinite) vec_cast<XT, FMT>(v[u], r, true, w);
+        else vec_cast<XT, FMT>(v[u], r, false, w);
+        if (E == 8) *reinterpret_cast<uint2*>(q + i * 8) = make_uint2(w[0], w[E / 4 - 1]);
+        else *reinterpret_cast<uint32_t*>(q + i * 4) = w[0];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per column (dynamic)
+// ---------------------------------------------------------------------------
+// Tile: 32 vectors across (256 bf16 / 128 fp32 columns) x kColRows rows.
+// Thread t: vector column t % 32, row lane t / 32 (8 lanes, stride 8).
+
+constexpr int kColVecs = 32;
+constexpr int kColRows = kColChunkRows;
+
+template <int XT>
+__global__ __launch_bounds__(kBlock) void colmax_partials_kernel(const uint4* __restrict__ x, int rows, int vpr,
+                                                                 uint32_t* __restrict__ partial) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t tile[8][kColVecs * E];
+  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
+  const int vc = blockIdx.x * kColVecs + tx;
+  const int r0 = blockIdx.y * kColRows;
+  const int r1 = min(rows, r0 + kColRows);
+  uint32_t m[E];
+  uint32_t nf = 0;  // bit e: column e of this vector saw an Inf/NaN
+#pragma unroll
+  for (int e = 0; e < E; ++e) m[e] = 0;
+  if (vc < vpr) {
+    for (int r = r0 + ty; r < r1; r += 8) {
+      const uint4 v = x[(size_t)r * vpr + vc];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t a = __float_as_uint(vec_elem<XT>(v, e)) & 0x7fffffffu;
+        m[e] = max(m[e], a < kInfBits ? a : 0u);
+        nf |= (a >= kInfBits ? 1u : 0u) << e;
+      }
+    }
+  }
+  // finite max in bits 0..30, non-finite seen in bit 31
+#pragma unroll
+  for (int e = 0; e < E; ++e) tile[ty][tx * E + e] = m[e] | (((nf >> e) & 1u) ? kNonfiniteBit : 0u);
+  __syncthreads();
+  for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
+    uint32_t acc = 0, flag = 0;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      acc = max(acc, tile[l][c] & ~kNonfiniteBit);
+      flag |= tile[l][c] & kNonfiniteBit;
+    }
+    const int col = blockIdx.x * kColVecs * E + c;
+    if (col < vpr * E) partial[(size_t)blockIdx.y * vpr * E + col] = acc | flag;
+  }
+}
+
+template <int XT, int FMT>
+__global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restrict__ x, int rows, int vpr,
+                                                            const uint32_t* __restrict__ partial, int nchunk,
+                                                            uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                            float* __restrict__ amax_out) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ float rcp[kColVecs * E];
+  __shared__ uint32_t flags[kColVecs * E];
+  const int cols = vpr * E;
+  for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
+    const int col = blockIdx.x * kColVecs * E + c;
+    uint32_t acc = 0, flag = 0;
+    if (col < cols) {
+      for (int k = 0; k < nchunk; ++k) {
+        const uint32_t p = partial[(size_t)k * cols + col];
+        acc = max(acc, p & ~kNonfiniteBit);
+        flag |= p & kNonfiniteBit;
+      }
+      const float amax = __uint_as_float(acc);
+      const float s = scale_from_amax<FMT>(amax);
+      rcp[c] = 1.0f / s;
+      if (blockIdx.y == 0) {
+        scale[col] = s;
+        if (amax_out) amax_out[col] = amax;
+      }
+    } else {
+      rcp[c] = 0.0f;
+    }
+    flags[c] = flag;
+  }
+  __syncthreads();
+  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
+  const int vc = blockIdx.x * kColVecs + tx;
+  if (vc >= vpr) return;
+  bool patch = false;
+  float r[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    r[e] = rcp[tx * E + e];
+    patch |= flags[tx * E + e] != 0;
+  }
+  const int r0 = blockIdx.y * kColRows;
+  const int r1 = min(rows, r0 + kColRows);
+  for (int row = r0 + ty; row < r1; row += 8) {
+    const uint4 v = x[(size_t)row * vpr + vc];
+    uint32_t w[E / 4];
+#pragma unroll
+    for (int d = 0; d < E / 4; ++d) {
+      const float a = vec_elem<XT>(v, 4 * d + 0) * r[4 * d + 0];
+      const float b = vec_elem<XT>(v, 4 * d + 1) * r[4 * d + 1];
+      const float c = vec_elem<XT>(v, 4 * d + 2) * r[4 * d + 2];
+      const float e = vec_elem<XT>(v, 4 * d + 3) * r[4 * d + 3];
+      w[d] = cvt4<FMT>(a, b, c, e);
+      if (patch) w[d] = patch_nan4(w[d], a, b, c, e);
+    }
+    uint8_t* dst = q + ((size_t)row * vpr + vc) * E;
+    if (E == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[E / 4 - 1]);
+    else *reinterpret_cast<uint32_t*>(dst) = w[0];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// delayed scaling: the amax-history ring
+// ---------------------------------------------------------------------------
+
+// Fold one amax sample into the ring [hist[len] | scale | counter] and publish
+// the next scale (readings: max-reduced window; next = max * 2^margin / fmax,
+// floored at 2^-126; an all-zero window keeps the scale; a non-finite sample
+// leaves the ring unchanged and sets the sticky flag). Resets the counter.
+template <int FMT>
+__device__ void ring_fold(float* state, int len, int idx, int margin, int32_t* flag, float amax,
+                          bool nonfinite) {
+  const bool finite = amax <= 3.40282347e38f;  // false for NaN and Inf
+  if (nonfinite || !finite) {
+    if (flag) *flag = 1;
+  } else {
+    state[idx] = amax;
+    float w = 0.0f;
+    for (int i = 0; i < len; ++i) w = fmaxf(w, state[i]);
+    if (w > 0.0f) {
+      const float cand = ldexpf(w, margin) / Fp8Fmt<FMT>::kMax;
+      if (cand <= 3.40282347e38f) state[len] = fmaxf(cand, kScaleFloor);
+      else if (flag) *flag = 1;
+    }
+  }
+  reinterpret_cast<uint32_t*>(state)[len + 1] = 0u;
+}
+
+template <int FMT>
+__global__ void ring_update_kernel(float* state, int len, int idx, int margin, int32_t* flag,
+                                   const float* __restrict__ amax) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const float a = *amax;
+  ring_fold<FMT>(state, len, idx, margin, flag, a, false);
+}
+
+template <int XT, int FMT>
+__global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __restrict__ x, size_t nvec,
+                                                               uint8_t* __restrict__ q, float* __restrict__ scale_out,
+                                                               float* __restrict__ amax_out, float* state, int len,
+                                                               int idx, int margin, int32_t* flag,
+                                                               uint32_t* partial) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t red[kBlock / 64];
+  __shared__ bool is_last;
+  const float s_t = state[len];
+  const float r = 1.0f / s_t;
+  uint32_t raw = 0, fin = 0;
+  const size_t stride = (size_t)gridDim.x * kBlock * kUnroll;
+  for (size_t base = blockIdx.x * (size_t)kBlock * kUnroll + threadIdx.x; base < nvec; base += stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (base + u * kBlock < nvec) v[u] = x[base + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t i = base + u * kBlock;
+      if (i < nvec) {
+        const uint32_t m = vec_absmax_raw<XT>(v[u]);
+        raw = max(raw, m);
+        fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
+        uint32_t w[E / 4];
+        vec_cast_checked<XT, FMT>(v[u], r, m, w);
+        if (E == 8) *reinterpret_cast<uint2*>(q + i * 8) = make_uint2(w[0], w[E / 4 - 1]);
+        else *reinterpret_cast<uint32_t*>(q + i * 4) = w[0];
+      }
+    }
+  }
+  const uint32_t braw = block_max_u32<kBlock>(raw, red);
+  const uint32_t bfin = block_max_u32<kBlock>(fin, red);
+  uint32_t* counter = reinterpret_cast<uint32_t*>(state) + len + 1;
+  if (threadIdx.x == 0) {
+    partial[blockIdx.x] = bfin | (braw >= kInfBits ? kNonfiniteBit : 0u);
+    __threadfence();  // release the partial (agent scope: visible to every XCD)
+    const uint32_t prev = atomicAdd(counter, 1u);
+    is_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();  // acquire the other blocks' partials
+  uint32_t m = 0, f = 0;
+  for (int i = threadIdx.x; i < (int)gridDim.x; i += kBlock) {
+    const uint32_t p = __hip_atomic_load(partial + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    m = max(m, p & ~kNonfiniteBit);
+    f |= p & kNonfiniteBit;
+  }
+  m = block_max_u32<kBlock>(m, red);
+  f = block_max_u32<kBlock>(f, red);
+  if (threadIdx.x == 0) {
+    const float amax = __uint_as_float(m);
+    scale_out[0] = s_t;
+    if (amax_out) amax_out[0] = amax;
+    ring_fold<FMT>(state, len, idx, margin, flag, amax, f != 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+// Blocks of the amax-partials pass and of the delayed kernel (= partials written).
+int tensor_partial_blocks(size_t nvec) {
+  size_t b = (nvec + kBlock * kUnroll - 1) / (kBlock * kUnroll);
+  if (b < 1) b = 1;
+  if (b > kMaxTensorPartials) b = kMaxTensorPartials;
+  return (int)b;
+}
+
+int col_chunks(int rows) { return (rows + kColRows - 1) / kColRows; }
+
+#define HQ_DISPATCH_XT_FMT(XT, FMT, CALL)                 \
+  do {                                                    \
+    if ((XT) == kBF16 && (FMT) == kE4M3) { CALL(kBF16, kE4M3); } \
+    else if ((XT) == kBF16) { CALL(kBF16, kE5M2); }       \
+    else if ((FMT) == kE4M3) { CALL(kF32, kE4M3); }       \
+    else { CALL(kF32, kE5M2); }                           \
+  } while (0)
+
+hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
+                             float* amax, hipStream_t st) {
+  const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
+#define CALL(A, B) return launch_rows_t<A, B>(x, rows, vpr, q, scale, amax, st)
+  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+#undef CALL
+}
+
+hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
+                               float* amax, void* ws, hipStream_t st) {
+  const size_t nvec = xt == kBF16 ? numel / 8 : numel / 4;
+  const int nb = tensor_partial_blocks(nvec);
+  uint32_t* partial = static_cast<uint32_t*>(ws);
+  const uint4* xv = static_cast<const uint4*>(x);
+  size_t qb = (nvec + kBlock * kUnroll - 1) / (kBlock * kUnroll);
+  if (qb > 2048) qb = 2048;
+  if (qb < 1) qb = 1;
+#define CALL(A, B)                                                                                    \
+  hipLaunchKernelGGL((amax_partials_kernel<A>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, partial);     \
+  hipLaunchKernelGGL((quant_tensor_kernel<A, B>), dim3((unsigned)qb), dim3(kBlock), 0, st, xv, nvec, \
+                     (const uint32_t*)partial, nb, q, scale, amax);                                   \
+  return hipGetLastError()
+  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+#undef CALL
+}
+
+hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
+                             float* amax, void* ws, hipStream_t st) {
+  const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
+  const dim3 grid((vpr + kColVecs - 1) / kColVecs, col_chunks(rows));
+  uint32_t* partial = static_cast<uint32_t*>(ws);
+  const uint4* xv = static_cast<const uint4*>(x);
+#define CALL(A, B)                                                                                  \
+  hipLaunchKernelGGL((colmax_partials_kernel<A>), grid, dim3(kBlock), 0, st, xv, rows, vpr, partial); \
+  hipLaunchKernelGGL((quant_cols_kernel<A, B>), grid, dim3(kBlock), 0, st, xv, rows, vpr,           \
+                     (const uint32_t*)partial, (int)grid.y, q, scale, amax);                        \
+  return hipGetLastError()
+  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+#undef CALL
+}
+
+hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
+                                float* amax, float* state, int len, int idx, int margin, int32_t* flag, void* ws,
+                                hipStream_t st) {
+  const size_t nvec = xt == kBF16 ? numel / 8 : numel / 4;
+  const int nb = tensor_partial_blocks(nvec);
+  uint32_t* partial = static_cast<uint32_t*>(ws);
+  const uint4* xv = static_cast<const uint4*>(x);
+#define CALL(A, B)                                                                                  \
+  hipLaunchKernelGGL((quant_delayed_kernel<A, B>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, q, scale, \
+                     amax, state, len, idx, margin, flag, partial);                                  \
+  return hipGetLastError()
+  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+#undef CALL
+}
+
+hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_t* flag, const float* amax,
+                              int fmt, hipStream_t st) {
+  if (fmt == kE4M3)
+    hipLaunchKernelGGL((ring_update_kernel<kE4M3>), dim3(1), dim3(64), 0, st, state, len, idx, margin, flag, amax);
+  else
+    hipLaunchKernelGGL((ring_update_kernel<kE5M2>), dim3(1), dim3(64), 0, st, state, len, idx, margin, flag, amax);
+  return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,196 @@
+/*
+ * hq.h -- C ABI of the MI355X (gfx950) FP8 dynamic-quantization + scaled FP8
+ * (a8w8) GEMM library, libhq.so.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; host pointers are marked "host". The caller allocates
+ *    and owns every buffer (inputs, outputs, workspaces, ring state). The
+ *    library allocates nothing, frees nothing and keeps no pointer after a call
+ *    returns (the caller-owned output of the aiter PR "gemm_a8w8_bpreshuffle_out",
+ *    Technical Details).
+ *  - Every call is asynchronous on `stream` (0 = the null stream): it validates
+ *    its arguments on the host, then enqueues kernels and returns.
+ *  - Errors: a status code, plus a thread-local message from hq_last_error().
+ *    All argument checks run before any launch, and on any error nothing is
+ *    written (aiter PR, Technical Details and Test Plan). The architecture check
+ *    (gfx950 only, cached per device) runs after the argument checks, so an
+ *    invalid argument always reports HQ_ERR_INVALID_ARGUMENT.
+ *  - Not checked (documented preconditions, since checking needs a device sync):
+ *    that device pointers are device memory of the current device (operands on
+ *    a non-current device faulted in the aiter PR's review), that scale values
+ *    are positive and finite (hip-quant README, "Memory Safety"), and that
+ *    grouped-GEMM offsets are valid (the kernels clamp them, so invalid offsets
+ *    give wrong rows but never an out-of-bounds access).
+ *  - Sizes are int64 on the ABI and must fit int32 where the kernels index with
+ *    32-bit math (hip-quant README, "Memory Safety": checked narrowing).
+ *  - Enum-typed parameters are passed as C `int`.
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hq_status {
+  HQ_OK = 0,
+  HQ_ERR_INVALID_ARGUMENT = 1,   /* bad pointer, size, alignment, overlap, enum  */
+  HQ_ERR_UNSUPPORTED_DEVICE = 2, /* no HIP device, or the current one is not gfx950 */
+  HQ_ERR_LAUNCH = 3              /* the HIP runtime rejected a kernel launch     */
+} hq_status;
+
+/* FP8 formats (hip-quant README, table "FP8 Formats (both APIs)"): E4M3 bias 7,
+ * max 448, NaN only; E5M2 bias 15, max 57344, +-Inf and NaN. Casts are
+ * saturating round-to-nearest-even; NaN encodes to 0x7F; +-Inf saturates. */
+typedef enum hq_fp8 { HQ_E4M3 = 0, HQ_E5M2 = 1 } hq_fp8;
+
+/* Element type of a high-precision input tensor. */
+typedef enum hq_dtype { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+
+/* Scale granularity (fuel-ir 0.22.4 quant_scale.rs, ScaleGranularity): one scale
+ * for the tensor, one per row ("token"), or one per column ("channel") of a
+ * row-major [rows, cols] tensor. A GEMM weight W [N, K] gets its
+ * per-output-channel scales from the per-row call (HQ_PER_TOKEN) on W. */
+typedef enum hq_gran { HQ_PER_TENSOR = 0, HQ_PER_TOKEN = 1, HQ_PER_CHANNEL = 2 } hq_gran;
+
+/* Delayed-scaling state (AstrAI ops.cu, pack_quantize_params and the commit
+ * "finalize fp8 scale rings inside quantize kernels"): `state` is a device
+ * float32 buffer of len + 2 entries laid out as
+ *     [hist[0 .. len-1] | scale | counter]
+ * Initialise it to hist = 0, scale = 1.0, counter = 0 (all bits zero); the
+ * counter is 0 again after every call. `idx` is this step's history slot
+ * (0 <= idx < len), `margin` the power-of-two headroom of the next scale
+ * (-64 <= margin <= 64). `nonfinite_flag` is an optional device int32 that a
+ * call sets to 1 (never clears) when it sees a NaN or Inf amax sample
+ * (hip-quant README, "Training-path numerical guards"). */
+typedef struct hq_ring {
+  float* state;
+  int32_t len;
+  int32_t idx;
+  int32_t margin;
+  int32_t* nonfinite_flag;
+} hq_ring;
+
+/* Number of float32 scales for a [rows, cols] tensor: 1, rows or cols
+ * (fuel-ir quant_scale.rs, ScaleGranularity::scale_count). Returns -1 for an
+ * unknown granularity or negative sizes. */
+int64_t hq_scale_count(int gran, int64_t rows, int64_t cols);
+
+/* Bytes of device workspace hq_quantize_fp8 needs for this granularity and
+ * shape: 0 for HQ_PER_TOKEN, a few KB of block partials for HQ_PER_TENSOR
+ * (dynamic or delayed), ceil(rows/128) * cols * 4 for HQ_PER_CHANNEL.
+ * Returns 0 for invalid arguments (hq_quantize_fp8 then reports the error). */
+size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
+
+/* Dynamic (or delayed) FP8 quantization of a row-major [rows, cols] tensor.
+ *
+ * Dynamic (ring == NULL), for each group of the granularity:
+ *   amax  = max |x| over the group's finite elements
+ *   s     = max(fl32(amax / fmax), 2^-126)        fmax = 448 (E4M3) or 57344 (E5M2)
+ *   r     = fl32(1 / s)
+ *   q     = saturating RNE cast of fl32(x * r)
+ * (the method statement: amax reduction, scale = amax / 448, saturating RNE cast;
+ * hip-quant README "Training-path numerical guards": the reciprocal of the
+ * pre-quant multiplier is the dequant scale). x ~= decode(q) * s.
+ *
+ * Delayed (ring != NULL, gran must be HQ_PER_TENSOR): s is the ring's scale as
+ * read when the call starts, q is cast with r = fl32(1/s); the tensor's amax is
+ * then folded into the ring in the same launch (last-block epilogue), exactly as
+ * hq_scale_ring_update would: hist[idx] = amax, next scale =
+ * max(hist) * 2^margin / fmax. A tensor holding any NaN/Inf leaves the ring
+ * unchanged and sets *nonfinite_flag.
+ *
+ *   x          device, [rows, cols] of `xt`, row-major, 16-byte aligned
+ *   q          device, [rows, cols] uint8 FP8 codes, row-major, 16-byte aligned
+ *   scale_out  device, float32 [hq_scale_count(gran, rows, cols)]: the dequant
+ *              scales s used for the codes (in delayed mode, the ring's s_t)
+ *   amax_out   device, optional (NULL), float32 [scale_count]: the group amax
+ *   ring       host pointer to an hq_ring, or NULL for dynamic scaling
+ *   workspace  device, at least hq_quantize_workspace_bytes(gran, rows, cols)
+ *              bytes (may be NULL when that is 0); contents need no init
+ * Requires cols % 16 == 0 (16-byte vector rows), 1 <= rows, cols < 2^31,
+ * rows * cols < 2^40. rows == 0 returns HQ_OK without a launch. Outputs must not
+ * overlap inputs. */
+hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols,
+                          int fmt, int gran, uint8_t* q, float* scale_out,
+                          float* amax_out, const hq_ring* ring,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Fold one amax sample into a ring and publish the next scale (the delayed
+ * update of hq_quantize_fp8, as its own launch). `amax` is a device float32
+ * scalar; a NaN or Inf sample leaves the ring unchanged and sets the flag. */
+hq_status hq_scale_ring_update(const hq_ring* ring, const float* amax, int fmt,
+                               hipStream_t stream);
+
+/* Bytes of the pre-shuffled form of an [n, k] FP8 weight:
+ * ceil(n/16)*16 * ceil(k/128)*128. Returns -1 for invalid sizes. */
+int64_t hq_preshuffled_bytes(int64_t n, int64_t k);
+
+/* Reorder a row-major FP8 weight WQ [n, k] into the GEMM's pre-shuffled layout
+ * (the aiter PR has the GEMM read a pre-shuffled, optionally K-padded weight;
+ * the order is this library's): 16-row x 128-column fragments of 2048 bytes,
+ * fragment (nb, kb) at byte (nb * ceil(k/128) + kb) * 2048, and inside it the
+ * byte of (n_in, k_in) at h*1024 + (g*16 + n_in)*16 + b with g = k_in/32,
+ * h = (k_in%32)/16, b = k_in%16. Padding bytes are written as 0.
+ *   wq      device, uint8 [n, k] row-major, 16-byte aligned, k % 16 == 0
+ *   wq_pre  device, hq_preshuffled_bytes(n, k) bytes, 16-byte aligned */
+hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
+                               uint8_t* wq_pre, hipStream_t stream);
+
+/* Scaled FP8 GEMM into a caller-owned bf16 buffer (the method statement; the
+ * operand set of the aiter PR's gemm_a8w8_bpreshuffle_out):
+ *   out[m, n] = bf16_rne( fp32( sum_k dec(XQ[m,k]) * dec(WQ[n,k]) ) * x_scale[m] * w_scale[n] )
+ * accumulated in fp32 on gfx950 FP8 MFMA.
+ *   xq        device, uint8 [m, k] codes in format xf, row-major, 16-byte aligned
+ *   wq_pre    device, hq_preshuffle_weight(WQ [n, k]) in format wf
+ *   x_scale   device, float32 [x_scale_count], x_scale_count = 1 or m
+ *   w_scale   device, float32 [w_scale_count], w_scale_count = 1 or n
+ *   out       device, bf16 bits [m, n] dense row-major, 16-byte aligned; must not
+ *             overlap any input. Written in full; nothing else is touched.
+ * Requires k % 16 == 0, 1 <= k, m, n < 2^31. m == 0 or n == 0 returns HQ_OK
+ * without a launch (aiter PR: an empty out is a no-op). */
+hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                       const float* x_scale, int64_t x_scale_count,
+                       const float* w_scale, int64_t w_scale_count,
+                       int64_t m, int64_t n, int64_t k, uint16_t* out,
+                       hipStream_t stream);
+
+/* Grouped (per-expert) scaled FP8 GEMM over row ranges (megablocks-hip grouped
+ * GEMM notes: per-expert products of concatenated tokens, written over, never
+ * accumulated into, the output). For each expert e with rows
+ * [offsets[e], offsets[e+1]):
+ *   out[t, :] = gemm_a8w8 row t of XQ with expert e's weight and scales
+ *   xq             device, uint8 [total_rows, k] row-major, 16-byte aligned
+ *   wq_pre         device, num_experts consecutive pre-shuffled weights, each
+ *                  hq_preshuffled_bytes(n, k) bytes
+ *   x_scale        device, float32 [x_scale_count], 1 or total_rows
+ *   w_scale        device, float32 [w_scale_count], num_experts (one per expert)
+ *                  or num_experts * n (per expert, per output channel)
+ *   group_offsets  device, int32 [num_experts + 1], 0 = offsets[0] <= ... <=
+ *                  offsets[num_experts] = total_rows (precondition; clamped)
+ *   out            device, bf16 bits [total_rows, n], 16-byte aligned. Rows of
+ *                  no group are left untouched.
+ * Requires 1 <= num_experts <= 1024, k % 16 == 0. total_rows == 0 or n == 0
+ * returns HQ_OK without a launch. */
+hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
+                               int wf, const float* x_scale, int64_t x_scale_count,
+                               const float* w_scale, int64_t w_scale_count,
+                               const int32_t* group_offsets, int32_t num_experts,
+                               int64_t total_rows, int64_t n, int64_t k,
+                               uint16_t* out, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* hq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H */

@@ -1,0 +1,241 @@
+"""GPU parity of hq_quantize_fp8 / hq_scale_ring_update with the oracle: codes,
+scales, amax and ring state must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import fp8, quantize as Q
+from tests.gpu_helpers import dev_bf16, dev_f32, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+GRANS = [Q.PER_TENSOR, Q.PER_TOKEN, Q.PER_CHANNEL]
+FMTS = [fp8.E4M3, fp8.E5M2]
+
+
+@pytest.fixture(scope="module")
+def hq():
+    return require_gpu()
+
+
+def _gpu_quant(hq, x_np, dtype, fmt, gran):
+    x = dev_bf16(x_np) if dtype == Q.BF16 else dev_f32(x_np)
+    q, s, a = hq.hq_quantize_fp8(x, fmt, gran)
+    torch.cuda.synchronize()
+    return host(q), host(s), host(a)
+
+
+def _assert_same(hq, x_np, dtype, fmt, gran, what=""):
+    q, s, a = _gpu_quant(hq, x_np, dtype, fmt, gran)
+    q_ref, s_ref, a_ref = Q.quantize_dynamic(x_np, dtype, fmt, gran)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32)), f"scale mismatch {what}"
+    assert np.array_equal(a.view(np.uint32), a_ref.view(np.uint32)), f"amax mismatch {what}"
+    if not np.array_equal(q, q_ref):
+        bad = np.argwhere(q != q_ref)
+        i, j = bad[0]
+        raise AssertionError(f"{len(bad)} code mismatches {what}; first at ({i},{j}): gpu {q[i, j]:#04x} "
+                             f"oracle {q_ref[i, j]:#04x}")
+
+
+def test_tiny_per_tensor_workload(hq):
+    x, w = workloads.tiny_per_tensor(0)
+    for t in (x, w):
+        for fmt in FMTS:
+            _assert_same(hq, t, Q.F32, fmt, Q.PER_TENSOR, "tiny")
+
+
+# shapes chosen to cover one vector, several blocks, ragged tails and every
+# register-cache variant of the per-row kernel (incl. the streamed fallback)
+SHAPES_BF16 = [(1, 16), (3, 48), (64, 512), (130, 4112), (257, 2064), (5, 16512), (300, 272)]
+SHAPES_F32 = [(1, 16), (16, 128), (70, 1040), (9, 8208), (129, 4096)]
+
+
+@pytest.mark.parametrize("shape", SHAPES_BF16)
+@pytest.mark.parametrize("gran", GRANS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_bf16_random(hq, shape, gran, fmt):
+    rng = np.random.default_rng(hash((shape, gran, fmt)) % 2**32)
+    x = rng.standard_t(3, size=shape).astype(np.float32)
+    x *= np.exp(rng.standard_normal((shape[0], 1)) * 2).astype(np.float32)
+    _assert_same(hq, workloads.to_bf16_bits(x), Q.BF16, fmt, gran, f"{shape}")
+
+
+@pytest.mark.parametrize("shape", SHAPES_F32)
+@pytest.mark.parametrize("gran", GRANS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_f32_random(hq, shape, gran, fmt):
+    rng = np.random.default_rng(hash((shape, gran, fmt, 1)) % 2**32)
+    x = (rng.standard_normal(shape) * np.exp(rng.standard_normal((1, shape[1])) * 3)).astype(np.float32)
+    _assert_same(hq, x, Q.F32, fmt, gran, f"{shape}")
+
+
+@pytest.mark.parametrize("gran", GRANS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_special_values(hq, gran, fmt):
+    rng = np.random.default_rng(99)
+    x = rng.standard_normal((40, 64)).astype(np.float32)
+    x[0, 3] = np.nan
+    x[1, 5] = np.inf
+    x[2, 7] = -np.inf
+    x[3, :] = 0.0
+    x[4, :] = -0.0
+    x[5, 1] = -0.0
+    x[6, :] = 1e-40            # float32 subnormals
+    x[7, 2] = 3.0e38
+    x[8, :] = 2.0 ** -130
+    x[9, 9] = -np.nan
+    x[:, 10] = 0.0
+    x[:, 11] = np.nan
+    _assert_same(hq, x, Q.F32, fmt, gran, "special f32")
+    bits = workloads.to_bf16_bits(x)
+    bits[20, 0] = 0x0001       # smallest bf16 subnormal
+    bits[20, 1] = 0x8001
+    bits[21, 0] = 0x7F80       # +Inf
+    bits[22, 0] = 0xFFC1       # NaN with payload
+    _assert_same(hq, bits, Q.BF16, fmt, gran, "special bf16")
+
+
+def test_every_bf16_pattern(hq):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    for fmt in FMTS:
+        for gran in GRANS:
+            _assert_same(hq, bits, Q.BF16, fmt, gran, "all bf16 patterns")
+
+
+# ---- the workloads at full size ------------------------------------------------
+
+def test_ptpc_square_full(hq):
+    x, w = workloads.ptpc_square(1)
+    _assert_same(hq, x, Q.BF16, fp8.E4M3, Q.PER_TOKEN, "ptpc X per-token")
+    _assert_same(hq, w, Q.BF16, fp8.E4M3, Q.PER_TOKEN, "ptpc W per-output-channel")
+    _assert_same(hq, x, Q.BF16, fp8.E4M3, Q.PER_TENSOR, "ptpc X per-tensor")
+    _assert_same(hq, x, Q.BF16, fp8.E4M3, Q.PER_CHANNEL, "ptpc X per-channel")
+
+
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_decode_skinny_full(hq, m):
+    x, w = workloads.decode_skinny(m)
+    _assert_same(hq, x, Q.BF16, fp8.E4M3, Q.PER_TOKEN, f"decode X m={m}")
+    if m == 32:
+        _assert_same(hq, w, Q.BF16, fp8.E4M3, Q.PER_TOKEN, "decode W")
+
+
+def test_grouped_moe_full(hq):
+    x, w, _ = workloads.grouped_moe(3)
+    _assert_same(hq, x, Q.BF16, fp8.E4M3, Q.PER_TOKEN, "moe X")
+    _assert_same(hq, w.reshape(-1, w.shape[-1]), Q.BF16, fp8.E4M3, Q.PER_TOKEN, "moe W")
+
+
+def test_repeated_calls_with_shared_workspace(hq):
+    """Per-tensor and per-channel reuse one workspace across calls of different
+    sizes; each result must be independent of the previous call."""
+    rng = np.random.default_rng(5)
+    shapes = [(512, 1024), (16, 64), (300, 2048), (1, 16)]
+    ws = torch.empty(max(hq.hq_quantize_workspace_bytes(g, *s) for s in shapes for g in GRANS),
+                     dtype=torch.uint8, device="cuda")
+    for it in range(2):
+        for shape in shapes:
+            for gran in (Q.PER_TENSOR, Q.PER_CHANNEL):
+                x = (rng.standard_normal(shape) * (10.0 ** rng.integers(-3, 3))).astype(np.float32)
+                q, s, a = hq.hq_quantize_fp8(dev_f32(x), fp8.E4M3, gran, workspace=ws)
+                q_ref, s_ref, a_ref = Q.quantize_dynamic(x, Q.F32, fp8.E4M3, gran)
+                assert np.array_equal(host(q), q_ref)
+                assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+
+
+# ---- delayed scaling ---------------------------------------------------------------
+
+def _ring_host(r):
+    return host(r.state).copy(), int(host(r.flag)[0])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dtype", [Q.BF16, Q.F32])
+def test_delayed_ring_sequence(hq, fmt, dtype):
+    """20 steps (wraps a 16-entry ring) with a moving amax, a NaN step and an
+    all-zero step; codes, used scale, amax and the whole ring state must match
+    the oracle after every step."""
+    rng = np.random.default_rng(17 + fmt + 2 * dtype)
+    ring = hq.Ring(16, margin=1 if fmt == fp8.E4M3 else 0)
+    st = Q.ring_new(16)
+    flag = 0
+    shape = (96, 320)
+    for t in range(20):
+        x = (rng.standard_normal(shape) * np.exp(rng.standard_normal() * 2)).astype(np.float32)
+        if t == 7:
+            x[5, 5] = np.nan
+        if t == 9:
+            x[:] = 0.0
+        xin = workloads.to_bf16_bits(x) if dtype == Q.BF16 else x
+        xd = dev_bf16(xin) if dtype == Q.BF16 else dev_f32(xin)
+        q, s, a = hq.hq_quantize_fp8(xd, fmt, Q.PER_TENSOR, ring=ring, ring_idx=t % 16)
+        q_ref, s_ref, a_ref, st, flag = Q.quantize_delayed(xin, dtype, fmt, st, t % 16, ring.margin, flag)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), q_ref), f"codes differ at step {t}"
+        assert host(s).view(np.uint32)[0] == s_ref.view(np.uint32)[0], f"scale differs at step {t}"
+        assert host(a).view(np.uint32)[0] == a_ref.view(np.uint32)[0], f"amax differs at step {t}"
+        gst, gflag = _ring_host(ring)
+        assert np.array_equal(gst.view(np.uint32), st.view(np.uint32)), f"ring differs at step {t}"
+        assert gflag == flag
+
+
+def test_delayed_large_tensor_many_blocks(hq):
+    """A tensor large enough for the maximum number of partial blocks; the
+    last-block election must see every block's amax."""
+    x, w = workloads.ptpc_square(1, m=2048, n=64, k=4096)
+    ring = hq.Ring(16)
+    st = Q.ring_new(16)
+    flag = 0
+    for t in range(3):
+        q, s, a = hq.hq_quantize_fp8(dev_bf16(x), fp8.E4M3, Q.PER_TENSOR, ring=ring, ring_idx=t)
+        q_ref, s_ref, a_ref, st, flag = Q.quantize_delayed(x, Q.BF16, fp8.E4M3, st, t, 0, flag)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), q_ref)
+        assert np.array_equal(host(ring.state).view(np.uint32), st.view(np.uint32))
+
+
+def test_ring_update_entry_point(hq):
+    ring = hq.Ring(4, margin=-1)
+    st = Q.ring_new(4)
+    flag = 0
+    samples = [3.0, 0.5, np.inf, 7.0, 0.0, 1e-30, np.nan, 2.5, 9.0]
+    for t, smp in enumerate(samples):
+        amax = torch.tensor([smp], dtype=torch.float32, device="cuda")
+        hq.hq_scale_ring_update(ring, amax, fp8.E5M2, ring_idx=t % 4)
+        st, flag = Q.ring_update(st, t % 4, -1, np.float32(smp), False, fp8.E5M2, flag)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ring.state).view(np.uint32), st.view(np.uint32)), t
+        assert int(host(ring.flag)[0]) == flag
+
+
+def test_training_linear_rings(hq):
+    """Two layers of the training workload for 20 steps: forward E4M3 X and W
+    rings, backward E5M2 G ring (16 entries, margin 0)."""
+    base, factors = workloads.training_linear(4, layers=2, steps=20)
+    for layer in range(2):
+        rings = [hq.Ring(16) for _ in range(3)]
+        sts = [Q.ring_new(16) for _ in range(3)]
+        flags = [0, 0, 0]
+        fmts = [fp8.E4M3, fp8.E4M3, fp8.E5M2]
+        for t in range(20):
+            tensors = workloads.training_step_inputs(base, factors, t, layer)
+            for i, (bits, fmt) in enumerate(zip(tensors, fmts)):
+                q, s, a = hq.hq_quantize_fp8(dev_bf16(bits), fmt, Q.PER_TENSOR, ring=rings[i], ring_idx=t % 16)
+                q_ref, s_ref, a_ref, sts[i], flags[i] = Q.quantize_delayed(bits, Q.BF16, fmt, sts[i], t % 16, 0,
+                                                                          flags[i])
+                torch.cuda.synchronize()
+                assert np.array_equal(host(q), q_ref), (layer, t, i)
+                assert np.array_equal(host(rings[i].state).view(np.uint32), sts[i].view(np.uint32)), (layer, t, i)
+
+
+def test_invalid_arguments_leave_outputs_untouched(hq):
+    x = torch.randn(8, 48, device="cuda")
+    q = torch.full((8, 48), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((8,), -1.0, device="cuda")
+    with pytest.raises(ValueError):
+        hq.hq_quantize_fp8(x, 7, Q.PER_TOKEN, q=q, scale_out=s)
+    with pytest.raises(ValueError):
+        hq.hq_quantize_fp8(x[:, :40], fp8.E4M3, Q.PER_TOKEN, q=q[:, :40], scale_out=s)
+    torch.cuda.synchronize()
+    assert bool((q == 0xAB).all()) and bool((s == -1.0).all())
