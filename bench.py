@@ -1,0 +1,282 @@
+"""Benchmark of the dynamic-FP8 quantize + a8w8 GEMM hot path on one MI355X.
+
+Workload (the PTPC square configuration): X bf16 [4096, 4096] N(0,1) with 0.1%
+of entries x50, W bf16 [4096, 4096] N(0, 0.02^2). One step is one pass of the
+whole path: per-token E4M3 quantization of X, per-output-channel E4M3
+quantization of W (row reduction on [N, K]), pre-shuffle of WQ, and the a8w8
+GEMM M = N = K = 4096 into bf16. Inputs are resident in HBM before timing;
+``--rotate`` input/output sets (default 4, ~600 MB) cycle so that no step hits
+data left in the 256 MB Infinity Cache by the previous one.
+
+Prints one JSON line (stdout). ``value`` = 2*M*N*K / step time (TFLOP/s of the
+whole step). ``roofline`` refers to the dominant kernel (the GEMM), timed with
+HIP events on the stream it runs on. ``cpu_baseline`` times the CPU oracle on a
+bounded sample (see --cpu-rows) and scales it to the same unit.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "a8w8 GEMM TFLOP/s + quantize GB/s (% of MI355X roofline), PTPC 4096³"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+M = N = K = 4096
+KERNEL_SOURCES = ["fp8_dynamic_quantization_amd/csrc/gemm.hip", "fp8_dynamic_quantization_amd/csrc/quantize.hip",
+                  "fp8_dynamic_quantization_amd/csrc/hq_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Buffers:
+    """One rotating set of device buffers for a step."""
+
+    def __init__(self, torch, x_bits, w_bits, pre_bytes):
+        dev = "cuda"
+        self.x = torch.from_numpy(x_bits.view("int16")).to(dev).view(torch.bfloat16)
+        self.w = torch.from_numpy(w_bits.view("int16")).to(dev).view(torch.bfloat16)
+        self.xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        self.wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty(M, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(N, dtype=torch.float32, device=dev)
+        self.xa = torch.empty(M, dtype=torch.float32, device=dev)
+        self.wa = torch.empty(N, dtype=torch.float32, device=dev)
+        self.wpre = torch.empty(pre_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.p = {k: p(getattr(self, k)) for k in ("x", "w", "xq", "wq", "xs", "ws", "xa", "wa", "wpre", "out")}
+
+
+def make_ops(hq, lib, stream):
+    """Per-kernel launch closures calling the C ABI with pre-marshalled pointers."""
+    E4M3, BF16, TOK = hq.HQ_E4M3, hq.HQ_BF16, hq.HQ_PER_TOKEN
+
+    def quant_x(b):
+        st = lib.hq_quantize_fp8(b.p["x"], BF16, M, K, E4M3, TOK, b.p["xq"], b.p["xs"], b.p["xa"], None, None, 0,
+                                 stream)
+        assert st == 0, hq.hq_last_error()
+
+    def quant_w(b):
+        st = lib.hq_quantize_fp8(b.p["w"], BF16, N, K, E4M3, TOK, b.p["wq"], b.p["ws"], b.p["wa"], None, None, 0,
+                                 stream)
+        assert st == 0, hq.hq_last_error()
+
+    def preshuffle(b):
+        st = lib.hq_preshuffle_weight(b.p["wq"], N, K, b.p["wpre"], stream)
+        assert st == 0, hq.hq_last_error()
+
+    def gemm(b):
+        st = lib.hq_gemm_a8w8(b.p["xq"], E4M3, b.p["wpre"], E4M3, b.p["xs"], M, b.p["ws"], N, M, N, K, b.p["out"],
+                              stream)
+        assert st == 0, hq.hq_last_error()
+
+    return {"quant_x": quant_x, "quant_w": quant_w, "preshuffle": preshuffle, "gemm": gemm}
+
+
+def time_kernel(torch, fn, sets, reps):
+    """Average duration (ms) of `fn` over `reps` launches on the current stream."""
+    for i in range(3):
+        fn(sets[i % len(sets)])
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(reps):
+        fn(sets[i % len(sets)])
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def traffic_from_profile(name):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(rows: int):
+    """Time the CPU oracle on a bounded sample of the step and scale it to the
+    whole 4096^3 step: quantization of `rows` rows of X and W, pre-shuffle of
+    `rows` rows of WQ, and a rows x rows x 4096 block of the float64 GEMM."""
+    import numpy as np
+
+    import workloads
+    from oracle import fp8, gemm as G, preshuffle as P, quantize as Q
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    x, w = workloads.ptpc_square(1)
+    xs_, ws_ = x[:rows], w[:rows]
+    t0 = time.perf_counter()
+    xq, xsc, _ = Q.quantize_dynamic(xs_, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
+    wq, wsc, _ = Q.quantize_dynamic(ws_, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
+    t1 = time.perf_counter()
+    P.preshuffle(wq)
+    t2 = time.perf_counter()
+    G.gemm_a8w8(xq, fp8.E4M3, wq, fp8.E4M3, xsc, wsc)
+    t3 = time.perf_counter()
+    t_quant = (t1 - t0) * (M + N) / (2 * rows)
+    t_pre = (t2 - t1) * N / rows
+    t_gemm = (t3 - t2) * (M * N) / (rows * rows)
+    total = t_quant + t_pre + t_gemm
+    return {
+        "value": round(2.0 * M * N * K / total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"oracle on rows 0..{rows - 1} of X and W (quantize), {rows} rows of WQ (pre-shuffle) and a "
+                   f"{rows}x{rows}x{K} float64 GEMM block, {t3 - t0:.2f} s measured, scaled linearly to the "
+                   f"full step ({total:.1f} s estimated)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled to defeat the MALL")
+    ap.add_argument("--kernel-reps", type=int, default=100)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (PMC calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (this build has no multi-GPU "
+              "path; run it with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_dynamic_quantization_amd as hq
+    import workloads
+
+    if not os.path.exists(hq.LIB_PATH):
+        from fp8_dynamic_quantization_amd import build as b
+        b.build()
+    lib = hq.load()
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x 1 GiB device copies")
+        return
+
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    log("generating inputs ...")
+    x_bits, w_bits = workloads.ptpc_square(1)
+    pre_bytes = hq.hq_preshuffled_bytes(N, K)
+    sets = [Buffers(torch, x_bits, w_bits, pre_bytes) for _ in range(args.rotate)]
+    ops = make_ops(hq, lib, stream)
+
+    def step(i):
+        b = sets[i % len(sets)]
+        ops["quant_x"](b)
+        ops["quant_w"](b)
+        ops["preshuffle"](b)
+        ops["gemm"](b)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+    log(f"step: {ms_step * 1e3:.1f} us")
+
+    kms = {name: time_kernel(torch, fn, sets, args.kernel_reps) for name, fn in ops.items()}
+    for name, ms in kms.items():
+        log(f"  {name}: {ms * 1e3:.2f} us")
+    quant_bytes = M * K * 2 + M * K + M * 4 * 2      # bf16 in, codes out, scale + amax out
+    pre_alg_bytes = N * K + pre_bytes
+    gemm_tflops = flops / (kms["gemm"] * 1e-3) / 1e12
+    quant_gbs = quant_bytes / (kms["quant_x"] * 1e-3) / 1e9
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (E4M3 codes, fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {
+            "workload": "PTPC square: X bf16 [4096,4096] N(0,1) with 0.1% of entries x50, W bf16 [4096,4096] "
+                        "N(0,0.02^2); per-token X, per-output-channel W, E4M3; GEMM M=N=K=4096 -> bf16",
+            "step": "quantize X + quantize W + pre-shuffle W + GEMM",
+            "m": M, "n": N, "k": K, "rotating_sets": args.rotate,
+        },
+        "roofline": {
+            "kernel": "gemm (hq_gemm_a8w8)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile("gemm_ptpc4096"),
+        },
+        "kernels_us": {k: round(v * 1e3, 3) for k, v in kms.items()},
+        "quantize": {
+            "kernel": "per-token quantize of X (hq_quantize_fp8)",
+            "bound": "hbm",
+            "achieved": round(quant_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": quant_bytes,
+            "traffic": traffic_from_profile("quant_rows_ptpc4096"),
+        },
+        "preshuffle_gbs": round(pre_alg_bytes / (kms["preshuffle"] * 1e-3) / 1e9, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
