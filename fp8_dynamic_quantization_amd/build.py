@@ -23,6 +23,11 @@ LIB = os.path.join(PKG, "libhq.so")
 
 SOURCES = ["quantize.hip", "gemm.hip", "hq_api.cpp"]
 
+# Per-source flags. The GEMM keeps its MFMA accumulators in VGPRs and the
+# operand fragments in AGPRs: with 256 accumulator registers per wavefront the
+# default AGPR-accumulator allocation spills to scratch, this form does not.
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [
@@ -35,7 +40,7 @@ COMMON = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

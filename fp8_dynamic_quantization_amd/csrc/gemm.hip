@@ -7,21 +7,26 @@
 // V_MFMA_F32_16X16X128_F8F6F4 instruction (FP8/BF8 selected per operand), fp32
 // accumulators, and a fused scale + bf16 epilogue.
 //
-// Operand register layout of one 16x16x128 MFMA (per 64-lane wavefront): lane l
-// holds row (or column) l % 16 and the 32 consecutive k values
-// 32*(l/16) .. 32*(l/16)+31 of both A and B; the 4 results of lane l are
-// column l % 16, rows 4*(l/16) + 0..3.
+// MFMA register layout (per 64-lane wavefront, 16x16x128): lane l holds row l%16
+// of the first operand and column l%16 of the second, each with the 32
+// consecutive k values 32*(l/16) .. +31; result lane l holds column l%16, rows
+// 4*(l/16) + 0..3. The kernels pass the weight fragment as the first operand and
+// the activation fragment as the second, so a lane's four results are four
+// weight "slots" of one activation row. The pre-shuffled weight puts output
+// channels 8g..8g+3 of a 32-channel group in slots 4g..4g+3 of its first
+// fragment and channels 8g+4..8g+7 in the same slots of its second fragment:
+// after the two MFMAs of a fragment pair, lane l holds 8 consecutive output
+// columns of one row, stored as one 16-byte write.
 //
-// Tiling: a workgroup computes a BM x BN output tile with WAVES_M x WAVES_N
-// wavefronts; K advances in steps of 128 through double-buffered LDS:
-//   A (XQ, row-major) is staged with an XOR swizzle of its 16-byte chunks
-//     (chunk c of row r at slot c ^ (r & 7)) so both the row-wise stores and the
-//     MFMA-order reads are free of bank conflicts;
-//   B (pre-shuffled WQ) is copied verbatim: a 2048-byte fragment is already in
-//     MFMA lane order, so each wavefront reads it as 64 consecutive 16-byte pieces.
-// Tails: rows past M are clamped on load and masked on store; weight fragments past
-// the last 16-column block are clamped on load and masked on store; the K tail of
-// A is zero-filled (the pre-shuffled B is zero-padded to a multiple of 128).
+// Tiling: a workgroup of four wavefronts computes a BM x (4*TN) tile. The BM
+// rows of A (XQ, row-major) are staged through double-buffered LDS with an XOR
+// swizzle of their 16-byte chunks (chunk c of row r at slot c ^ (r & 7)), which
+// keeps the row-wise stores and the MFMA-order reads free of bank conflicts.
+// Wavefront w owns TN columns and streams their pre-shuffled B fragments from
+// global memory straight into registers (each fragment half is one coalesced
+// 1 KB load), so B never touches LDS. Tails: rows past M are clamped on load
+// and masked on store; fragments past the padded N are clamped on load and their
+// columns masked on store; the K tail of A is zeroed (B is zero-padded).
 #include "hq_device.h"
 #include "hq_launch.h"
 
@@ -29,92 +34,135 @@ namespace hq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;          // K per pipeline stage = one MFMA
-constexpr int kFragBytes = 2048;  // 16 rows x 128 k
+constexpr int kFragBytes = 2048;  // 16 slots x 128 k
+// Third flags word of a raw (stride 0) buffer resource on gfx9-class parts:
+// 32-bit data format, range-checked against the extent.
+constexpr int kRsrcFlags = 0x00020000;
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 as_uint4(v4u v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
 // ---------------------------------------------------------------------------
 // pre-shuffle
 // ---------------------------------------------------------------------------
-// One thread per 16-byte piece of the output: piece P of fragment (nb, kb) holds
-// h = P / 64, lane = P % 64 -> row nb*16 + lane%16, columns kb*128 + 32*(lane/16)
-// + 16*h .. +15.
+// One thread per 16-byte piece of the output. Piece P of fragment (nb, kb):
+// h = P / 64, slot = P % 16, quarter q = (P % 64) / 16 -> weight row
+// 32*(nb/2) + 8*(slot/4) + 4*(nb%2) + slot%4, columns kb*128 + 32*q + 16*h .. +15.
 __global__ __launch_bounds__(256) void preshuffle_kernel(const uint8_t* __restrict__ wq, int n, int k, int kblocks,
                                                          size_t npieces, uint8_t* __restrict__ out) {
   const size_t pc = blockIdx.x * (size_t)256 + threadIdx.x;
   if (pc >= npieces) return;
   const size_t frag = pc / 128;
   const int p = (int)(pc % 128);
-  const int h = p / 64, lane = p % 64;
+  const int h = p / 64, q = (p % 64) / 16, slot = p % 16;
   const int nb = (int)(frag / kblocks), kb = (int)(frag % kblocks);
-  const int row = nb * 16 + (lane & 15);
-  const int col = kb * kBK + (lane >> 4) * 32 + h * 16;
+  const int row = 32 * (nb >> 1) + 8 * (slot >> 2) + 4 * (nb & 1) + (slot & 3);
+  const int col = kb * kBK + q * 32 + h * 16;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (row < n && col < k) v = *reinterpret_cast<const uint4*>(wq + (size_t)row * k + col);
   *reinterpret_cast<uint4*>(out + pc * 16) = v;
 }
 
+// Number of 16-slot fragments along N after padding N to a multiple of 32.
+__host__ __device__ inline int frag_rows(int n) { return (n + 31) / 32 * 2; }
+
 hipError_t launch_preshuffle(const uint8_t* wq, int n, int k, uint8_t* out, hipStream_t st) {
-  const int nblocks16 = (n + 15) / 16;
   const int kblocks = (k + kBK - 1) / kBK;
-  const size_t npieces = (size_t)nblocks16 * kblocks * 128;
+  const size_t npieces = (size_t)frag_rows(n) * kblocks * 128;
   const size_t grid = (npieces + 255) / 256;
   hipLaunchKernelGGL(preshuffle_kernel, dim3((unsigned)grid), dim3(256), 0, st, wq, n, k, kblocks, npieces, out);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// GEMM
+// GEMM tile
 // ---------------------------------------------------------------------------
-
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-struct TileCfg {
-  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
-  static constexpr int kTM = BM / WAVES_M, kTN = BN / WAVES_N;
-  static constexpr int kIM = kTM / 16, kIN = kTN / 16;
+// Per 128-deep K step a wavefront issues BM/16 x TN/16 MFMAs. A is double-
+// buffered in LDS and B in registers; the K loop is unrolled by two so every
+// register buffer has a compile-time index.
+template <int BM, int TN, int WM>
+struct BsCfg {
+  static constexpr int kWaves = 4 * WM;            // WM wavefront rows x 4 wavefront columns
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBN = 4 * TN;
+  static constexpr int kWR = BM / WM;              // rows per wavefront
+  static constexpr int kIM = kWR / 16, kIN = TN / 16;
   static constexpr int kAVec = BM * 8 / kThreads;  // 16-byte A pieces per thread per stage
-  static constexpr int kBVec = BN * 8 / kThreads;  // 16-byte B pieces per thread per stage
-  static constexpr int kABytes = BM * kBK, kBBytes = BN * kBK;
-  static constexpr int kStage = kABytes + kBBytes;
-  static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile");
-  static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "loads");
+  static constexpr int kRowStep = kThreads / 8;    // rows between a thread's A pieces
+  static constexpr int kABytes = BM * kBK;         // one LDS stage
+  static constexpr int kLdsBytes = 2 * kABytes + (BM + kBN) * 4;  // two A stages + epilogue scales
+  static_assert(BM % 32 == 0 && TN % 32 == 0 && kWR % 16 == 0, "tile");
 };
 
-// One output tile. Rows [m0, row_end) are valid (row_end > m0); weight `wq`
-// points at this operand's pre-shuffled matrix; `ws` at its scales.
-template <int XF, int WF, int BM, int BN, int WAVES_M, int WAVES_N>
+// KTAIL: K is not a multiple of 128, so the A chunks past K are zeroed on their
+// way to LDS; without it the K loop has no masking at all.
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m0, int row_end, int n0,
                                           const uint8_t* __restrict__ wq, const float* __restrict__ ws) {
-  using C = TileCfg<BM, BN, WAVES_M, WAVES_N>;
+  using C = BsCfg<BM, TN, WM>;
+  static_assert(C::kAVec <= C::kIM && 2 * C::kIN <= C::kIM, "slot schedule: one A piece and one B half per slot");
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront column
+  const int wrow = __builtin_amdgcn_readfirstlane(tid >> 8);        // wavefront row
   const int K = a.k;
   const int nkb = (K + kBK - 1) / kBK;
-  const int nblk16 = (a.n + 15) / 16;
+  const int nfrag = frag_rows(a.n);
 
-  // global source offsets (constant across K steps)
-  size_t a_src[C::kAVec];
-  int a_col[C::kAVec], a_dst[C::kAVec];
+  // A staging: piece v of thread t is row v*kRowStep + t/8, 16-byte chunk t%8.
+  // The swizzle (chunk ^ row%8) only depends on t, so every piece of a thread
+  // shares one LDS offset plus a compile-time v*kRowStep*128.
+  const int a_c = tid & 7, a_r = tid >> 3;
+  const int a_dst = a_r * kBK + ((a_c ^ (a_r & 7)) << 4);
+  const int a_kmax = K - 16 - a_c * 16;  // largest in-row offset of this thread's chunk
+  // Global loads are buffer loads: a resource descriptor (base + extent) in
+  // scalar registers, a 32-bit per-lane offset that stays fixed for the whole K
+  // loop and a wavefront-uniform offset that carries the K step, so the loop
+  // keeps no 64-bit addresses in vector registers.
+  // A: offsets from the tile's first row (K < 2^24 keeps BM*K below 2^32); rows
+  // past row_end are clamped to the last valid row.
+  const int a_rmax = row_end - 1 - m0;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.xq + (size_t)m0 * K), (short)0, (a_rmax + 1) * K, kRsrcFlags);
+  uint32_t a_off[C::kAVec];
 #pragma unroll
-  for (int v = 0; v < C::kAVec; ++v) {
-    const int L = v * C::kThreads + tid;
-    const int r = L >> 3, c = L & 7;
-    const int grow = min(m0 + r, row_end - 1);
-    a_src[v] = (size_t)grow * K + c * 16;
-    a_col[v] = c * 16;
-    a_dst[v] = r * kBK + ((c ^ (r & 7)) << 4);
-  }
-  size_t b_src[C::kBVec];
-  int b_dst[C::kBVec];
+  for (int v = 0; v < C::kAVec; ++v) a_off[v] = (uint32_t)min(v * C::kRowStep + a_r, a_rmax) * (uint32_t)K + a_c * 16;
+  // B: one resource on the wavefront's first fragment row; fragment j (clamped
+  // to the last one) sits b_joff[j] bytes further, a uniform offset.
+  const int nbw = __builtin_amdgcn_readfirstlane((n0 + wave * TN) / 16);
+  const int nbw_c = min(nbw, nfrag - 1);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wq + (size_t)nbw_c * nkb * kFragBytes), (short)0, min(C::kIN, nfrag - nbw_c) * nkb * kFragBytes,
+      kRsrcFlags);
+  int b_joff[C::kIN];
 #pragma unroll
-  for (int v = 0; v < C::kBVec; ++v) {
-    const int L = v * C::kThreads + tid;
-    const int f = L >> 7, p = L & 127;
-    const int nb = min(n0 / 16 + f, nblk16 - 1);
-    b_src[v] = (size_t)nb * nkb * kFragBytes + p * 16;
-    b_dst[v] = C::kABytes + f * kFragBytes + p * 16;
+  for (int j = 0; j < C::kIN; ++j) b_joff[j] = (min(nbw + j, nfrag - 1) - nbw_c) * nkb * kFragBytes;
+  const int b_lane = lane * 16;
+
+  // The epilogue's scales go to LDS (after the two A stages) at the start, so
+  // their load latency hides behind the K loop: x_scale of the tile's BM rows,
+  // w_scale of its 4*TN columns (clamped at the edges; masked on store).
+  float* s_xs = reinterpret_cast<float*>(lds + 2 * C::kABytes);
+  float* s_ws = s_xs + BM;
+  for (int t = tid; t < BM; t += C::kThreads) {
+    const int row = min(m0 + t, row_end - 1);
+    s_xs[t] = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
   }
+  for (int t = tid; t < C::kBN; t += C::kThreads) {
+    const int col = min(n0 + t, a.n - 1);
+    s_ws[t] = a.w_scale_per_col ? ws[col] : ws[0];
+  }
+
+  // MFMA-order reads: fragment i is rows i*16 .. i*16+15; lane l reads row
+  // i*16 + l%16, chunks 2*(l/16) and 2*(l/16)+1; the swizzle again only depends
+  // on the lane, fragment i adds i*2048.
+  const int rl = lane & 15, cg = 2 * (lane >> 4);
+  const int a_rd0 = wrow * C::kWR * kBK + rl * kBK + ((cg ^ (rl & 7)) << 4);
+  const int a_rd1 = wrow * C::kWR * kBK + rl * kBK + (((cg + 1) ^ (rl & 7)) << 4);
 
   v4f acc[C::kIM][C::kIN];
 #pragma unroll
@@ -122,119 +170,201 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #pragma unroll
     for (int j = 0; j < C::kIN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // MFMA-order read offsets inside a stage
-  int a_rd0[C::kIM], a_rd1[C::kIM];
+  uint4 ra[C::kAVec];                       // A pieces in flight (two K steps ahead)
+  bool ra_valid = true;                     // K-tail mask of the pieces in ra
+  uint4 fb0[2 * C::kIN], fb1[2 * C::kIN];  // B fragment halves: current step, next step
+  // A fragments read ahead from LDS: two ahead with one wavefront per SIMD, one
+  // ahead with two (the second wavefront hides the rest, and registers are halved).
+  constexpr int kFaDepth = WM == 1 ? 3 : 2;
+
+#define HQ_LOAD_A_PIECE(KB, V)                                                                      \
+  ra[V] = KTAIL ? as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[V] + min((KB) * kBK, a_kmax), 0, 0)) \
+                : as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[V], (KB) * kBK, 0))
+#define HQ_STORE_A_PIECE(BUF, V)                                          \
+  *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
+      (!KTAIL || ra_valid) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
+#define HQ_STORE_A_PIECE_V(BUF, V, VALID)                                  \
+  *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
+      (!KTAIL || (VALID)) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
+#define HQ_LOAD_B_HALF(KB, FB, H)                                                                   \
+  FB[H] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + ((H) & 1) * 1024,               \
+                                                         b_joff[(H) >> 1] + (KB) * kFragBytes, 0))
+#define HQ_READ_A(BASE, I, LO, HI)                                         \
+  do {                                                                     \
+    LO = *reinterpret_cast<const uint4*>((BASE) + a_rd0 + (I) * 2048);     \
+    HI = *reinterpret_cast<const uint4*>((BASE) + a_rd1 + (I) * 2048);     \
+  } while (0)
+#define HQ_V8(LO, HI) v8i{(int)LO.x, (int)LO.y, (int)LO.z, (int)LO.w, (int)HI.x, (int)HI.y, (int)HI.z, (int)HI.w}
+
+  // One K step, as kIM slots. Slot i: read an upcoming A fragment from LDS, then memory
+  // operations, then the kIN MFMAs of A fragment i. Slot v < kAVec stores A piece
+  // v of step KB+1 (loaded one step earlier) into the other LDS buffer and reuses
+  // its register for piece v of step KB+2, so every A load has a whole step to
+  // land; slots 0 .. 2*kIN-1 also load the B halves of step KB+1. Loads are never
+  // behind a branch, so the wait counters the compiler inserts stay exact; steps
+  // past the end reload the last one.
+#define HQ_STEP(KB, BUF, FBC, FBN)                                                                     \
+  do {                                                                                                 \
+    const int nb1_ = min((KB) + 1, nkb - 1);                                                           \
+    const int nb2_ = min((KB) + 2, nkb - 1);                                                           \
+    const uint8_t* cur_ = lds + (BUF) * C::kABytes;                                                    \
+    uint4 lo0_, hi0_, lo1_, hi1_, lo2_, hi2_;                                                          \
+    bool st_valid_ = ra_valid;                                                                         \
+    HQ_READ_A(cur_, 0, lo0_, hi0_);                                                                    \
+    if (kFaDepth == 3) HQ_READ_A(cur_, 1, lo1_, hi1_);                                                 \
+    _Pragma("unroll") for (int i = 0; i < C::kIM; ++i) {                                               \
+      if (kFaDepth == 3 && i + 2 < C::kIM) {                                                           \
+        if (i % 3 == 0) HQ_READ_A(cur_, i + 2, lo2_, hi2_);                                            \
+        else if (i % 3 == 1) HQ_READ_A(cur_, i + 2, lo0_, hi0_);                                       \
+        else HQ_READ_A(cur_, i + 2, lo1_, hi1_);                                                       \
+      }                                                                                                \
+      if (kFaDepth == 2 && i + 1 < C::kIM) {                                                           \
+        if (i & 1) HQ_READ_A(cur_, i + 1, lo0_, hi0_);                                                 \
+        else HQ_READ_A(cur_, i + 1, lo1_, hi1_);                                                       \
+      }                                                                                                \
+      if (i < C::kAVec) {                                                                              \
+        HQ_STORE_A_PIECE_V((BUF) ^ 1, i, st_valid_);                                                   \
+        HQ_LOAD_A_PIECE(nb2_, i);                                                                      \
+        if (i == C::kAVec - 1 && KTAIL) ra_valid = nb2_ * kBK + a_c * 16 < K;                          \
+      }                                                                                                \
+      if (i < 2 * C::kIN) HQ_LOAD_B_HALF(nb1_, FBN, i);                                                \
+      const v8i fa_ = kFaDepth == 2 ? ((i & 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo0_, hi0_))                \
+                    : (i % 3 == 0) ? HQ_V8(lo0_, hi0_) : (i % 3 == 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo2_, hi2_); \
+      _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                               \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, \
+                                                                     acc[i][j], WF, XF, 0, 0, 0, 0);   \
+      __builtin_amdgcn_sched_barrier(0);                                                               \
+    }                                                                                                  \
+    __syncthreads();                                                                                   \
+  } while (0)
+
+  // prologue: A(0) to LDS buffer 0, B(0) to registers, A(1) in flight
+#pragma unroll
+  for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(0, v);
+  ra_valid = a_c * 16 < K;
+#pragma unroll
+  for (int h = 0; h < 2 * C::kIN; ++h) HQ_LOAD_B_HALF(0, fb0, h);
+#pragma unroll
+  for (int v = 0; v < C::kAVec; ++v) HQ_STORE_A_PIECE(0, v);
+  {
+    const int nb1 = min(1, nkb - 1);
+#pragma unroll
+    for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(nb1, v);
+    ra_valid = nb1 * kBK + a_c * 16 < K;
+  }
+  __syncthreads();
+  // Two unconditional steps per iteration (LDS buffers and B register sets both
+  // alternate); an odd last step follows the loop, so the loop body has no branch.
+  int kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    HQ_STEP(kb, 0, fb0, fb1);
+    HQ_STEP(kb + 1, 1, fb1, fb0);
+  }
+  if (kb < nkb) HQ_STEP(kb, 0, fb0, fb1);
+#undef HQ_LOAD_A_PIECE
+#undef HQ_STORE_A_PIECE
+#undef HQ_STORE_A_PIECE_V
+#undef HQ_LOAD_B_HALF
+#undef HQ_READ_A
+#undef HQ_V8
+#undef HQ_STEP
+
+  // Epilogue: fragment pair (2*jp, 2*jp+1) gives lane l the 8 consecutive output
+  // columns n0 + wave*TN + 32*jp + 8*(l/16) .. +7 of row m0 + 16*i + l%16.
+  // Scale in fp32, round to bf16 (v_cvt_pk_bf16_f32, nearest-even), store 16 bytes.
+  const bool vec_ok = (a.n & 7) == 0;
+  const int ccol = 8 * (lane >> 4);
+  float wsc[C::kIN / 2][8];
+#pragma unroll
+  for (int jp = 0; jp < C::kIN / 2; ++jp)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wsc[jp][e] = s_ws[wave * TN + 32 * jp + ccol + e];
 #pragma unroll
   for (int i = 0; i < C::kIM; ++i) {
-    const int r = wm * C::kTM + i * 16 + (lane & 15);
-    const int c0 = 2 * (lane >> 4), c1 = c0 + 1;
-    a_rd0[i] = r * kBK + ((c0 ^ (r & 7)) << 4);
-    a_rd1[i] = r * kBK + ((c1 ^ (r & 7)) << 4);
-  }
-  const int b_rd = C::kABytes + (wn * C::kIN) * kFragBytes + lane * 16;
-
-  uint4 ra[C::kAVec], rb[C::kBVec];
-#define HQ_LOAD_STAGE(KB)                                                                              \
-  do {                                                                                                 \
-    const int k0_ = (KB) * kBK;                                                                        \
-    _Pragma("unroll") for (int v = 0; v < C::kAVec; ++v) {                                             \
-      ra[v] = make_uint4(0u, 0u, 0u, 0u);                                                              \
-      if (k0_ + a_col[v] < K) ra[v] = *reinterpret_cast<const uint4*>(a.xq + a_src[v] + k0_);          \
-    }                                                                                                  \
-    _Pragma("unroll") for (int v = 0; v < C::kBVec; ++v)                                               \
-      rb[v] = *reinterpret_cast<const uint4*>(wq + b_src[v] + (size_t)(KB) * kFragBytes);              \
-  } while (0)
-#define HQ_STORE_STAGE(BUF)                                                                            \
-  do {                                                                                                 \
-    uint8_t* base_ = lds + (BUF) * C::kStage;                                                          \
-    _Pragma("unroll") for (int v = 0; v < C::kAVec; ++v) *reinterpret_cast<uint4*>(base_ + a_dst[v]) = ra[v]; \
-    _Pragma("unroll") for (int v = 0; v < C::kBVec; ++v) *reinterpret_cast<uint4*>(base_ + b_dst[v]) = rb[v]; \
-  } while (0)
-
-  HQ_LOAD_STAGE(0);
-  HQ_STORE_STAGE(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) HQ_LOAD_STAGE(kb + 1);
-    const uint8_t* base = lds + cur * C::kStage;
-    v8i fa[C::kIM], fb[C::kIN];
+    const int row = m0 + wrow * C::kWR + i * 16 + (lane & 15);
+    if (row >= row_end) continue;
+    const float xsc = s_xs[wrow * C::kWR + i * 16 + (lane & 15)];
 #pragma unroll
-    for (int i = 0; i < C::kIM; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(base + a_rd0[i]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(base + a_rd1[i]);
-      fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+    for (int jp = 0; jp < C::kIN / 2; ++jp) {
+      const int col0 = n0 + wave * TN + 32 * jp + ccol;
+      if (col0 >= a.n) continue;
+      const v4f p0 = acc[i][2 * jp], p1 = acc[i][2 * jp + 1];
+      const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      uint32_t w[4];
 #pragma unroll
-    for (int j = 0; j < C::kIN; ++j) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(base + b_rd + j * kFragBytes);
-      const uint4 hi = *reinterpret_cast<const uint4*>(base + b_rd + j * kFragBytes + 1024);
-      fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+      for (int e = 0; e < 4; ++e) {
+        const f2v pr = {v[2 * e] * xsc * wsc[jp][2 * e], v[2 * e + 1] * xsc * wsc[jp][2 * e + 1]};
+        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
+      }
+      uint16_t* dst = a.out + (size_t)row * a.n + col0;
+      if (vec_ok && col0 + 8 <= a.n) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
 #pragma unroll
-    for (int i = 0; i < C::kIM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::kIN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], XF, WF, 0, 0, 0, 0);
-    if (kb + 1 < nkb) HQ_STORE_STAGE(cur ^ 1);
-    __syncthreads();
-  }
-#undef HQ_LOAD_STAGE
-#undef HQ_STORE_STAGE
-
-  // epilogue: scale, round to bf16, store (rows past row_end and columns past n masked)
-#pragma unroll
-  for (int j = 0; j < C::kIN; ++j) {
-    const int col = n0 + wn * C::kTN + j * 16 + (lane & 15);
-    if (col >= a.n) continue;
-    const float wsc = a.w_scale_per_col ? ws[col] : ws[0];
-#pragma unroll
-    for (int i = 0; i < C::kIM; ++i) {
-      const int rb0 = m0 + wm * C::kTM + i * 16 + 4 * (lane >> 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rb0 + r;
-        if (row < row_end) {
-          const float xsc = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
-          a.out[(size_t)row * a.n + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] * xsc * wsc);
-        }
+        for (int e = 0; e < 8; ++e)
+          if (col0 + e < a.n) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
       }
     }
   }
 }
 
-template <int XF, int WF, int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmArgs a, int tiles_n) {
-  using C = TileCfg<BM, BN, WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::kStage];
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+// Tile order: with T tiles, a multiple of the 8 XCDs, workgroup b (placed on XCD
+// b % 8 by the dispatcher) takes tile (b % 8) * T/8 + b / 8, so each XCD gets one
+// contiguous run of tiles; tiles are numbered in groups of kGroupM tile rows,
+// column-major inside a group, so a run covers a compact block of A rows and B
+// columns that stays resident in that XCD's L2.
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  return total % 8 == 0 ? (b % 8) * (total / 8) + b / 8 : b;
+}
+
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_m);
+  const int r = t % per_group;
+  *tm = first_m + r % gm;
+  *tn = r / gm;
+}
+
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
+__global__ __launch_bounds__(256 * WM) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  using C = BsCfg<BM, TN, WM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  int tm, tn;
+  tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM;
-  gemm_tile<XF, WF, BM, BN, WAVES_M, WAVES_N>(a, lds, m0, min(a.m, m0 + BM), tn * BN, a.wq_pre, a.w_scale);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
 }
 
 // Grouped: a linear tile id enumerates, per expert in order, its row tiles x the
 // column tiles. Offsets are clamped so any input stays in bounds.
-template <int XF, int WF, int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs a, const int32_t* offsets,
-                                                                              int experts, int tiles_n,
-                                                                              size_t expert_bytes) {
-  using C = TileCfg<BM, BN, WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::kStage];
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
+__global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, const int32_t* offsets, int experts,
+                                                                int tiles_n, size_t expert_bytes) {
+  using C = BsCfg<BM, TN, WM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
   __shared__ int s_sel[3];  // expert, first row, row end
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
   if (threadIdx.x == 0) {
-    const int tm_target = blockIdx.x / tiles_n;
+    const int tm_target = t / tiles_n;
     int acc = 0, lo = 0;
     s_sel[0] = -1;
     for (int e = 0; e < experts; ++e) {
       // clamp to [previous end, m] so the ranges are disjoint and in bounds
       const int b = min(max(offsets[e], lo), a.m);
-      const int t = min(max(offsets[e + 1], b), a.m);
-      lo = t;
-      const int cnt = (t - b + BM - 1) / BM;
+      const int end = min(max(offsets[e + 1], b), a.m);
+      lo = end;
+      const int cnt = (end - b + BM - 1) / BM;
       if (tm_target < acc + cnt) {
         s_sel[0] = e;
         s_sel[1] = b + (tm_target - acc) * BM;
-        s_sel[2] = t;
+        s_sel[2] = end;
         break;
       }
       acc += cnt;
@@ -245,36 +375,69 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
   if (e < 0) return;
   const int m0 = s_sel[1];
   const int row_end = min(s_sel[2], m0 + BM);
-  const int tn = blockIdx.x % tiles_n;
+  const int tn = t % tiles_n;
   const float* ws = a.w_scale + (size_t)e * (a.w_scale_per_col ? a.n : 1);
-  gemm_tile<XF, WF, BM, BN, WAVES_M, WAVES_N>(a, lds, m0, row_end, tn * BN, a.wq_pre + e * expert_bytes, ws);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL>(a, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
 }
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+// Tile choice: the 256 x 256 tile when it still yields about one tile per CU,
+// otherwise 128 x 128.
+static bool use_big_tile(long rows, long n) { return ((rows + 255) / 256) * ((n + 255) / 256) >= 200; }
+
+template <int XF, int WF, int BM, int TN, int WM>
+static hipError_t launch_plain(const GemmArgs& a, hipStream_t st) {
+  using C = BsCfg<BM, TN, WM>;
+  const int tiles_m = (a.m + BM - 1) / BM, tiles_n = (a.n + C::kBN - 1) / C::kBN;
+  if (a.k % kBK == 0)
+    hipLaunchKernelGGL((gemm_kernel<XF, WF, BM, TN, WM, false>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, st, a,
+                       tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_kernel<XF, WF, BM, TN, WM, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, st, a,
+                       tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int XF, int WF, int BM, int TN, int WM>
+static hipError_t launch_grouped_cfg(const GemmArgs& a, const int32_t* offsets, int experts, hipStream_t st) {
+  using C = BsCfg<BM, TN, WM>;
+  const int tiles_n = (a.n + C::kBN - 1) / C::kBN;
+  const int tiles_m = (a.m + BM - 1) / BM + experts;  // bound for any clamped offsets
+  const size_t expert_bytes = (size_t)frag_rows(a.n) * 16 * (size_t)((a.k + kBK - 1) / kBK * kBK);
+  if (a.k % kBK == 0)
+    hipLaunchKernelGGL((grouped_gemm_kernel<XF, WF, BM, TN, WM, false>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       st, a, offsets, experts, tiles_n, expert_bytes);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<XF, WF, BM, TN, WM, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       st, a, offsets, experts, tiles_n, expert_bytes);
+  return hipGetLastError();
+}
+
+#ifndef HQ_BIG_WM
+#define HQ_BIG_WM 2
+#endif
 
 template <int XF, int WF>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
-  const int tiles_m = (a.m + BM - 1) / BM, tiles_n = (a.n + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<XF, WF, BM, BN, 2, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a, tiles_n);
-  return hipGetLastError();
+  if (use_big_tile(a.m, a.n)) return launch_plain<XF, WF, 256, 64, HQ_BIG_WM>(a, st);
+  return launch_plain<XF, WF, 128, 32, 1>(a, st);
 }
 
 template <int XF, int WF>
 static hipError_t launch_grouped_t(const GemmArgs& a, const int32_t* offsets, int experts, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
-  const int tiles_n = (a.n + BN - 1) / BN;
-  const int tiles_m = (a.m + BM - 1) / BM + experts;  // bound for valid offsets
-  const size_t expert_bytes = (size_t)((a.n + 15) / 16 * 16) * (size_t)((a.k + kBK - 1) / kBK * kBK);
-  hipLaunchKernelGGL((grouped_gemm_kernel<XF, WF, BM, BN, 2, 2>), dim3(tiles_m * tiles_n), dim3(256), 0, st, a,
-                     offsets, experts, tiles_n, expert_bytes);
-  return hipGetLastError();
+  if (use_big_tile(a.m, a.n)) return launch_grouped_cfg<XF, WF, 256, 64, HQ_BIG_WM>(a, offsets, experts, st);
+  return launch_grouped_cfg<XF, WF, 128, 32, 1>(a, offsets, experts, st);
 }
 
-#define HQ_DISPATCH_FMT_PAIR(XF, WF, CALL)               \
-  do {                                                   \
-    if ((XF) == kE4M3 && (WF) == kE4M3) { CALL(kE4M3, kE4M3); } \
-    else if ((XF) == kE4M3) { CALL(kE4M3, kE5M2); }       \
-    else if ((WF) == kE4M3) { CALL(kE5M2, kE4M3); }       \
-    else { CALL(kE5M2, kE5M2); }                          \
+#define HQ_DISPATCH_FMT_PAIR(XF, WF, CALL)                        \
+  do {                                                            \
+    if ((XF) == kE4M3 && (WF) == kE4M3) { CALL(kE4M3, kE4M3); }   \
+    else if ((XF) == kE4M3) { CALL(kE4M3, kE5M2); }               \
+    else if ((WF) == kE4M3) { CALL(kE5M2, kE4M3); }               \
+    else { CALL(kE5M2, kE5M2); }                                  \
   } while (0)
 
 hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, hipStream_t st) {

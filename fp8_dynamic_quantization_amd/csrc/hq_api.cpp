@@ -104,7 +104,7 @@ hq_status launched(hipError_t e, const char* what) {
 
 bool valid_fmt(int f) { return f == HQ_E4M3 || f == HQ_E5M2; }
 
-int64_t padded_bytes(int64_t n, int64_t k) { return ((n + 15) / 16 * 16) * ((k + 127) / 128 * 128); }
+int64_t padded_bytes(int64_t n, int64_t k) { return ((n + 31) / 32 * 32) * ((k + 127) / 128 * 128); }
 
 hq_status check_ring(const hq_ring* ring) {
   if (!ring->state) return fail(HQ_ERR_INVALID_ARGUMENT, "ring->state is NULL");
@@ -252,8 +252,8 @@ static hq_status check_gemm_common(int xf, int wf, int64_t m, int64_t n, int64_t
   if (!valid_fmt(xf) || !valid_fmt(wf)) return fail(HQ_ERR_INVALID_ARGUMENT, "xf and wf must be HQ_E4M3 or HQ_E5M2");
   if (m < 0 || m > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "m must be in [0, 2^31), got %lld", (long long)m);
   if (n < 0 || n > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31), got %lld", (long long)n);
-  if (k < 16 || k > kI32Max || k % 16 != 0)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16 below 2^31, got %lld", (long long)k);
+  if (k < 16 || k >= (1 << 24) || k % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16 below 2^24, got %lld", (long long)k);
   if ((double)((m + 127) / 128) * (double)((n + 127) / 128) > 1.0e9)
     return fail(HQ_ERR_INVALID_ARGUMENT, "output too large for one launch");
   return HQ_OK;

@@ -130,15 +130,17 @@ hq_status hq_scale_ring_update(const hq_ring* ring, const float* amax, int fmt,
                                hipStream_t stream);
 
 /* Bytes of the pre-shuffled form of an [n, k] FP8 weight:
- * ceil(n/16)*16 * ceil(k/128)*128. Returns -1 for invalid sizes. */
+ * ceil(n/32)*32 * ceil(k/128)*128. Returns -1 for invalid sizes. */
 int64_t hq_preshuffled_bytes(int64_t n, int64_t k);
 
 /* Reorder a row-major FP8 weight WQ [n, k] into the GEMM's pre-shuffled layout
  * (the aiter PR has the GEMM read a pre-shuffled, optionally K-padded weight;
- * the order is this library's): 16-row x 128-column fragments of 2048 bytes,
- * fragment (nb, kb) at byte (nb * ceil(k/128) + kb) * 2048, and inside it the
- * byte of (n_in, k_in) at h*1024 + (g*16 + n_in)*16 + b with g = k_in/32,
- * h = (k_in%32)/16, b = k_in%16. Padding bytes are written as 0.
+ * the order is this library's). n is padded to a multiple of 32 and k to a
+ * multiple of 128 with zero bytes. Row n = 32*G + 8*g + 4*p + r (g < 4, p < 2,
+ * r < 4) becomes slot s = 4*g + r of fragment nb = 2*G + p; fragment (nb, kb)
+ * holds 16 slots x 128 columns at byte (nb * ceil(k/128) + kb) * 2048, and the
+ * byte of (slot s, column k_in) sits at h*1024 + (q*16 + s)*16 + b with
+ * q = k_in/32, h = (k_in%32)/16, b = k_in%16.
  *   wq      device, uint8 [n, k] row-major, 16-byte aligned, k % 16 == 0
  *   wq_pre  device, hq_preshuffled_bytes(n, k) bytes, 16-byte aligned */
 hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
@@ -154,7 +156,7 @@ hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
  *   w_scale   device, float32 [w_scale_count], w_scale_count = 1 or n
  *   out       device, bf16 bits [m, n] dense row-major, 16-byte aligned; must not
  *             overlap any input. Written in full; nothing else is touched.
- * Requires k % 16 == 0, 1 <= k, m, n < 2^31. m == 0 or n == 0 returns HQ_OK
+ * Requires k % 16 == 0, 16 <= k < 2^24, m, n < 2^31. m == 0 or n == 0 returns HQ_OK
  * without a launch (aiter PR: an empty out is a no-op). */
 hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                        const float* x_scale, int64_t x_scale_count,
@@ -177,7 +179,7 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
  *                  offsets[num_experts] = total_rows (precondition; clamped)
  *   out            device, bf16 bits [total_rows, n], 16-byte aligned. Rows of
  *                  no group are left untouched.
- * Requires 1 <= num_experts <= 1024, k % 16 == 0. total_rows == 0 or n == 0
+ * Requires 1 <= num_experts <= 1024, k % 16 == 0, 16 <= k < 2^24. total_rows == 0 or n == 0
  * returns HQ_OK without a launch. */
 hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
                                int wf, const float* x_scale, int64_t x_scale_count,

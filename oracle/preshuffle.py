@@ -7,19 +7,18 @@ the GEMM read a weight WQ [N, K] that was pre-shuffled into a kernel-friendly
 order, and allows a K-padded WQ; it does not print the order. The order below
 is this library's own, written from its specification (not from kernel code):
 
-  * N is padded with zero rows to NP = ceil(N / 16) * 16 and K with zero
+  * N is padded with zero rows to NP = ceil(N / 32) * 32 and K with zero
     columns to KP = ceil(K / 128) * 128.
-  * The padded matrix is cut into fragments of 16 rows x 128 columns
-    (2048 bytes). Fragment (nb, kb) starts at byte (nb * (KP / 128) + kb) * 2048,
-    so one 16-row block is contiguous along K.
-  * Inside a fragment, the byte of row n_in (0..15) and column k_in (0..127)
-    sits at   h * 1024 + lane * 16 + b   where
-        g    = k_in // 32          (which quarter of the 128 columns)
-        h    = (k_in % 32) // 16   (which 16-byte half of that quarter)
-        b    = k_in % 16
-        lane = g * 16 + n_in.
-    A 64-lane wavefront therefore reads one half-fragment as 64 consecutive
-    16-byte pieces, lane l getting row l % 16 and columns 32*(l//16) + 16*h ..+15.
+  * Each group of 32 rows (output channels) n = 32*G + n32 is split over two
+    fragments of 16 "slots": with n32 = 8*g + 4*p + r (g in 0..3, p in 0..1,
+    r in 0..3) the row goes to fragment nb = 2*G + p, slot s = 4*g + r.
+  * Fragment (nb, kb) covers slots 0..15 and columns kb*128 .. kb*128+127 and
+    starts at byte (nb * (KP / 128) + kb) * 2048, so one fragment row block is
+    contiguous along K.
+  * Inside a fragment, the byte of slot s and column k_in (0..127) sits at
+        h * 1024 + (q * 16 + s) * 16 + b
+    with q = k_in // 32, h = (k_in % 32) // 16, b = k_in % 16. A 64-lane
+    wavefront reads one half-fragment as 64 consecutive 16-byte pieces.
 
 Padding bytes are 0x00 (+0.0 in both FP8 formats).
 """
@@ -28,12 +27,13 @@ from __future__ import annotations
 import numpy as np
 
 FRAG_N = 16
+GROUP_N = 32
 FRAG_K = 128
 FRAG_BYTES = FRAG_N * FRAG_K
 
 
 def padded_dims(n: int, k: int):
-    np_ = -(-n // FRAG_N) * FRAG_N
+    np_ = -(-n // GROUP_N) * GROUP_N
     kp = -(-k // FRAG_K) * FRAG_K
     return np_, kp
 
@@ -49,13 +49,15 @@ def offset_of(n_idx, k_idx, k: int):
     k_idx = np.asarray(k_idx, dtype=np.int64)
     _, kp = padded_dims(1, k)
     kblocks = kp // FRAG_K
-    nb, n_in = n_idx // FRAG_N, n_idx % FRAG_N
+    grp, n32 = n_idx // GROUP_N, n_idx % GROUP_N
+    g, p, r = n32 // 8, (n32 // 4) % 2, n32 % 4
+    nb = 2 * grp + p
+    slot = 4 * g + r
     kb, k_in = k_idx // FRAG_K, k_idx % FRAG_K
-    g = k_in // 32
+    q = k_in // 32
     h = (k_in % 32) // 16
     b = k_in % 16
-    lane = g * 16 + n_in
-    return (nb * kblocks + kb) * FRAG_BYTES + h * 1024 + lane * 16 + b
+    return (nb * kblocks + kb) * FRAG_BYTES + h * 1024 + (q * 16 + slot) * 16 + b
 
 
 def preshuffle(wq: np.ndarray) -> np.ndarray:

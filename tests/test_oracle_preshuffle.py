@@ -28,18 +28,35 @@ def test_round_trip_and_padding(n, k):
 
 
 def test_hand_derived_positions():
-    k = 256  # two 128-column blocks per 16-row block
+    k = 256  # two 128-column blocks per fragment row block
     cases = {
         (0, 0): 0,
-        (1, 0): 16,            # next lane
-        (0, 1): 1,             # next byte in the lane
+        (1, 0): 16,            # next slot
+        (0, 1): 1,             # next byte in the slot's piece
         (0, 16): 1024,         # second 16-byte half of the first quarter
-        (0, 32): 256,          # quarter 1 -> lane 16
-        (0, 96): 768,          # quarter 3 -> lane 48
-        (15, 127): 2047,       # last byte of a fragment
-        (0, 128): 2048,        # next K block of the same rows
-        (16, 0): 4096,         # next 16-row block (after 2 K blocks)
-        (17, 130): 4096 + 2048 + 16 + 2,
+        (0, 32): 256,          # quarter 1 -> piece 16
+        (0, 96): 768,          # quarter 3 -> piece 48
+        (8, 0): 64,            # n32 = 8: g = 1 -> slot 4
+        (4, 0): 4096,          # n32 = 4: p = 1 -> second fragment of the group
+        (31, 127): 6143,       # g 3, p 1, r 3 -> fragment 1 slot 15, last byte
+        (0, 128): 2048,        # next K block of the same fragment
+        (32, 0): 8192,         # next 32-row group -> fragment 2
+        (13, 130): 6226,       # g 1, p 1, r 1 -> fragment 1 slot 5, K block 1, byte 2
     }
     for (n, kk), off in cases.items():
         assert int(P.offset_of(n, kk, k)) == off, (n, kk)
+
+
+def test_fragment_pair_holds_eight_consecutive_rows_per_slot_quad():
+    """Slots 4g..4g+3 of the two fragments of a 32-row group hold rows
+    8g .. 8g+7 of the group: first 4 in fragment 0, next 4 in fragment 1."""
+    k = 128
+    for g in range(4):
+        rows = []
+        for p_ in range(2):
+            for r in range(4):
+                slot = 4 * g + r
+                off = p_ * 2048 + slot * 16     # k = 0 of fragment p_
+                n = [n for n in range(32) if int(P.offset_of(n, 0, k)) == off]
+                rows.append(n[0])
+        assert rows == list(range(8 * g, 8 * g + 8))
