@@ -24,9 +24,10 @@
 // keeps the row-wise stores and the MFMA-order reads free of bank conflicts.
 // Wavefront w owns TN columns and streams their pre-shuffled B fragments from
 // global memory straight into registers (each fragment half is one coalesced
-// 1 KB load), so B never touches LDS. Tails: rows past M are clamped on load
-// and masked on store; fragments past the padded N are clamped on load and their
-// columns masked on store; the K tail of A is zeroed (B is zero-padded).
+// 1 KB load), so B never touches LDS. Tails: A rows past the tile's last row and
+// B fragments past the padded N fall outside their buffer resource's extent and
+// read as zero, and their outputs are masked on store; the K tail of A is zeroed
+// on its way to LDS (B is zero-padded).
 #include "hq_device.h"
 #include "hq_launch.h"
 
@@ -104,7 +105,7 @@ template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m0, int row_end, int n0,
                                           const uint8_t* __restrict__ wq, const float* __restrict__ ws) {
   using C = BsCfg<BM, TN, WM>;
-  static_assert(C::kAVec <= C::kIM && 2 * C::kIN <= C::kIM, "slot schedule: one A piece and one B half per slot");
+  static_assert(C::kAVec <= C::kIM && C::kIN <= C::kIM, "slot schedule: at most one A piece and two B halves per slot");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront column
@@ -118,30 +119,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // shares one LDS offset plus a compile-time v*kRowStep*128.
   const int a_c = tid & 7, a_r = tid >> 3;
   const int a_dst = a_r * kBK + ((a_c ^ (a_r & 7)) << 4);
-  const int a_kmax = K - 16 - a_c * 16;  // largest in-row offset of this thread's chunk
-  // Global loads are buffer loads: a resource descriptor (base + extent) in
-  // scalar registers, a 32-bit per-lane offset that stays fixed for the whole K
-  // loop and a wavefront-uniform offset that carries the K step, so the loop
-  // keeps no 64-bit addresses in vector registers.
-  // A: offsets from the tile's first row (K < 2^24 keeps BM*K below 2^32); rows
-  // past row_end are clamped to the last valid row.
-  const int a_rmax = row_end - 1 - m0;
+
+  // Global loads are buffer loads: a resource (base and extent in bytes) in
+  // scalar registers, one 32-bit per-lane offset that stays fixed for the whole
+  // K loop, and a wavefront-uniform offset that carries the piece and the K
+  // step. A load reads zero for every dword at or past the extent (the per-lane
+  // and uniform offsets both count), which covers all tails without clamping:
+  // A rows past row_end and B fragments past the padded N read zero, and their
+  // outputs are masked on store. K < 2^24 keeps every offset below 2^32.
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.xq + (size_t)m0 * K), (short)0, (a_rmax + 1) * K, kRsrcFlags);
-  uint32_t a_off[C::kAVec];
-#pragma unroll
-  for (int v = 0; v < C::kAVec; ++v) a_off[v] = (uint32_t)min(v * C::kRowStep + a_r, a_rmax) * (uint32_t)K + a_c * 16;
-  // B: one resource on the wavefront's first fragment row; fragment j (clamped
-  // to the last one) sits b_joff[j] bytes further, a uniform offset.
+      (void*)(a.xq + (size_t)m0 * K), (short)0, (row_end - m0) * K, kRsrcFlags);
+  const int a_vo = a_r * K + a_c * 16;
   const int nbw = __builtin_amdgcn_readfirstlane((n0 + wave * TN) / 16);
-  const int nbw_c = min(nbw, nfrag - 1);
+  const int nbw_c = min(nbw, nfrag);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(wq + (size_t)nbw_c * nkb * kFragBytes), (short)0, min(C::kIN, nfrag - nbw_c) * nkb * kFragBytes,
       kRsrcFlags);
-  int b_joff[C::kIN];
-#pragma unroll
-  for (int j = 0; j < C::kIN; ++j) b_joff[j] = (min(nbw + j, nfrag - 1) - nbw_c) * nkb * kFragBytes;
-  const int b_lane = lane * 16;
+  const int b_vo = lane * 16;
 
   // The epilogue's scales go to LDS (after the two A stages) at the start, so
   // their load latency hides behind the K loop: x_scale of the tile's BM rows,
@@ -177,18 +171,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // ahead with two (the second wavefront hides the rest, and registers are halved).
   constexpr int kFaDepth = WM == 1 ? 3 : 2;
 
-#define HQ_LOAD_A_PIECE(KB, V)                                                                      \
-  ra[V] = KTAIL ? as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[V] + min((KB) * kBK, a_kmax), 0, 0)) \
-                : as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[V], (KB) * kBK, 0))
+#define HQ_LOAD_A_PIECE(KB, V) \
+  ra[V] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_vo, (V) * C::kRowStep * K + (KB) * kBK, 0))
 #define HQ_STORE_A_PIECE(BUF, V)                                          \
   *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
       (!KTAIL || ra_valid) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
 #define HQ_STORE_A_PIECE_V(BUF, V, VALID)                                  \
   *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
       (!KTAIL || (VALID)) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
-#define HQ_LOAD_B_HALF(KB, FB, H)                                                                   \
-  FB[H] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + ((H) & 1) * 1024,               \
-                                                         b_joff[(H) >> 1] + (KB) * kFragBytes, 0))
+#define HQ_LOAD_B_HALF(KB, FB, H)                                                                 \
+  FB[H] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_vo + ((H) & 1) * 1024,               \
+                                                         ((H) >> 1) * nkb * kFragBytes + (KB) * kFragBytes, 0))
 #define HQ_READ_A(BASE, I, LO, HI)                                         \
   do {                                                                     \
     LO = *reinterpret_cast<const uint4*>((BASE) + a_rd0 + (I) * 2048);     \
@@ -197,12 +190,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #define HQ_V8(LO, HI) v8i{(int)LO.x, (int)LO.y, (int)LO.z, (int)LO.w, (int)HI.x, (int)HI.y, (int)HI.z, (int)HI.w}
 
   // One K step, as kIM slots. Slot i: read an upcoming A fragment from LDS, then memory
-  // operations, then the kIN MFMAs of A fragment i. Slot v < kAVec stores A piece
-  // v of step KB+1 (loaded one step earlier) into the other LDS buffer and reuses
-  // its register for piece v of step KB+2, so every A load has a whole step to
-  // land; slots 0 .. 2*kIN-1 also load the B halves of step KB+1. Loads are never
-  // behind a branch, so the wait counters the compiler inserts stay exact; steps
-  // past the end reload the last one.
+  // operations, then the kIN MFMAs of A fragment i. Slots 0 .. kIN-1 load the B
+  // halves of step KB+1 (two each), as early as possible, since step KB+1 needs
+  // them in its first slot. The last kAVec slots each store one A piece of step
+  // KB+1 (loaded one step earlier) into the other LDS buffer and reuse its
+  // register for the same piece of step KB+2, so every A load has a whole step to
+  // land. Loads are never behind a branch, so the wait counters the compiler
+  // inserts stay exact; steps past the end reload the last one.
 #define HQ_STEP(KB, BUF, FBC, FBN)                                                                     \
   do {                                                                                                 \
     const int nb1_ = min((KB) + 1, nkb - 1);                                                           \
@@ -222,12 +216,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
         if (i & 1) HQ_READ_A(cur_, i + 1, lo0_, hi0_);                                                 \
         else HQ_READ_A(cur_, i + 1, lo1_, hi1_);                                                       \
       }                                                                                                \
-      if (i < C::kAVec) {                                                                              \
-        HQ_STORE_A_PIECE_V((BUF) ^ 1, i, st_valid_);                                                   \
-        HQ_LOAD_A_PIECE(nb2_, i);                                                                      \
-        if (i == C::kAVec - 1 && KTAIL) ra_valid = nb2_ * kBK + a_c * 16 < K;                          \
+      if (i < C::kIN) {                                                                                \
+        HQ_LOAD_B_HALF(nb1_, FBN, 2 * i);                                                              \
+        HQ_LOAD_B_HALF(nb1_, FBN, 2 * i + 1);                                                          \
       }                                                                                                \
-      if (i < 2 * C::kIN) HQ_LOAD_B_HALF(nb1_, FBN, i);                                                \
+      if (i >= C::kIM - C::kAVec) {                                                                    \
+        const int v_ = i - (C::kIM - C::kAVec);                                                        \
+        HQ_STORE_A_PIECE_V((BUF) ^ 1, v_, st_valid_);                                                  \
+        HQ_LOAD_A_PIECE(nb2_, v_);                                                                     \
+        if (v_ == C::kAVec - 1 && KTAIL) ra_valid = nb2_ * kBK + a_c * 16 < K;                         \
+      }                                                                                                \
       const v8i fa_ = kFaDepth == 2 ? ((i & 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo0_, hi0_))                \
                     : (i % 3 == 0) ? HQ_V8(lo0_, hi0_) : (i % 3 == 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo2_, hi2_); \
       _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                               \
