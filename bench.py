@@ -14,6 +14,12 @@ HIP events on the stream it runs on. ``cpu_baseline`` times the CPU oracle on a
 bounded sample (see --cpu-rows) and scales it to the same unit.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+
+Helpers for the rocprofv3 summaries kept with the sources (they read
+``--output-format csv`` output and run on any host):
+
+    python bench.py --summarize DIR            # markdown table of a trace/PMC run
+    python bench.py --write-traffic NAME KERNEL FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 """
 from __future__ import annotations
 
@@ -32,6 +38,8 @@ METRIC = "a8w8 GEMM TFLOP/s + quantize GB/s (% of MI355X roofline), PTPC 4096³"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 M = N = K = 4096
+COPY_PROBE_BYTES = 1 << 30
+COPY_PROBE_KERNEL = "bitwise_not"
 KERNEL_SOURCES = ["fp8_dynamic_quantization_amd/csrc/gemm.hip", "fp8_dynamic_quantization_amd/csrc/quantize.hip",
                   "fp8_dynamic_quantization_amd/csrc/hq_device.h"]
 
@@ -158,7 +166,89 @@ def cpu_baseline(rows: int):
     }
 
 
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize(directory):
+    """Markdown summary of a rocprofv3 run (--output-format csv): per-kernel
+    statistics of a --kernel-trace --stats run and/or per-dispatch means of the
+    counters of a --pmc run."""
+    lines = []
+    stats = _csv_rows(directory, "kernel_stats.csv")
+    if stats:
+        lines += ["| kernel | calls | average us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
+        for r in stats:
+            lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f} |")
+    counters = _csv_rows(directory, "counter_collection.csv")
+    if counters:
+        agg = {}
+        for r in counters:
+            key = (r["Kernel_Name"][:110], r["Counter_Name"])
+            d = agg.setdefault(key, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        lines += ["", "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---:|---:|"]
+        for (k, c), d in sorted(agg.items()):
+            lines.append(f"| `{k}` | {c} | {len(d)} | {sum(d.values()) / len(d):.1f} |")
+    return "\n".join(lines)
+
+
+def counter_mean(directory, counter, kernel_substr):
+    """Mean per dispatch of `counter` over the dispatches whose kernel name
+    contains `kernel_substr`."""
+    per = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} under {directory}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_traffic(name, kernel_substr, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per launch of one kernel from FETCH_SIZE / WRITE_SIZE runs
+    (KiB per dispatch), each scaled by what the same counter reads for the copy
+    probe (COPY_PROBE_BYTES read and written per dispatch)."""
+    fetch, nf = counter_mean(fetch_dir, "FETCH_SIZE", kernel_substr)
+    write, nw = counter_mean(write_dir, "WRITE_SIZE", kernel_substr)
+    cfetch, _ = counter_mean(copy_fetch_dir, "FETCH_SIZE", COPY_PROBE_KERNEL)
+    cwrite, _ = counter_mean(copy_write_dir, "WRITE_SIZE", COPY_PROBE_KERNEL)
+    f_read = COPY_PROBE_BYTES / (cfetch * 1024.0)
+    f_write = COPY_PROBE_BYTES / (cwrite * 1024.0)
+    read_b = fetch * 1024.0 * f_read
+    write_b = write * 1024.0 * f_write
+    out = {
+        "kernel": kernel_substr,
+        "source_hash": source_hash(),
+        "fetch_kib_per_dispatch": round(fetch, 1), "fetch_dispatches": nf,
+        "write_kib_per_dispatch": round(write, 1), "write_dispatches": nw,
+        "copy_probe_fetch_kib": round(cfetch, 1), "copy_probe_write_kib": round(cwrite, 1),
+        "read_scale": round(f_read, 5), "write_scale": round(f_write, 5),
+        "read_bytes_per_launch": round(read_b), "write_bytes_per_launch": round(write_b),
+        "bytes_per_launch": round(read_b + write_b),
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        print(summarize(sys.argv[2]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
+        print(json.dumps(write_traffic(*sys.argv[2:8])))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -188,12 +278,14 @@ def main():
     torch.cuda.set_device(0)
 
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # An elementwise kernel that reads 1 GiB and writes 1 GiB (a plain
+        # memcpy may go to a DMA engine, which the shader counters miss).
+        src = torch.zeros(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
-        log("copy probe: 3 x 1 GiB device copies")
+        log(f"copy probe: 3 x bitwise_not over {COPY_PROBE_BYTES} bytes")
         return
 
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
