@@ -5,8 +5,8 @@ of entries x50, W bf16 [4096, 4096] N(0, 0.02^2). One step is one pass of the
 whole path: per-token E4M3 quantization of X, per-output-channel E4M3
 quantization of W (row reduction on [N, K]), pre-shuffle of WQ, and the a8w8
 GEMM M = N = K = 4096 into bf16. Inputs are resident in HBM before timing;
-``--rotate`` input/output sets (default 4, ~600 MB) cycle so that no step hits
-data left in the 256 MB Infinity Cache by the previous one.
+``--rotate`` input/output sets (default 8, ~1.2 GB) cycle so that neither a step
+nor a single kernel's timing loop finds its data in the 256 MB Infinity Cache.
 
 Prints one JSON line (stdout). ``value`` = 2*M*N*K / step time (TFLOP/s of the
 whole step). ``roofline`` refers to the dominant kernel (the GEMM), timed with
@@ -166,6 +166,117 @@ def cpu_baseline(rows: int):
     }
 
 
+def time_graph(torch, launch, reps, replays=5):
+    """Average duration (ms) of one launch: `reps` launches captured in a HIP
+    graph (launch(i, stream_handle)), replayed back to back, so host launch
+    overhead does not hide short kernels."""
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(reps):
+            launch(i, h)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (replays * reps)
+
+
+def other_workloads(torch, hq, lib, reps):
+    """Decode-skinny GEMM, grouped MoE GEMM and per-tensor / per-channel
+    quantize, each timed on rotating buffers larger than the Infinity Cache."""
+    import numpy as np
+
+    import workloads
+    P = ctypes.c_void_p
+    E4M3, BF16 = hq.HQ_E4M3, hq.HQ_BF16
+    res = {}
+
+    # decode: X [m, 7168] x W [2048, 7168], 24 weight copies (353 MB)
+    dn, dk, copies = 2048, 7168, 24
+    dec = {}
+    for m in (1, 8, 32):
+        x, w = workloads.decode_skinny(m)
+        gx, gxs, _ = hq.hq_quantize_fp8(torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16), E4M3,
+                                        hq.HQ_PER_TOKEN)
+        if m == 1:
+            gw, gws, _ = hq.hq_quantize_fp8(torch.from_numpy(w.view("int16")).cuda().view(torch.bfloat16), E4M3,
+                                            hq.HQ_PER_TOKEN)
+            pre = hq.hq_preshuffle_weight(gw)
+            pres = [pre.clone() for _ in range(copies)]
+            del gw
+        out = torch.empty((m, dn), dtype=torch.bfloat16, device="cuda")
+
+        def launch(i, h, gx=gx, gxs=gxs, out=out, m=m):
+            st = lib.hq_gemm_a8w8(P(gx.data_ptr()), E4M3, P(pres[i % copies].data_ptr()), E4M3, P(gxs.data_ptr()),
+                                  m, P(gws.data_ptr()), dn, m, dn, dk, P(out.data_ptr()), h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, launch, 2 * copies)
+        alg = dn * dk + m * dk + 2 * m * dn + 4 * (m + dn)
+        dec[f"m{m}"] = {"us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}
+    res["decode_skinny"] = {"shape": "M in {1,8,32}, N=2048, K=7168, per-token x per-channel E4M3",
+                            "rotating_weight_copies": copies, **dec}
+    del pres
+
+    # grouped MoE: 8 experts, N=2048, K=1024, 8192 rows; 5 rotating sets
+    x, w, offs = workloads.grouped_moe()
+    e_, gn, gk = w.shape
+    t = x.shape[0]
+    gx, gxs, _ = hq.hq_quantize_fp8(torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16), E4M3,
+                                    hq.HQ_PER_TOKEN)
+    gw, gws, _ = hq.hq_quantize_fp8(torch.from_numpy(w.reshape(e_ * gn, gk).view("int16")).cuda()
+                                    .view(torch.bfloat16), E4M3, hq.HQ_PER_TOKEN)
+    pre = torch.cat([hq.hq_preshuffle_weight(gw[i * gn:(i + 1) * gn]) for i in range(e_)])
+    off_d = torch.from_numpy(offs).cuda()
+    gsets = [(gx.clone(), pre.clone(), torch.empty((t, gn), dtype=torch.bfloat16, device="cuda"))
+             for _ in range(5)]
+
+    def glaunch(i, h):
+        a, b, o = gsets[i % len(gsets)]
+        st = lib.hq_grouped_gemm_a8w8(P(a.data_ptr()), E4M3, P(b.data_ptr()), E4M3, P(gxs.data_ptr()), t,
+                                      P(gws.data_ptr()), e_ * gn, P(off_d.data_ptr()), e_, t, gn, gk,
+                                      P(o.data_ptr()), h)
+        assert st == 0, hq.hq_last_error()
+    ms = time_graph(torch, glaunch, 10)
+    nonempty = int(np.count_nonzero(np.diff(offs)))
+    flops = 2.0 * t * gn * gk
+    alg = t * gk + nonempty * gn * gk + 2 * t * gn + 4 * (t + e_ * gn)
+    res["grouped_moe"] = {"shape": f"{e_} experts ({nonempty} non-empty), N={gn}, K={gk}, {t} rows",
+                          "us": round(ms * 1e3, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                          "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                          "gbs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg}
+    del gsets, gw, pre
+
+    # quantize of the PTPC X [4096, 4096] bf16 at the other two granularities
+    x, _ = workloads.ptpc_square(1)
+    xs_ = [torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16) for _ in range(8)]
+    q = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in range(8)]
+    qv = {}
+    for name, gran in (("per_tensor", hq.HQ_PER_TENSOR), ("per_channel", hq.HQ_PER_CHANNEL)):
+        cnt = int(lib.hq_scale_count(gran, M, K))
+        so = torch.empty(cnt, dtype=torch.float32, device="cuda")
+        ao = torch.empty(cnt, dtype=torch.float32, device="cuda")
+        wsb = int(lib.hq_quantize_workspace_bytes(gran, M, K))
+        wsp = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+        def qlaunch(i, h, gran=gran, so=so, ao=ao, wsp=wsp, wsb=wsb):
+            st = lib.hq_quantize_fp8(P(xs_[i % 8].data_ptr()), BF16, M, K, E4M3, gran, P(q[i % 8].data_ptr()),
+                                     P(so.data_ptr()), P(ao.data_ptr()), None, P(wsp.data_ptr()), wsb, h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, qlaunch, 24)
+        alg = M * K * 3 + 8 * cnt
+        qv[name] = {"us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}
+    res["quantize_x_other_granularities"] = {"shape": "X bf16 [4096,4096] -> E4M3", **qv}
+    return res
+
+
 def _csv_rows(directory, suffix):
     import csv
     import glob
@@ -253,10 +364,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled to defeat the MALL")
+    ap.add_argument("--rotate", type=int, default=8, help="input/output sets cycled to defeat the MALL")
     ap.add_argument("--kernel-reps", type=int, default=100)
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the decode / grouped / quantize-variant timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC calibration) and exit")
     args = ap.parse_args()
@@ -323,6 +435,16 @@ def main():
     gemm_tflops = flops / (kms["gemm"] * 1e-3) / 1e12
     quant_gbs = quant_bytes / (kms["quant_x"] * 1e-3) / 1e9
 
+    # practical HBM ceiling: an elementwise read+write pass over 2 x 512 MiB
+    src = torch.zeros(1 << 29, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = time_kernel(torch, lambda _: torch.bitwise_not(src, out=dst), [None], 5)
+    copy_gbs = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
+    log(f"  copy probe: {copy_gbs:.0f} GB/s")
+    del src, dst
+    other = None if args.no_other else other_workloads(torch, hq, lib, args.kernel_reps)
+    if other:
+        log(json.dumps(other))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_rows)
 
     out = {
@@ -365,6 +487,8 @@ def main():
             "traffic": traffic_from_profile("quant_rows_ptpc4096"),
         },
         "preshuffle_gbs": round(pre_alg_bytes / (kms["preshuffle"] * 1e-3) / 1e9, 1),
+        "copy_probe_gbs": round(copy_gbs, 1),
+        "other_workloads": other,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -379,6 +379,120 @@ __global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, cons
 }
 
 // ---------------------------------------------------------------------------
+// skinny M (decode): weight streaming
+// ---------------------------------------------------------------------------
+// For M <= 64 the GEMM is bound by reading WQ once. A workgroup of kSkWaves
+// wavefronts owns one 16-slot weight fragment row (16 output columns) and the
+// whole K; wavefront w takes the K blocks w, w + kSkWaves, ... so the
+// workgroup reads its fragment row (contiguous along K) front to back. A
+// wavefront issues every load of a chunk of KPW K blocks before its first
+// MFMA, so a CU keeps up to kSkWaves * KPW * (2 + 2*MB) KB in flight; the
+// weight fragment is the MFMA's first operand and MB 16-row activation
+// fragments the second. The per-wavefront partial sums are added in LDS in a
+// fixed order (wavefront 0 first), then scaled and stored as bf16.
+constexpr int kSkWaves = 16;
+constexpr int kBadOffset = int(0x80000000u);  // past any extent: the buffer load reads zero
+
+template <int XF, int WF, int MB, int KPW>
+__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) float red[kSkWaves][MB][64][4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = blockIdx.x;  // fragment row
+  const int K = a.k, nkb = (K + kBK - 1) / kBK;
+  // B: the fragment row's nkb * 2048 bytes; blocks past nkb read zero.
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.wq_pre + (size_t)nb * nkb * kFragBytes), (short)0, nkb * kFragBytes, kRsrcFlags);
+  // X: rows past M read zero through the extent; columns past K are sent past
+  // the extent too (they would otherwise read the next row).
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, a.m * K, kRsrcFlags);
+  const int xr = lane & 15, xc = 32 * (lane >> 4);
+
+  v4f acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunks = (nkb + kSkWaves * KPW - 1) / (kSkWaves * KPW);
+  for (int c = 0; c < nchunks; ++c) {
+    uint4 fb[KPW][2], fx[KPW][MB][2];
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int kb = (c * KPW + j) * kSkWaves + wave;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fb[j][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, lane * 16 + h * 1024, kb * kFragBytes, 0));
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = kb * kBK + xc + 16 * h;
+          const int vo = col < K ? (i * 16 + xr) * K + col : kBadOffset;
+          fx[j][i][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(x_rsrc, vo, 0, 0));
+        }
+    }
+    // keep every load of the chunk ahead of its first MFMA
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const v8i bw = v8i{(int)fb[j][0].x, (int)fb[j][0].y, (int)fb[j][0].z, (int)fb[j][0].w,
+                         (int)fb[j][1].x, (int)fb[j][1].y, (int)fb[j][1].z, (int)fb[j][1].w};
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const v8i xa = v8i{(int)fx[j][i][0].x, (int)fx[j][i][0].y, (int)fx[j][i][0].z, (int)fx[j][i][0].w,
+                           (int)fx[j][i][1].x, (int)fx[j][i][1].y, (int)fx[j][i][1].z, (int)fx[j][i][1].w};
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw, xa, acc[i], WF, XF, 0, 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i) *reinterpret_cast<v4f*>(&red[wave][i][lane][0]) = acc[i];
+  __syncthreads();
+  if (wave >= MB) return;
+  // Wavefront i adds up activation block i: lane l holds row 16*i + l%16 and
+  // weight slots 4*(l/16) .. +3 = output columns 32*(nb/2) + 8*(l/16) + 4*(nb%2) .. +3.
+  v4f sum = *reinterpret_cast<const v4f*>(&red[0][wave][lane][0]);
+#pragma unroll
+  for (int w = 1; w < kSkWaves; ++w) {
+    const v4f t = *reinterpret_cast<const v4f*>(&red[w][wave][lane][0]);
+    sum = v4f{sum[0] + t[0], sum[1] + t[1], sum[2] + t[2], sum[3] + t[3]};
+  }
+  const int row = wave * 16 + xr;
+  const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
+  if (row >= a.m || col0 >= a.n) return;
+  const float xsc = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
+  uint32_t w2[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c0 = min(col0 + 2 * e, a.n - 1), c1 = min(col0 + 2 * e + 1, a.n - 1);
+    const float ws0 = a.w_scale_per_col ? a.w_scale[c0] : a.w_scale[0];
+    const float ws1 = a.w_scale_per_col ? a.w_scale[c1] : a.w_scale[0];
+    const f2v pr = {sum[2 * e] * xsc * ws0, sum[2 * e + 1] * xsc * ws1};
+    w2[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
+  }
+  uint16_t* dst = a.out + (size_t)row * a.n + col0;
+  if ((a.n & 3) == 0) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col0 + e < a.n) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+template <int XF, int WF>
+static hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid(frag_rows(a.n)), block(64 * kSkWaves);
+  if (a.m <= 16)
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 4>), grid, block, 0, st, a);
+  else if (a.m <= 32)
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 4>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -418,8 +532,12 @@ static hipError_t launch_grouped_cfg(const GemmArgs& a, const int32_t* offsets, 
 #define HQ_BIG_WM 2
 #endif
 
+// Up to this many rows the weight-streaming kernel runs the GEMM.
+constexpr int kSkinnyMaxM = 64;
+
 template <int XF, int WF>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t st) {
+  if (a.m <= kSkinnyMaxM) return launch_skinny<XF, WF>(a, st);
   if (use_big_tile(a.m, a.n)) return launch_plain<XF, WF, 256, 64, HQ_BIG_WM>(a, st);
   return launch_plain<XF, WF, 128, 32, 1>(a, st);
 }

@@ -6,8 +6,10 @@
 // 2^-126), r = 1/s, q = saturating RNE cast of fl32(x*r).
 //
 // Kernels (all read the input once from HBM with 16-byte vector loads):
-//   quant_rows       one workgroup per row ("per token"): the row is held in
-//                    registers between the amax reduction and the cast
+//   quant_rows_wave  one wavefront per row ("per token", rows up to 512
+//                    vectors): the row is held in registers between the amax
+//                    reduction (wavefront shuffles) and the cast
+//   quant_rows       one workgroup per row for longer rows, same scheme
 //   amax_partials +  per tensor: block partial maxima, then every block folds
 //   quant_tensor     the partials and casts its share (two launches)
 //   colmax_partials  per column ("per channel"): 256-column x 128-row tiles write
@@ -89,8 +91,7 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
       if (i < vpr) {
         uint32_t w[E / 4];
         vec_cast_checked<XT, FMT>(v[j], r, raw[j], w);
-        if (E == 8) *reinterpret_cast<uint2*>(qr + (size_t)i * 8) = make_uint2(w[0], w[E / 4 - 1]);
-        else *reinterpret_cast<uint32_t*>(qr + (size_t)i * 4) = w[0];
+        store_codes<E>(qr + (size_t)i * E, w);
       }
     }
   } else {
@@ -98,8 +99,59 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
       const uint4 vv = xr[i];
       uint32_t w[E / 4];
       vec_cast_checked<XT, FMT>(vv, r, vec_absmax_raw<XT>(vv), w);
-      if (E == 8) *reinterpret_cast<uint2*>(qr + (size_t)i * 8) = make_uint2(w[0], w[E / 4 - 1]);
-      else *reinterpret_cast<uint32_t*>(qr + (size_t)i * 4) = w[0];
+      store_codes<E>(qr + (size_t)i * E, w);
+    }
+  }
+}
+
+// One wavefront per row, for rows of up to 64*NV vectors: the lane loads are
+// all issued before the first use, the amax is a wavefront shuffle reduction
+// (no LDS round trip, no barrier), and kRowsPerBlock rows share a workgroup.
+constexpr int kRowsPerBlock = 4;
+
+template <int XT, int FMT, int NV>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
+    const uint4* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ amax_out, int rows, int vpr) {
+  constexpr int E = VecTraits<XT>::kElems;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wavefronts only
+  const uint4* xr = x + (size_t)row * vpr;
+  uint8_t* qr = q + (size_t)row * vpr * E;
+  uint4 v[NV];
+  uint32_t raw[NV];
+  // lanes past the row end reload the row's last vector (a real element, so it
+  // cannot change the max) and skip the store
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = xr[min(lane + 64 * j, vpr - 1)];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    raw[j] = vec_absmax_raw<XT>(v[j]);
+    mx = max(mx, raw[j]);
+  }
+  mx = wave_max_u32(mx);
+  if (mx >= kInfBits) {  // the row holds an Inf/NaN: recompute over finite elements
+    uint32_t f = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) f = max(f, vec_absmax_finite<XT>(v[j]));
+    mx = wave_max_u32(f);
+  }
+  const float amax = __uint_as_float(mx);
+  const float s = scale_from_amax<FMT>(amax);
+  const float r = 1.0f / s;
+  if (lane == 0) {
+    scale[row] = s;
+    if (amax_out) amax_out[row] = amax;
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = lane + 64 * j;
+    if (i < vpr) {
+      uint32_t w[E / 4];
+      vec_cast_checked<XT, FMT>(v[j], r, raw[j], w);
+      store_codes<E>(qr + (size_t)i * E, w);
     }
   }
 }
@@ -109,12 +161,15 @@ static hipError_t launch_rows_t(const void* x, int rows, int vpr, uint8_t* q, fl
                                 float* amax, hipStream_t st) {
   const uint4* xv = static_cast<const uint4*>(x);
   const dim3 grid(rows);
+  const dim3 wgrid((rows + kRowsPerBlock - 1) / kRowsPerBlock), wblock(64 * kRowsPerBlock);
   if (vpr <= 64) {
-    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 1, 64>), grid, dim3(64), 0, st, xv, q, scale, amax, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 1>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
+  } else if (vpr <= 128) {
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 2>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
   } else if (vpr <= 256) {
-    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 1, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 4>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
   } else if (vpr <= 512) {
-    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 2, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 8>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
   } else if (vpr <= 1024) {
     hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 4, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
   } else if (vpr <= 2048) {
@@ -197,8 +252,7 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
         uint32_t w[E / 4];
         if (nonfinite) vec_cast<XT, FMT>(v[u], r, true, w);
         else vec_cast<XT, FMT>(v[u], r, false, w);
-        if (E == 8) *reinterpret_cast<uint2*>(q + i * 8) = make_uint2(w[0], w[E / 4 - 1]);
-        else *reinterpret_cast<uint32_t*>(q + i * 4) = w[0];
+        store_codes<E>(q + i * E, w);
       }
     }
   }
@@ -309,8 +363,7 @@ __global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restr
       if (patch) w[d] = patch_nan4(w[d], a, b, c, e);
     }
     uint8_t* dst = q + ((size_t)row * vpr + vc) * E;
-    if (E == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[E / 4 - 1]);
-    else *reinterpret_cast<uint32_t*>(dst) = w[0];
+    store_codes<E>(dst, w);
   }
 }
 
@@ -376,8 +429,7 @@ __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __re
         fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
         uint32_t w[E / 4];
         vec_cast_checked<XT, FMT>(v[u], r, m, w);
-        if (E == 8) *reinterpret_cast<uint2*>(q + i * 8) = make_uint2(w[0], w[E / 4 - 1]);
-        else *reinterpret_cast<uint32_t*>(q + i * 4) = w[0];
+        store_codes<E>(q + i * E, w);
       }
     }
   }

@@ -42,8 +42,16 @@ def test_preshuffle_bit_exact(hq, nk):
     assert np.array_equal(got, P.preshuffle(w))
 
 
+# M <= 64 runs the weight-streaming kernel (one block per 16-column fragment,
+# K split over 16 wavefronts, chunks of 4 or 2 K blocks), larger M the tiles.
 SHAPES = [(1, 16, 16), (16, 64, 128), (17, 33, 144), (130, 200, 400), (256, 256, 256), (300, 520, 1040),
-          (129, 130, 2064)]
+          (129, 130, 2064),
+          (4, 64, 16384),      # several K chunks per wavefront
+          (33, 48, 2064),      # 4 activation blocks, ragged K
+          (64, 100, 1040),     # largest skinny M, ragged N
+          (65, 96, 256),       # smallest tiled M
+          (8, 7, 304),         # N not a multiple of 4: element stores
+          (2, 2050, 384)]      # many fragments, ragged last group
 
 
 @pytest.mark.parametrize("shape", SHAPES)
