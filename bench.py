@@ -95,7 +95,7 @@ def make_ops(hq, lib, stream):
 
     def gemm(b):
         st = lib.hq_gemm_a8w8(b.p["xq"], E4M3, b.p["wpre"], E4M3, b.p["xs"], M, b.p["ws"], N, M, N, K, b.p["out"],
-                              stream)
+                              None, 0, stream)
         assert st == 0, hq.hq_last_error()
 
     return {"quant_x": quant_x, "quant_w": quant_w, "preshuffle": preshuffle, "gemm": gemm}
@@ -211,10 +211,12 @@ def other_workloads(torch, hq, lib, reps):
             pres = [pre.clone() for _ in range(copies)]
             del gw
         out = torch.empty((m, dn), dtype=torch.bfloat16, device="cuda")
+        wsb = hq.hq_gemm_workspace_bytes(m, dn, dk)
+        work = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
 
-        def launch(i, h, gx=gx, gxs=gxs, out=out, m=m):
+        def launch(i, h, gx=gx, gxs=gxs, out=out, m=m, work=work, wsb=wsb):
             st = lib.hq_gemm_a8w8(P(gx.data_ptr()), E4M3, P(pres[i % copies].data_ptr()), E4M3, P(gxs.data_ptr()),
-                                  m, P(gws.data_ptr()), dn, m, dn, dk, P(out.data_ptr()), h)
+                                  m, P(gws.data_ptr()), dn, m, dn, dk, P(out.data_ptr()), P(work.data_ptr()), wsb, h)
             assert st == 0, hq.hq_last_error()
         ms = time_graph(torch, launch, 2 * copies)
         alg = dn * dk + m * dk + 2 * m * dn + 4 * (m + dn)

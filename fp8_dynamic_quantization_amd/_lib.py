@@ -68,7 +68,8 @@ SIGNATURES = {
     "hq_scale_ring_update": (_I, [ctypes.POINTER(hq_ring), _P, _I, _P]),
     "hq_preshuffled_bytes": (_I64, [_I64, _I64]),
     "hq_preshuffle_weight": (_I, [_P, _I64, _I64, _P, _P]),
-    "hq_gemm_a8w8": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P]),
+    "hq_gemm_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "hq_gemm_a8w8": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "hq_grouped_gemm_a8w8": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P]),
     "hq_last_error": (ctypes.c_char_p, []),
 }

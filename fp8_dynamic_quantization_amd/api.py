@@ -50,6 +50,10 @@ def hq_preshuffled_bytes(n: int, k: int) -> int:
     return int(load().hq_preshuffled_bytes(n, k))
 
 
+def hq_gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load().hq_gemm_workspace_bytes(m, n, k))
+
+
 class Ring:
     """Device state of a delayed-scaling amax-history ring.
 
@@ -121,18 +125,46 @@ def hq_preshuffle_weight(wq: torch.Tensor, out=None, stream=None) -> torch.Tenso
     return out
 
 
+_GEMM_WORKSPACE = {}
+
+
+def gemm_workspace(device, nbytes: int) -> torch.Tensor | None:
+    """A GEMM workspace of at least `nbytes` for `device`, zero-filled when made
+    and kept for reuse (the kernels leave its counters at zero). Calls sharing
+    it must not overlap, so pass your own `workspace=` to GEMMs that run
+    concurrently on other streams."""
+    if nbytes <= 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _GEMM_WORKSPACE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _GEMM_WORKSPACE[key] = ws
+    return ws
+
+
 def hq_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_scale: torch.Tensor,
-                 w_scale: torch.Tensor, n: int, out=None, stream=None) -> torch.Tensor:
-    """out[m, n] = bf16(x_scale[m] * w_scale[n] * sum_k XQ[m,k] WQ[n,k]); returns out."""
+                 w_scale: torch.Tensor, n: int, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """out[m, n] = bf16(x_scale[m] * w_scale[n] * sum_k XQ[m,k] WQ[n,k]); returns out.
+
+    `workspace`: None (a shared zero-filled buffer of the size the shape wants),
+    False (run without one) or a zero-filled uint8 device tensor."""
     xq = xq.contiguous()
     m, k = xq.shape
     x_scale = x_scale.contiguous()
     w_scale = w_scale.contiguous()
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
-    check(load().hq_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
-                              _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out),
-                              _stream(xq.device, stream)))
+    lib = load()
+    if workspace is None:
+        workspace = gemm_workspace(xq.device, int(lib.hq_gemm_workspace_bytes(m, n, k)))
+    elif workspace is False:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib.hq_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                           _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out), _ptr(workspace), ws_bytes,
+                           _stream(xq.device, stream)))
     return out
 
 

@@ -43,6 +43,7 @@ constexpr int kFragBytes = 2048;  // 16 slots x 128 k
 // Third flags word of a raw (stride 0) buffer resource on gfx9-class parts:
 // 32-bit data format, range-checked against the extent.
 constexpr int kRsrcFlags = 0x00020000;
+constexpr int kBadOffset = int(0x80000000u);  // past any extent: a buffer load there reads zero
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 as_uint4(v4u v) { return make_uint4(v[0], v[1], v[2], v[3]); }
@@ -381,47 +382,99 @@ __global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, cons
 // ---------------------------------------------------------------------------
 // skinny M (decode): weight streaming
 // ---------------------------------------------------------------------------
-// For M <= 64 the GEMM is bound by reading WQ once. A workgroup of kSkWaves
-// wavefronts owns one 16-slot weight fragment row (16 output columns) and the
-// whole K; wavefront w takes the K blocks w, w + kSkWaves, ... so the
-// workgroup reads its fragment row (contiguous along K) front to back. A
-// wavefront issues every load of a chunk of KPW K blocks before its first
-// MFMA, so a CU keeps up to kSkWaves * KPW * (2 + 2*MB) KB in flight; the
-// weight fragment is the MFMA's first operand and MB 16-row activation
-// fragments the second. The per-wavefront partial sums are added in LDS in a
-// fixed order (wavefront 0 first), then scaled and stored as bf16.
+// For M <= 64 the GEMM is bound by reading WQ once, and a CU streams from HBM
+// at a rate set by how many misses it can keep in flight, so the work is
+// spread over every CU. A fragment group is F consecutive 16-slot weight
+// fragments (16*F output columns); its K blocks are dealt to kSkWaves
+// wavefronts (wavefront g takes blocks g, g + kSkWaves, ...), which sit in S
+// workgroups of kSkWaves/S wavefronts. Each wavefront issues every load of a
+// chunk of KPW K blocks (F weight fragments and MB 16-row activation fragments
+// each) before its MFMAs, and reuses each activation fragment for F weight
+// fragments. Partial sums are added in LDS in wavefront order; with S > 1 each
+// workgroup writes its sums to the workspace and the last of the S to finish
+// (device-scope counter, reset by that workgroup) adds the S partials in split
+// order and runs the epilogue, so results do not depend on arrival order.
 constexpr int kSkWaves = 16;
-constexpr int kBadOffset = int(0x80000000u);  // past any extent: the buffer load reads zero
 
-template <int XF, int WF, int MB, int KPW>
-__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[kSkWaves][MB][64][4];
+SkinnyPlan skinny_plan(int m, int n, int k) {
+  SkinnyPlan p{};
+  p.mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+  p.f = p.mb == 1 ? 1 : 2;
+  p.kpw = p.mb == 1 ? 4 : (p.mb == 2 ? 2 : 1);  // loads in flight within the 128-VGPR budget
+  p.groups = (frag_rows(n) + p.f - 1) / p.f;
+  // Split only when one workgroup per group would take its wavefronts through
+  // more than one chunk of loads: below that the cross-workgroup step costs
+  // more latency than the extra workgroups save.
+  p.splits = 1;
+  const int nkb = (k + kBK - 1) / kBK;
+  if (nkb > kSkWaves * p.kpw) {
+    while (p.splits < 8 && p.groups * p.splits < 256) p.splits *= 2;
+    while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;  // at least 2 K blocks per workgroup
+  }
+  p.workspace_bytes = p.splits == 1 ? 0
+                                    : ((size_t)p.groups * 4 + 255) / 256 * 256 +
+                                          (size_t)p.groups * p.splits * p.f * p.mb * 1024;
+  return p;
+}
+
+template <int XF, int WF, int MB, int F, int KPW>
+__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, int splits, int chunk,
+                                                                  uint32_t* counters, float* partials) {
+  __shared__ __attribute__((aligned(16))) float red[kSkWaves][64][4];
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int waves = blockDim.x >> 6;  // kSkWaves / splits
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = blockIdx.x;  // fragment row
+  const int fg = blockIdx.x / splits, split = blockIdx.x % splits;
+  const int g = split * waves + wave;  // wavefront index within the fragment group
   const int K = a.k, nkb = (K + kBK - 1) / kBK;
-  // B: the fragment row's nkb * 2048 bytes; blocks past nkb read zero.
+  const int nfrag = frag_rows(a.n);
+  // B: the group's fragment rows (F * nkb * 2048 contiguous bytes); fragments
+  // past the padded N and blocks past nkb read zero.
+  const int nb0 = fg * F;
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.wq_pre + (size_t)nb * nkb * kFragBytes), (short)0, nkb * kFragBytes, kRsrcFlags);
+      (void*)(a.wq_pre + (size_t)nb0 * nkb * kFragBytes), (short)0, min(F, nfrag - nb0) * nkb * kFragBytes,
+      kRsrcFlags);
   // X: rows past M read zero through the extent; columns past K are sent past
-  // the extent too (they would otherwise read the next row).
+  // it too (they would otherwise read the next row).
   const __amdgpu_buffer_rsrc_t x_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, a.m * K, kRsrcFlags);
   const int xr = lane & 15, xc = 32 * (lane >> 4);
 
-  v4f acc[MB];
+  // Epilogue scales of every slice this lane may store, fetched before the K
+  // loop so their latency hides behind it (indices clamped; masked on store).
+  // Slice (f, i): row 16*i + l%16, columns col0(f) .. +3 (see the epilogue).
+  float xs_r[MB], ws_r[F][4];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MB; ++i) xs_r[i] = a.x_scale[a.x_scale_per_row ? min(i * 16 + xr, a.m - 1) : 0];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    const int nb = nb0 + f;
+    const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ws_r[f][e] = a.w_scale[a.w_scale_per_col ? min(col0 + e, a.n - 1) : 0];
+  }
+
+  v4f acc[F][MB];
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = (nkb + kSkWaves * KPW - 1) / (kSkWaves * KPW);
   for (int c = 0; c < nchunks; ++c) {
-    uint4 fb[KPW][2], fx[KPW][MB][2];
+    uint4 fb[KPW][F][2], fx[KPW][MB][2];
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
-      const int kb = (c * KPW + j) * kSkWaves + wave;
+      const int kb = (c * KPW + j) * kSkWaves + g;
+      // a block past nkb would land in the next fragment's row: send it past the extent
+      const int bvo = kb < nkb ? lane * 16 : kBadOffset;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        fb[j][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, lane * 16 + h * 1024, kb * kFragBytes, 0));
+      for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          fb[j][f][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(
+              b_rsrc, bvo + h * 1024, (f * nkb + min(kb, nkb - 1)) * kFragBytes, 0));
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -434,61 +487,132 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a) 
     // keep every load of the chunk ahead of its first MFMA
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const v8i bw = v8i{(int)fb[j][0].x, (int)fb[j][0].y, (int)fb[j][0].z, (int)fb[j][0].w,
-                         (int)fb[j][1].x, (int)fb[j][1].y, (int)fb[j][1].z, (int)fb[j][1].w};
+    for (int j = 0; j < KPW; ++j)
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const v8i xa = v8i{(int)fx[j][i][0].x, (int)fx[j][i][0].y, (int)fx[j][i][0].z, (int)fx[j][i][0].w,
-                           (int)fx[j][i][1].x, (int)fx[j][i][1].y, (int)fx[j][i][1].z, (int)fx[j][i][1].w};
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw, xa, acc[i], WF, XF, 0, 0, 0, 0);
+      for (int f = 0; f < F; ++f) {
+        const v8i bw = v8i{(int)fb[j][f][0].x, (int)fb[j][f][0].y, (int)fb[j][f][0].z, (int)fb[j][f][0].w,
+                           (int)fb[j][f][1].x, (int)fb[j][f][1].y, (int)fb[j][f][1].z, (int)fb[j][f][1].w};
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const v8i xa = v8i{(int)fx[j][i][0].x, (int)fx[j][i][0].y, (int)fx[j][i][0].z, (int)fx[j][i][0].w,
+                             (int)fx[j][i][1].x, (int)fx[j][i][1].y, (int)fx[j][i][1].z, (int)fx[j][i][1].w};
+          acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw, xa, acc[f][i], WF, XF, 0, 0, 0, 0);
+        }
       }
+  }
+
+  // Epilogue of slice (f, i): lane l holds activation row 16*i + l%16 and weight
+  // slots 4*(l/16) .. +3 of fragment nb0 + f, i.e. 4 consecutive output columns.
+  // Scale, round to bf16, one 8-byte store.
+  auto epilogue = [&](int f, int i, v4f t) {
+    const int nb = nb0 + f;
+    const int row = i * 16 + xr;
+    const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
+    if (row >= a.m || col0 >= a.n) return;
+    const float xsc = xs_r[i];
+    uint32_t w2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f2v pr = {t[2 * e] * xsc * ws_r[f][2 * e], t[2 * e + 1] * xsc * ws_r[f][2 * e + 1]};
+      w2[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
     }
-  }
+    uint16_t* dst = a.out + (size_t)row * a.n + col0;
+    if ((a.n & 3) == 0) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (col0 + e < a.n) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
+    }
+  };
+
+  // Workgroup sum of slice (f, i); wavefront (f*MB + i) % waves owns it. The
+  // association is fixed by `chunk` (the wavefronts per workgroup of the
+  // planned split): each run of `chunk` wavefronts is added left to right, then
+  // the runs left to right, exactly as the split form adds its workgroups'
+  // sums, so a launch gives the same bits split or not.
+  // With splits > 1 the sums go to partials[fg][split][f][i][lane][4].
+  float* mine = partials + ((size_t)fg * splits + split) * (F * MB * 256);
 #pragma unroll
-  for (int i = 0; i < MB; ++i) *reinterpret_cast<v4f*>(&red[wave][i][lane][0]) = acc[i];
+  for (int f = 0; f < F; ++f)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      *reinterpret_cast<v4f*>(&red[wave][lane][0]) = acc[f][i];
+      __syncthreads();
+      if (wave == (f * MB + i) % waves) {
+        v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < waves; c0 += chunk) {
+          v4f u = *reinterpret_cast<const v4f*>(&red[c0][lane][0]);
+          for (int w = 1; w < chunk; ++w) {
+            const v4f v = *reinterpret_cast<const v4f*>(&red[c0 + w][lane][0]);
+            u = v4f{u[0] + v[0], u[1] + v[1], u[2] + v[2], u[3] + v[3]};
+          }
+          t = c0 == 0 ? u : v4f{t[0] + u[0], t[1] + u[1], t[2] + u[2], t[3] + u[3]};
+        }
+        if (splits == 1) {
+          epilogue(f, i, t);
+        } else {
+          float* p = mine + ((f * MB + i) * 64 + lane) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) __hip_atomic_store(p + e, t[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+    }
+  if (splits == 1) return;
+
+  // Cross-workgroup step: publish, count, and let the last workgroup finish.
+  // The partials were written with device-scope atomic stores, which write
+  // through to the coherence point; waiting for their completion before the
+  // barrier, and the barrier before thread 0's counter increment, publishes
+  // them without a release fence (on this part a fence writes back the XCD's
+  // whole L2). The last workgroup reads them with device-scope atomic loads,
+  // which also go to the coherence point, so it needs no acquire fence (that
+  // would invalidate the L2 under the other workgroups of the XCD).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (wave >= MB) return;
-  // Wavefront i adds up activation block i: lane l holds row 16*i + l%16 and
-  // weight slots 4*(l/16) .. +3 = output columns 32*(nb/2) + 8*(l/16) + 4*(nb%2) .. +3.
-  v4f sum = *reinterpret_cast<const v4f*>(&red[0][wave][lane][0]);
-#pragma unroll
-  for (int w = 1; w < kSkWaves; ++w) {
-    const v4f t = *reinterpret_cast<const v4f*>(&red[w][wave][lane][0]);
-    sum = v4f{sum[0] + t[0], sum[1] + t[1], sum[2] + t[2], sum[3] + t[3]};
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(counters + fg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == (uint32_t)(splits - 1);
   }
-  const int row = wave * 16 + xr;
-  const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
-  if (row >= a.m || col0 >= a.n) return;
-  const float xsc = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
-  uint32_t w2[2];
+  __syncthreads();
+  if (!s_last) return;
+  const float* base = partials + (size_t)fg * splits * (F * MB * 256);
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int c0 = min(col0 + 2 * e, a.n - 1), c1 = min(col0 + 2 * e + 1, a.n - 1);
-    const float ws0 = a.w_scale_per_col ? a.w_scale[c0] : a.w_scale[0];
-    const float ws1 = a.w_scale_per_col ? a.w_scale[c1] : a.w_scale[0];
-    const f2v pr = {sum[2 * e] * xsc * ws0, sum[2 * e + 1] * xsc * ws1};
-    w2[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
-  }
-  uint16_t* dst = a.out + (size_t)row * a.n + col0;
-  if ((a.n & 3) == 0) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
-  } else {
+  for (int f = 0; f < F; ++f)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (col0 + e < a.n) dst[e] = (uint16_t)(w2[e >> 1] >> (16 * (e & 1)));
-  }
+    for (int i = 0; i < MB; ++i) {
+      if (wave != (f * MB + i) % waves) continue;
+      v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < splits; ++sp) {
+        const float* p = base + ((size_t)sp * (F * MB) + f * MB + i) * 256 + lane * 4;
+        const v4f u = v4f{__hip_atomic_load(p + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                          __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                          __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                          __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+        t = sp == 0 ? u : v4f{t[0] + u[0], t[1] + u[1], t[2] + u[2], t[3] + u[3]};
+      }
+      epilogue(f, i, t);
+    }
+  if (tid == 0) __hip_atomic_store(counters + fg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// `workspace` may be null: the plan then runs with one workgroup per group.
 template <int XF, int WF>
-static hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(frag_rows(a.n)), block(64 * kSkWaves);
-  if (a.m <= 16)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 4>), grid, block, 0, st, a);
-  else if (a.m <= 32)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 4>), grid, block, 0, st, a);
+static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  SkinnyPlan p = skinny_plan(a.m, a.n, a.k);
+  const int chunk = kSkWaves / p.splits;  // the planned association, kept when run unsplit
+  if (p.splits > 1 && (workspace == nullptr || workspace_bytes < p.workspace_bytes)) p.splits = 1;
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  float* partials = p.splits > 1
+                        ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ((size_t)p.groups * 4 + 255) / 256 * 256)
+                        : nullptr;
+  const dim3 grid(p.groups * p.splits), block(64 * (kSkWaves / p.splits));
+  if (p.mb == 1)
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 4>), grid, block, 0, st, a, p.splits, chunk, counters, partials);
+  else if (p.mb == 2)
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 2, 2>), grid, block, 0, st, a, p.splits, chunk, counters, partials);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2, 1>), grid, block, 0, st, a, p.splits, chunk, counters, partials);
   return hipGetLastError();
 }
 
@@ -536,8 +660,8 @@ static hipError_t launch_grouped_cfg(const GemmArgs& a, const int32_t* offsets, 
 constexpr int kSkinnyMaxM = 64;
 
 template <int XF, int WF>
-static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t st) {
-  if (a.m <= kSkinnyMaxM) return launch_skinny<XF, WF>(a, st);
+static hipError_t launch_gemm_t(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (a.m <= kSkinnyMaxM) return launch_skinny<XF, WF>(a, ws, ws_bytes, st);
   if (use_big_tile(a.m, a.n)) return launch_plain<XF, WF, 256, 64, HQ_BIG_WM>(a, st);
   return launch_plain<XF, WF, 128, 32, 1>(a, st);
 }
@@ -556,8 +680,12 @@ static hipError_t launch_grouped_t(const GemmArgs& a, const int32_t* offsets, in
     else { CALL(kE5M2, kE5M2); }                                  \
   } while (0)
 
-hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, hipStream_t st) {
-#define CALL(X, W) return launch_gemm_t<X, W>(a, st)
+size_t gemm_workspace_bytes(int m, int n, int k) {
+  return m >= 1 && m <= kSkinnyMaxM ? skinny_plan(m, n, k).workspace_bytes : 0;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_t workspace_bytes, hipStream_t st) {
+#define CALL(X, W) return launch_gemm_t<X, W>(a, workspace, workspace_bytes, st)
   HQ_DISPATCH_FMT_PAIR(xf, wf, CALL);
 #undef CALL
 }

@@ -259,11 +259,21 @@ static hq_status check_gemm_common(int xf, int wf, int64_t m, int64_t n, int64_t
   return HQ_OK;
 }
 
+int64_t hq_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 16 || k % 16 != 0 || k >= (int64_t(1) << 24) || m > INT32_MAX || n > INT32_MAX) return -1;
+  if (m == 0 || n == 0) return 0;
+  return (int64_t)hq::gemm_workspace_bytes((int)m, (int)n, (int)k);
+}
+
 hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
                        int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m, int64_t n,
-                       int64_t k, uint16_t* out, hipStream_t stream) {
+                       int64_t k, uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, m, n, k);
   if (st != HQ_OK) return st;
+  if (workspace_bytes > 0 && workspace == nullptr)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "workspace is NULL but workspace_bytes is %zu", workspace_bytes);
+  if (workspace_bytes > 0 && !aligned(workspace, 16))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   if (x_scale_count != 1 && x_scale_count != m)
     return fail(HQ_ERR_INVALID_ARGUMENT, "x_scale_count must be 1 or m (%lld), got %lld", (long long)m, (long long)x_scale_count);
   if (w_scale_count != 1 && w_scale_count != n)
@@ -274,21 +284,24 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
   if (!aligned(xq, 16) || !aligned(wq_pre, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "xq and wq_pre must be 16-byte aligned");
   if (!aligned(out, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+  const size_t ws_used = workspace_bytes > 0 ? workspace_bytes : 0;
   const Range rg[] = {
       {out, (size_t)m * (size_t)n * 2, "out"},
+      {workspace, ws_used, "workspace"},
       {xq, (size_t)m * (size_t)k, "xq"},
       {wq_pre, (size_t)padded_bytes(n, k), "wq_pre"},
       {x_scale, (size_t)x_scale_count * 4, "x_scale"},
       {w_scale, (size_t)w_scale_count * 4, "w_scale"},
   };
   const char* other = nullptr;
-  const char* a = find_overlap(rg, 5, &other);
-  if (a && (strcmp(a, "out") == 0)) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
+  const char* a = find_overlap(rg, 6, &other);
+  if (a && (strcmp(a, "out") == 0 || strcmp(a, "workspace") == 0))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
   st = check_device();
   if (st != HQ_OK) return st;
   hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1};
   (void)hipGetLastError();
-  return launched(hq::launch_gemm(g, xf, wf, stream), "hq_gemm_a8w8");
+  return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), "hq_gemm_a8w8");
 }
 
 hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,

@@ -39,7 +39,21 @@ struct GemmArgs {
   int w_scale_per_col;    // 0: w_scale[0] (per expert) for every column
 };
 
-hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, hipStream_t st);
+// Decode-shape (small M) launch plan: MB 16-row activation blocks, F weight
+// fragments per group, KPW K blocks per wavefront chunk, `groups` fragment
+// groups, each split over `splits` workgroups; workspace_bytes is what the
+// split needs (0 when splits == 1).
+struct SkinnyPlan {
+  int mb, f, kpw, groups, splits;
+  size_t workspace_bytes;
+};
+SkinnyPlan skinny_plan(int m, int n, int k);
+
+// Scratch the GEMM can use for m x n x k (0: none). With less (or none) the
+// launch runs unsplit. Its leading counters must be zero before first use and
+// are left zero by every launch.
+size_t gemm_workspace_bytes(int m, int n, int k);
+hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_t workspace_bytes, hipStream_t st);
 
 // Grouped form: rows [offsets[e], offsets[e+1]) use expert e's weight at
 // wq_pre + e * preshuffled_bytes(n, k) and scales w_scale + e * (per_col ? n : 1).

@@ -146,6 +146,12 @@ int64_t hq_preshuffled_bytes(int64_t n, int64_t k);
 hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
                                uint8_t* wq_pre, hipStream_t stream);
 
+/* Bytes of GEMM workspace worth passing to hq_gemm_a8w8 for an m x n x k
+ * product: nonzero only for the decode shapes (1 <= m <= 64) whose weight
+ * stream is split over several workgroups per column group. Returns -1 for
+ * invalid sizes. */
+int64_t hq_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
 /* Scaled FP8 GEMM into a caller-owned bf16 buffer (the method statement; the
  * operand set of the aiter PR's gemm_a8w8_bpreshuffle_out):
  *   out[m, n] = bf16_rne( fp32( sum_k dec(XQ[m,k]) * dec(WQ[n,k]) ) * x_scale[m] * w_scale[n] )
@@ -156,13 +162,23 @@ hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
  *   w_scale   device, float32 [w_scale_count], w_scale_count = 1 or n
  *   out       device, bf16 bits [m, n] dense row-major, 16-byte aligned; must not
  *             overlap any input. Written in full; nothing else is touched.
+ *   workspace device scratch of workspace_bytes bytes, 16-byte aligned, or NULL
+ *             with workspace_bytes == 0. Zero-fill it once before its first
+ *             use: its leading words are per-column-group arrival counters that
+ *             every call leaves at zero again (the rest holds partial sums and
+ *             needs no reset). With at least
+ *             hq_gemm_workspace_bytes(m, n, k) bytes the decode shapes split
+ *             their weight stream over more workgroups; with less they run
+ *             unsplit, slower but with the same output bits (the order of the
+ *             sums depends only on m, n and k).
+ *             Calls that share a workspace must not run concurrently.
  * Requires k % 16 == 0, 16 <= k < 2^24, m, n < 2^31. m == 0 or n == 0 returns HQ_OK
  * without a launch (aiter PR: an empty out is a no-op). */
 hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                        const float* x_scale, int64_t x_scale_count,
                        const float* w_scale, int64_t w_scale_count,
                        int64_t m, int64_t n, int64_t k, uint16_t* out,
-                       hipStream_t stream);
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Grouped (per-expert) scaled FP8 GEMM over row ranges (megablocks-hip grouped
  * GEMM notes: per-expert products of concatenated tokens, written over, never

@@ -148,8 +148,8 @@ def test_quantize_valid_call_reaches_device_gate(hq):
 
 
 def _gemm(hq, xq=fake(0), xf=0, wq=fake(1), wf=0, xs=fake(2), xsc=64, ws=fake(3), wsc=128, m=64, n=128,
-          k=256, out=fake(4)):
-    return hq.load().hq_gemm_a8w8(xq, xf, wq, wf, xs, xsc, ws, wsc, m, n, k, out, None)
+          k=256, out=fake(4), work=None, work_bytes=0):
+    return hq.load().hq_gemm_a8w8(xq, xf, wq, wf, xs, xsc, ws, wsc, m, n, k, out, work, work_bytes, None)
 
 
 def test_gemm_validation(hq):
@@ -168,6 +168,11 @@ def test_gemm_validation(hq):
     assert "overlaps" in hq.hq_last_error()
     assert _gemm(hq, out=fake(3)) == E        # out overlaps w_scale
     assert _gemm(hq, xs=ctypes.c_void_p(0)) == E
+    assert _gemm(hq, work_bytes=4096) == E                    # NULL workspace with a size
+    assert _gemm(hq, work=fake(5, 8), work_bytes=4096) == E   # misaligned workspace
+    assert _gemm(hq, work=fake(4, 1024), work_bytes=4096) == E  # workspace overlaps out
+    assert "overlaps" in hq.hq_last_error()
+    assert _gemm(hq, work=fake(1), work_bytes=4096) == E      # workspace overlaps wq_pre
     # empty output is a no-op
     assert _gemm(hq, m=0, xsc=1) == hq.HQ_OK
     assert _gemm(hq, n=0, wsc=1) == hq.HQ_OK
@@ -176,6 +181,34 @@ def test_gemm_validation(hq):
 @no_gpu
 def test_gemm_valid_call_reaches_device_gate(hq):
     assert _gemm(hq) == hq.HQ_ERR_UNSUPPORTED_DEVICE
+    assert _gemm(hq, m=8, xsc=8, work=fake(5), work_bytes=1 << 20) == hq.HQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_gemm_workspace_bytes(hq):
+    """Split plan of the weight-streaming kernel: one 4-byte counter per column
+    group (padded to 256 bytes) + 1 KB of fp32 partials per (group, split,
+    fragment, 16-row block)."""
+    # m <= 16 splits only past 64 K blocks (16 wavefronts x 4 blocks per chunk)
+    assert hq.hq_gemm_workspace_bytes(1, 2048, 7168) == 0
+    assert hq.hq_gemm_workspace_bytes(16, 2048, 8192) == 0
+    # m=1, n=2048, k=14336: 128 one-fragment groups, split 2 -> 256 workgroups
+    assert hq.hq_gemm_workspace_bytes(1, 2048, 14336) == 512 + 128 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(16, 2048, 8208) == 512 + 128 * 2 * 1024
+    # m=32 (past 32 K blocks): 64 two-fragment groups of 2 row blocks, split 4
+    assert hq.hq_gemm_workspace_bytes(32, 2048, 7168) == 256 + 64 * 4 * 2 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(32, 2048, 4096) == 0
+    # m=64 (past 16 K blocks): 4 row blocks
+    assert hq.hq_gemm_workspace_bytes(64, 2048, 7168) == 256 + 64 * 4 * 2 * 4 * 1024
+    assert hq.hq_gemm_workspace_bytes(64, 2048, 2048) == 0
+    # enough column groups already (n=7168: 448 fragments) -> no split
+    assert hq.hq_gemm_workspace_bytes(4, 7168, 2048) == 0
+    # too few K blocks to split (k=128: one block)
+    assert hq.hq_gemm_workspace_bytes(1, 2048, 128) == 0
+    # tiled shapes and empty products need none
+    assert hq.hq_gemm_workspace_bytes(65, 2048, 7168) == 0
+    assert hq.hq_gemm_workspace_bytes(0, 2048, 7168) == 0
+    for bad in [(-1, 16, 16), (1, 16, 15), (1, 16, 8), (1, 16, 1 << 24)]:
+        assert hq.hq_gemm_workspace_bytes(*bad) == -1
     assert _gemm(hq, xsc=1, wsc=1) == hq.HQ_ERR_UNSUPPORTED_DEVICE
     # inputs may alias each other (read-only)
     assert _gemm(hq, ws=fake(2), wsc=1, xsc=1) == hq.HQ_ERR_UNSUPPORTED_DEVICE

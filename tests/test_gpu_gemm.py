@@ -164,6 +164,41 @@ def test_decode_skinny_into_view(hq, m):
     print(f"decode m={m}:", st)
 
 
+# shapes whose unsplit launch needs more than one chunk of loads per wavefront
+# (the only ones the plan splits): K blocks > 64 for M <= 16, > 32 for M <= 32,
+# > 16 for M <= 64
+@pytest.mark.parametrize("shape", [(1, 2048, 14336), (16, 2048, 9216), (32, 2048, 7168), (33, 96, 2304),
+                                   (64, 520, 4096), (8, 64, 8336)])
+def test_skinny_split_matches_unsplit_and_oracle(hq, shape):
+    """The decode shapes split their weight stream over several workgroups when
+    given a workspace; the output must be bit-identical to the unsplit launch
+    (same summation order), stay so over repeated calls on the same workspace
+    (the last workgroup of each column group resets its counter), leave the
+    counters zero, and match the oracle within the GEMM bound."""
+    m, n, k = shape
+    need = hq.hq_gemm_workspace_bytes(m, n, k)
+    assert need > 0
+    rng = np.random.default_rng(hash(shape) % 2**32)
+    xq = _finite_codes(rng, (m, k), fp8.E4M3)
+    wq = _finite_codes(rng, (n, k), fp8.E4M3)
+    xs = rng.uniform(1e-4, 1e-2, m).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
+    gx, gw = dev_u8(xq), dev_u8(wq)
+    pre = hq.hq_preshuffle_weight(gw)
+    gxs, gws = dev_f32(xs), dev_f32(ws)
+    plain = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, n, workspace=False))
+    work = torch.zeros(need + 64, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        split = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, n, workspace=work))
+        assert np.array_equal(split, plain)
+    torch.cuda.synchronize()
+    # the per-group counters (the workspace's first words) are back at zero
+    frags = -(-n // 32) * 2
+    groups = frags if m <= 16 else -(-frags // 2)
+    assert int(work[:4 * groups].count_nonzero()) == 0
+    check_gemm(plain, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, max_strict_frac=0.05)
+
+
 def test_empty_output_is_noop(hq):
     xq = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
     wq = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
