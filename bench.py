@@ -76,26 +76,27 @@ class Buffers:
 
 
 def make_ops(hq, lib, stream):
-    """Per-kernel launch closures calling the C ABI with pre-marshalled pointers."""
+    """Per-kernel launch closures calling the C ABI with pre-marshalled pointers
+    (on `stream` unless a stream handle is passed)."""
     E4M3, BF16, TOK = hq.HQ_E4M3, hq.HQ_BF16, hq.HQ_PER_TOKEN
 
-    def quant_x(b):
+    def quant_x(b, h=None):
         st = lib.hq_quantize_fp8(b.p["x"], BF16, M, K, E4M3, TOK, b.p["xq"], b.p["xs"], b.p["xa"], None, None, 0,
-                                 stream)
+                                 h or stream)
         assert st == 0, hq.hq_last_error()
 
-    def quant_w(b):
+    def quant_w(b, h=None):
         st = lib.hq_quantize_fp8(b.p["w"], BF16, N, K, E4M3, TOK, b.p["wq"], b.p["ws"], b.p["wa"], None, None, 0,
-                                 stream)
+                                 h or stream)
         assert st == 0, hq.hq_last_error()
 
-    def preshuffle(b):
-        st = lib.hq_preshuffle_weight(b.p["wq"], N, K, b.p["wpre"], stream)
+    def preshuffle(b, h=None):
+        st = lib.hq_preshuffle_weight(b.p["wq"], N, K, b.p["wpre"], h or stream)
         assert st == 0, hq.hq_last_error()
 
-    def gemm(b):
+    def gemm(b, h=None):
         st = lib.hq_gemm_a8w8(b.p["xq"], E4M3, b.p["wpre"], E4M3, b.p["xs"], M, b.p["ws"], N, M, N, K, b.p["out"],
-                              None, 0, stream)
+                              None, 0, h or stream)
         assert st == 0, hq.hq_last_error()
 
     return {"quant_x": quant_x, "quant_w": quant_w, "preshuffle": preshuffle, "gemm": gemm}
@@ -128,11 +129,11 @@ def traffic_from_profile(name):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(rows: int):
-    """Time the CPU oracle on a bounded sample of the step and scale it to the
-    whole 4096^3 step: quantization of `rows` rows of X and W, pre-shuffle of
-    `rows` rows of WQ, and a rows x rows x 4096 block of the float64 GEMM."""
-    import numpy as np
+def cpu_baseline(min_seconds: float):
+    """Time the CPU oracle on the whole 4096^3 step (per-token quantization of X
+    and W, pre-shuffle of WQ, float64 GEMM), repeated until at least
+    `min_seconds` have passed; reports the mean over the repetitions."""
+    import numpy as np  # noqa: F401
 
     import workloads
     from oracle import fp8, gemm as G, preshuffle as P, quantize as Q
@@ -142,27 +143,23 @@ def cpu_baseline(rows: int):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     x, w = workloads.ptpc_square(1)
-    xs_, ws_ = x[:rows], w[:rows]
-    t0 = time.perf_counter()
-    xq, xsc, _ = Q.quantize_dynamic(xs_, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
-    wq, wsc, _ = Q.quantize_dynamic(ws_, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
-    t1 = time.perf_counter()
-    P.preshuffle(wq)
-    t2 = time.perf_counter()
-    G.gemm_a8w8(xq, fp8.E4M3, wq, fp8.E4M3, xsc, wsc)
-    t3 = time.perf_counter()
-    t_quant = (t1 - t0) * (M + N) / (2 * rows)
-    t_pre = (t2 - t1) * N / rows
-    t_gemm = (t3 - t2) * (M * N) / (rows * rows)
-    total = t_quant + t_pre + t_gemm
+    reps, t_all = 0, 0.0
+    while reps == 0 or t_all < min_seconds:
+        t0 = time.perf_counter()
+        xq, xsc, _ = Q.quantize_dynamic(x, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
+        wq, wsc, _ = Q.quantize_dynamic(w, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
+        P.preshuffle(wq)
+        G.gemm_a8w8(xq, fp8.E4M3, wq, fp8.E4M3, xsc, wsc)
+        t_all += time.perf_counter() - t0
+        reps += 1
+    per = t_all / reps
     return {
-        "value": round(2.0 * M * N * K / total / 1e12, 6),
+        "value": round(2.0 * M * N * K / per / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"oracle on rows 0..{rows - 1} of X and W (quantize), {rows} rows of WQ (pre-shuffle) and a "
-                   f"{rows}x{rows}x{K} float64 GEMM block, {t3 - t0:.2f} s measured, scaled linearly to the "
-                   f"full step ({total:.1f} s estimated)"),
+        "sample": (f"the whole step at full size (oracle per-token quantization of X and W, pre-shuffle of WQ, "
+                   f"float64 {M}x{N}x{K} GEMM), {reps} repetitions, {t_all:.1f} s in total, {per:.2f} s each"),
     }
 
 
@@ -276,7 +273,83 @@ def other_workloads(torch, hq, lib, reps):
         qv[name] = {"us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
                     "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}
     res["quantize_x_other_granularities"] = {"shape": "X bf16 [4096,4096] -> E4M3", **qv}
+    del xs_, q
+
+    res["training_linear"] = training_linear_timings(torch, hq, lib)
     return res
+
+
+def training_linear_timings(torch, hq, lib, copies=12):
+    """One layer of the training-linear workload (X [2048,1024], W [4096,1024],
+    G [2048,4096] bf16): the delayed-scaling quantizations (E4M3 X and W, E5M2
+    G, each with its 16-entry ring folded in the same launch) and the three
+    GEMMs (forward E4M3, dgrad and wgrad E5M2 x E5M2), each timed over `copies`
+    layers' worth of distinct buffers (> 256 MB in all)."""
+    import numpy as np  # noqa: F401
+
+    import workloads
+    P = ctypes.c_void_p
+    E4M3, E5M2, BF16, TEN = hq.HQ_E4M3, hq.HQ_E5M2, hq.HQ_BF16, hq.HQ_PER_TENSOR
+    base, factors = workloads.training_linear(4, layers=1, steps=1)
+    bits = workloads.training_step_inputs(base, factors, 0, 0)
+    dev = [torch.from_numpy(b.view("int16")).cuda().view(torch.bfloat16) for b in bits]
+    names = ("x", "w", "g")
+    fmts = (E4M3, E4M3, E5M2)
+    out = {}
+    for t, name, fmt in zip(dev, names, fmts):
+        rows, cols = t.shape
+        srcs = [t.clone() for _ in range(copies)]
+        qs = [torch.empty((rows, cols), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        rings = [hq.Ring(16) for _ in range(copies)]
+        so = torch.empty(1, dtype=torch.float32, device="cuda")
+        wsb = int(lib.hq_quantize_workspace_bytes(TEN, rows, cols))
+        wsp = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        ring_structs = [r.c_struct(0) for r in rings]
+
+        def launch(i, h, srcs=srcs, qs=qs, rows=rows, cols=cols, fmt=fmt, so=so, wsp=wsp, wsb=wsb):
+            st = lib.hq_quantize_fp8(P(srcs[i % copies].data_ptr()), BF16, rows, cols, fmt, TEN,
+                                     P(qs[i % copies].data_ptr()), P(so.data_ptr()), None,
+                                     ctypes.byref(ring_structs[i % copies]), P(wsp.data_ptr()), wsb, h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, launch, 2 * copies)
+        alg = rows * cols * 3 + 4 * 18
+        out[f"quant_{name}_delayed"] = {"shape": f"[{rows},{cols}] bf16 -> {'E4M3' if fmt == E4M3 else 'E5M2'}",
+                                         "us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                                         "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del srcs, qs, rings
+    # GEMM operands (made once, untimed): E4M3 X, W for the forward; E5M2 G, W^T, G^T, X^T for the backward
+    def quant(t, fmt):
+        return hq.hq_quantize_fp8(t, fmt, TEN)
+
+    xq, xs, _ = quant(dev[0], E4M3)
+    wq, ws, _ = quant(dev[1], E4M3)
+    gq, gs, _ = quant(dev[2], E5M2)
+    wq5, ws5, _ = quant(dev[1], E5M2)
+    xq5, xs5, _ = quant(dev[0], E5M2)
+    cases = {
+        "gemm_fwd": (xq, E4M3, wq, E4M3, xs, ws),
+        "gemm_dgrad": (gq, E5M2, wq5.t().contiguous(), E5M2, gs, ws5),
+        "gemm_wgrad": (gq.t().contiguous(), E5M2, xq5.t().contiguous(), E5M2, gs, xs5),
+    }
+    for name, (a, af, b, bf, sa, sb) in cases.items():
+        m, k = a.shape
+        n = b.shape[0]
+        pre = hq.hq_preshuffle_weight(b)
+        sets = [(a.clone(), pre.clone(), torch.empty((m, n), dtype=torch.bfloat16, device="cuda"))
+                for _ in range(copies)]
+
+        def glaunch(i, h, sets=sets, m=m, n=n, k=k, af=af, bf=bf, sa=sa, sb=sb):
+            a_, p_, o_ = sets[i % copies]
+            st = lib.hq_gemm_a8w8(P(a_.data_ptr()), af, P(p_.data_ptr()), bf, P(sa.data_ptr()), 1,
+                                  P(sb.data_ptr()), 1, m, n, k, P(o_.data_ptr()), None, 0, h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, glaunch, 2 * copies)
+        fl = 2.0 * m * n * k
+        out[name] = {"shape": f"{m}x{n}x{k} {'E4M3' if af == E4M3 else 'E5M2'}", "us": round(ms * 1e3, 3),
+                     "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        del sets
+    return out
 
 
 def _csv_rows(directory, suffix):
@@ -368,7 +441,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=8, help="input/output sets cycled to defeat the MALL")
     ap.add_argument("--kernel-reps", type=int, default=100)
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the decode / grouped / quantize-variant timings")
     ap.add_argument("--copy-probe", action="store_true",
@@ -411,10 +484,8 @@ def main():
 
     def step(i):
         b = sets[i % len(sets)]
-        ops["quant_x"](b)
-        ops["quant_w"](b)
-        ops["preshuffle"](b)
-        ops["gemm"](b)
+        for fn in ops.values():
+            fn(b)
 
     for i in range(args.warmup):
         step(i)
@@ -429,7 +500,14 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     log(f"step: {ms_step * 1e3:.1f} us")
 
-    kms = {name: time_kernel(torch, fn, sets, args.kernel_reps) for name, fn in ops.items()}
+    # Per-kernel durations: each kernel launched back to back over the rotating
+    # sets inside a HIP graph on a side stream, bracketed by HIP events on that
+    # stream (no host launch overhead, no event between launches).
+    kms = {}
+    for name, fn in ops.items():
+        def launch(i, h, fn=fn):
+            fn(sets[i % len(sets)], h)
+        kms[name] = time_graph(torch, launch, 2 * len(sets))
     for name, ms in kms.items():
         log(f"  {name}: {ms * 1e3:.2f} us")
     quant_bytes = M * K * 2 + M * K + M * 4 * 2      # bf16 in, codes out, scale + amax out
@@ -447,7 +525,7 @@ def main():
     other = None if args.no_other else other_workloads(torch, hq, lib, args.kernel_reps)
     if other:
         log(json.dumps(other))
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_rows)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
         "metric": METRIC,

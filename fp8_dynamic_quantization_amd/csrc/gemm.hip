@@ -18,7 +18,9 @@
 // after the two MFMAs of a fragment pair, lane l holds 8 consecutive output
 // columns of one row, stored as one 16-byte write.
 //
-// Tiling: a workgroup of four wavefronts computes a BM x (4*TN) tile. The BM
+// Tiling: a workgroup of 4*WM wavefronts (WM rows x 4 columns) computes a
+// BM x (4*TN) tile: 256 x 256 with eight wavefronts (two per SIMD, 128
+// accumulators each), or 128 x 256, 128 x 128 and 64 x 128 with four. The BM
 // rows of A (XQ, row-major) are staged through double-buffered LDS with an XOR
 // swizzle of their 16-byte chunks (chunk c of row r at slot c ^ (r & 7)), which
 // keeps the row-wise stores and the MFMA-order reads free of bank conflicts.
@@ -620,9 +622,41 @@ static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t works
 // launchers
 // ---------------------------------------------------------------------------
 
-// Tile choice: the 256 x 256 tile when it still yields about one tile per CU,
-// otherwise 128 x 128.
-static bool use_big_tile(long rows, long n) { return ((rows + 255) / 256) * ((n + 255) / 256) >= 200; }
+// Tile choice. Candidates (rows x columns per workgroup) with their measured
+// throughput per tile area relative to the 256 x 256 tile (4096^3 with random
+// FP8 operands, each candidate alone):
+// 128 x 256 0.89, 128 x 128 0.81, 64 x 128 0.67. A launch costs about
+// ceil(tiles / CUs) rounds of one tile each, so the choice minimises
+// ceil(tiles / 256) * area / efficiency. Grouped launches choose between the
+// two smaller tiles only (measured on the MoE shape: 128 x 128 32.5 us,
+// 256 x 256 38.9 us) and count the upper bound of their
+// row tiles, ceil(rows / BM) + experts, since the per-expert counts stay on
+// the device.
+enum TileCfg { kTile256, kTile128x256, kTile128, kTile64x128 };
+
+static TileCfg pick_tile(long rows, long n, int experts) {
+  struct Cand {
+    TileCfg cfg;
+    int bm, bn;
+    double eff;
+  };
+  const Cand cands[] = {{kTile256, 256, 256, 1.0},
+                        {kTile128x256, 128, 256, 0.89},
+                        {kTile128, 128, 128, 0.81},
+                        {kTile64x128, 64, 128, 0.67}};
+  TileCfg best = experts ? kTile128 : kTile256;
+  double best_cost = 0.0;
+  for (const Cand& c : cands) {
+    if (experts && (c.cfg == kTile256 || c.cfg == kTile128x256)) continue;
+    const long tiles = ((rows + c.bm - 1) / c.bm + experts) * ((n + c.bn - 1) / c.bn);
+    const double cost = (double)((tiles + kNumCUs - 1) / kNumCUs) * c.bm * c.bn / c.eff;
+    if (best_cost == 0.0 || cost < best_cost) {
+      best = c.cfg;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 template <int XF, int WF, int BM, int TN, int WM>
 static hipError_t launch_plain(const GemmArgs& a, hipStream_t st) {
@@ -652,24 +686,24 @@ static hipError_t launch_grouped_cfg(const GemmArgs& a, const int32_t* offsets, 
   return hipGetLastError();
 }
 
-#ifndef HQ_BIG_WM
-#define HQ_BIG_WM 2
-#endif
-
 // Up to this many rows the weight-streaming kernel runs the GEMM.
 constexpr int kSkinnyMaxM = 64;
 
 template <int XF, int WF>
 static hipError_t launch_gemm_t(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   if (a.m <= kSkinnyMaxM) return launch_skinny<XF, WF>(a, ws, ws_bytes, st);
-  if (use_big_tile(a.m, a.n)) return launch_plain<XF, WF, 256, 64, HQ_BIG_WM>(a, st);
-  return launch_plain<XF, WF, 128, 32, 1>(a, st);
+  switch (pick_tile(a.m, a.n, 0)) {
+    case kTile256: return launch_plain<XF, WF, 256, 64, 2>(a, st);
+    case kTile128x256: return launch_plain<XF, WF, 128, 64, 1>(a, st);
+    case kTile128: return launch_plain<XF, WF, 128, 32, 1>(a, st);
+    default: return launch_plain<XF, WF, 64, 32, 1>(a, st);
+  }
 }
 
 template <int XF, int WF>
 static hipError_t launch_grouped_t(const GemmArgs& a, const int32_t* offsets, int experts, hipStream_t st) {
-  if (use_big_tile(a.m, a.n)) return launch_grouped_cfg<XF, WF, 256, 64, HQ_BIG_WM>(a, offsets, experts, st);
-  return launch_grouped_cfg<XF, WF, 128, 32, 1>(a, offsets, experts, st);
+  if (pick_tile(a.m, a.n, experts) == kTile128) return launch_grouped_cfg<XF, WF, 128, 32, 1>(a, offsets, experts, st);
+  return launch_grouped_cfg<XF, WF, 64, 32, 1>(a, offsets, experts, st);
 }
 
 #define HQ_DISPATCH_FMT_PAIR(XF, WF, CALL)                        \

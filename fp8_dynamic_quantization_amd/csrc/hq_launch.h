@@ -8,6 +8,7 @@
 
 namespace hq {
 
+constexpr int kNumCUs = 256;              // compute units of an MI355X / MI350X (gfx950)
 constexpr int kMaxTensorPartials = 1024;  // blocks of the per-tensor partial pass
 constexpr int kColChunkRows = 128;        // rows per partial in the per-column pass
 

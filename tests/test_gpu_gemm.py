@@ -1,5 +1,7 @@
 """GPU parity of hq_preshuffle_weight, hq_gemm_a8w8 and hq_grouped_gemm_a8w8 with
 the oracle (pre-shuffle bit-exact; GEMM within the tolerance of gpu_helpers)."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -61,7 +63,7 @@ def test_gemm_narrow_operands_strict(hq, shape, pair, scales):
     """Every output element within the strict bound (MFMA runs exact here)."""
     m, n, k = shape
     xf, wf = pair
-    rng = np.random.default_rng(hash((shape, pair, scales)) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(repr((shape, pair, scales)).encode()))
     xq = narrow_codes(rng, (m, k), xf)
     wq = narrow_codes(rng, (n, k), wf)
     if scales == "vector":
@@ -71,6 +73,36 @@ def test_gemm_narrow_operands_strict(hq, shape, pair, scales):
         xs, ws = np.float32(0.37), np.float32(1.9)
     out = _gemm(hq, xq, xf, wq, wf, xs, ws)
     check_gemm(out, xq, xf, wq, wf, xs, ws, strict_only=True)
+
+
+def _edge_pairs(rng, m, n, count):
+    """Random output positions plus every combination of tile-edge rows and
+    columns (first, 255/256 and 127/128 boundaries, last)."""
+    rows = sorted({0, 127, 128, 255, 256, m // 2, m - 2, m - 1})
+    cols = sorted({0, 7, 8, 127, 128, 255, 256, n // 2, n - 9, n - 8, n - 1})
+    edge = np.array([(r, c) for r in rows for c in cols if 0 <= r < m and 0 <= c < n], dtype=np.int64)
+    rnd = np.stack([rng.integers(0, m, count), rng.integers(0, n, count)], axis=1)
+    return np.concatenate([edge, rnd])
+
+
+# One shape per tile configuration the launcher's cost model picks (ragged M,
+# N and K): 256 x 256 (eight wavefronts), 128 x 256, 128 x 128 and
+# 64 x 128 (the small test shapes above all take 64 x 128 as well).
+@pytest.mark.parametrize("shape", [(3600, 3700, 400), (3841, 3330, 1024),   # 256 x 256
+                                   (2000, 4000, 272),                       # 128 x 256
+                                   (4000, 1000, 272),                       # 128 x 128
+                                   (1000, 1000, 400)])                      # 64 x 128
+@pytest.mark.parametrize("pair", PAIRS)
+def test_gemm_tile_configs_narrow_strict(hq, shape, pair):
+    m, n, k = shape
+    xf, wf = pair
+    rng = np.random.default_rng(zlib.crc32(repr((shape, pair, "tiles")).encode()))
+    xq = narrow_codes(rng, (m, k), xf)
+    wq = narrow_codes(rng, (n, k), wf)
+    xs = rng.uniform(1e-3, 2.0, m).astype(np.float32)
+    ws = rng.uniform(1e-3, 2.0, n).astype(np.float32)
+    out = _gemm(hq, xq, xf, wq, wf, xs, ws)
+    check_gemm(out, xq, xf, wq, wf, xs, ws, pairs=_edge_pairs(rng, m, n, 3000), strict_only=True)
 
 
 @pytest.mark.parametrize("shape", [(16, 64, 128), (130, 200, 400), (64, 96, 1024)])
