@@ -262,7 +262,7 @@ def other_workloads(torch, hq, lib, reps):
         so = torch.empty(cnt, dtype=torch.float32, device="cuda")
         ao = torch.empty(cnt, dtype=torch.float32, device="cuda")
         wsb = int(lib.hq_quantize_workspace_bytes(gran, M, K))
-        wsp = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
 
         def qlaunch(i, h, gran=gran, so=so, ao=ao, wsp=wsp, wsb=wsb):
             st = lib.hq_quantize_fp8(P(xs_[i % 8].data_ptr()), BF16, M, K, E4M3, gran, P(q[i % 8].data_ptr()),
@@ -303,7 +303,7 @@ def training_linear_timings(torch, hq, lib, copies=12):
         rings = [hq.Ring(16) for _ in range(copies)]
         so = torch.empty(1, dtype=torch.float32, device="cuda")
         wsb = int(lib.hq_quantize_workspace_bytes(TEN, rows, cols))
-        wsp = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
         ring_structs = [r.c_struct(0) for r in rings]
 
         def launch(i, h, srcs=srcs, qs=qs, rows=rows, cols=cols, fmt=fmt, so=so, wsp=wsp, wsb=wsb):

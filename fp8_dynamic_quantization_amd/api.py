@@ -93,7 +93,8 @@ def hq_quantize_fp8(x: torch.Tensor, fmt: int = HQ_E4M3, gran: int = HQ_PER_TOKE
         amax_out = torch.empty(count, dtype=torch.float32, device=dev)
     need = int(lib.hq_quantize_workspace_bytes(gran, rows, cols))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        # zero-filled: delayed scaling keeps arrival counters there
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ring_c = ctypes.byref(ring.c_struct(ring_idx)) if ring is not None else None
     st = lib.hq_quantize_fp8(_ptr(x), _XT[x.dtype], rows, cols, fmt, gran, _ptr(q), _ptr(scale_out),

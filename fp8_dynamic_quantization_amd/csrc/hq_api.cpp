@@ -138,7 +138,7 @@ int64_t hq_scale_count(int gran, int64_t rows, int64_t cols) {
 size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0 || rows > kI32Max || cols > kI32Max) return 0;
   switch (gran) {
-    case HQ_PER_TENSOR: return (size_t)hq::kMaxTensorPartials * 4;
+    case HQ_PER_TENSOR: return hq::kTensorWorkspaceBytes;
     case HQ_PER_TOKEN: return 0;
     case HQ_PER_CHANNEL: return (size_t)hq::col_chunks((int)rows) * (size_t)cols * 4;
     default: return 0;
@@ -173,7 +173,7 @@ hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int
   if (!aligned(x, 16) || !aligned(q, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "x and q must be 16-byte aligned");
   if (!aligned(scale_out, 4) || (amax_out && !aligned(amax_out, 4)))
     return fail(HQ_ERR_INVALID_ARGUMENT, "scale_out and amax_out must be 4-byte aligned");
-  const size_t need = ring ? (size_t)hq::kMaxTensorPartials * 4 : hq_quantize_workspace_bytes(gran, rows, cols);
+  const size_t need = ring ? hq::kTensorWorkspaceBytes : hq_quantize_workspace_bytes(gran, rows, cols);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(HQ_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,

@@ -10,6 +10,13 @@ namespace hq {
 
 constexpr int kNumCUs = 256;              // compute units of an MI355X / MI350X (gfx950)
 constexpr int kMaxTensorPartials = 1024;  // blocks of the per-tensor partial pass
+// Delayed scaling counts its blocks in through kArrivalGroups arrival counters
+// (one per 128-byte line, after the partials) whose last arrivals then count
+// into the ring's own counter: one counter for every block serialised the
+// blocks' device-scope increments (17 us instead of 6 us for 8M elements).
+constexpr int kArrivalGroups = 32;
+constexpr int kArrivalStride = 32;        // uint32 words between arrival counters (128 bytes)
+constexpr size_t kTensorWorkspaceBytes = (size_t)kMaxTensorPartials * 4 + (size_t)kArrivalGroups * kArrivalStride * 4;
 constexpr int kColChunkRows = 128;        // rows per partial in the per-column pass
 
 int tensor_partial_blocks(size_t nvec);   // partials written by the per-tensor passes

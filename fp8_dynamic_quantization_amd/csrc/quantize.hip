@@ -421,16 +421,23 @@ __global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restr
 // the next scale (readings: max-reduced window; next = max * 2^margin / fmax,
 // floored at 2^-126; an all-zero window keeps the scale; a non-finite sample
 // leaves the ring unchanged and sets the sticky flag). Resets the counter.
-template <int FMT>
+// Every thread of the block calls it: the window is read in parallel (one
+// history entry per thread, the new sample standing in for entry idx) and
+// reduced with the block max; thread 0 writes the ring.
+template <int FMT, int BLOCK>
 __device__ void ring_fold(float* state, int len, int idx, int margin, int32_t* flag, float amax,
-                          bool nonfinite) {
-  const bool finite = amax <= 3.40282347e38f;  // false for NaN and Inf
-  if (nonfinite || !finite) {
+                          bool nonfinite, uint32_t* red) {
+  const bool ok = !nonfinite && amax <= 3.40282347e38f;  // false for NaN and Inf
+  float w = 0.0f;
+  if (ok)
+    for (int i = threadIdx.x; i < len; i += BLOCK) w = fmaxf(w, i == idx ? amax : state[i]);
+  // window entries are finite and >= 0, so their bit patterns order like the values
+  w = __uint_as_float(block_max_u32<BLOCK>(__float_as_uint(w), red));
+  if (threadIdx.x != 0) return;
+  if (!ok) {
     if (flag) *flag = 1;
   } else {
     state[idx] = amax;
-    float w = 0.0f;
-    for (int i = 0; i < len; ++i) w = fmaxf(w, state[i]);
     if (w > 0.0f) {
       const float cand = ldexpf(w, margin) / Fp8Fmt<FMT>::kMax;
       if (cand <= 3.40282347e38f) state[len] = fmaxf(cand, kScaleFloor);
@@ -443,11 +450,9 @@ __device__ void ring_fold(float* state, int len, int idx, int margin, int32_t* f
 }
 
 template <int FMT>
-__global__ void ring_update_kernel(float* state, int len, int idx, int margin, int32_t* flag,
-                                   const float* __restrict__ amax) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  const float a = *amax;
-  ring_fold<FMT>(state, len, idx, margin, flag, a, false);
+__global__ __launch_bounds__(64) void ring_update_kernel(float* state, int len, int idx, int margin, int32_t* flag,
+                                                         const float* __restrict__ amax) {
+  ring_fold<FMT, 64>(state, len, idx, margin, flag, *amax, false, nullptr);
 }
 
 template <int XT, int FMT>
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __re
                                                                uint8_t* __restrict__ q, float* __restrict__ scale_out,
                                                                float* __restrict__ amax_out, float* state, int len,
                                                                int idx, int margin, int32_t* flag,
-                                                               uint32_t* partial) {
+                                                               uint32_t* partial, uint32_t* arrivals) {
   constexpr int E = VecTraits<XT>::kElems;
   __shared__ uint32_t red[kBlock / 64];
   __shared__ bool is_last;
@@ -491,13 +496,24 @@ __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __re
   // back the XCD's whole L2, which cost more than the quantization itself.
   // The last block reads the partials with device-scope atomic loads, which
   // also go to the coherence point, so it needs no acquire fence either.
+  // Counting is a two-level tree: block b counts into arrival counter b % G;
+  // the last arrival of each group resets that counter and counts into the
+  // ring's counter, and the G-th arrival there is the last block overall.
   uint32_t* counter = reinterpret_cast<uint32_t*>(state) + len + 1;
   if (threadIdx.x == 0) {
     __hip_atomic_store(partial + blockIdx.x, bfin | (braw >= kInfBits ? kNonfiniteBit : 0u), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == gridDim.x - 1;
+    const uint32_t groups = min(gridDim.x, (uint32_t)kArrivalGroups);
+    const uint32_t g = blockIdx.x % groups;
+    const uint32_t members = (gridDim.x - g + groups - 1) / groups;
+    uint32_t* sub = arrivals + g * kArrivalStride;
+    bool last = false;
+    if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+      __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    }
+    is_last = last;
   }
   __syncthreads();
   if (!is_last) return;
@@ -509,12 +525,12 @@ __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __re
   }
   m = block_max_u32<kBlock>(m, red);
   f = block_max_u32<kBlock>(f, red);
+  const float amax = __uint_as_float(m);
   if (threadIdx.x == 0) {
-    const float amax = __uint_as_float(m);
     scale_out[0] = s_t;
     if (amax_out) amax_out[0] = amax;
-    ring_fold<FMT>(state, len, idx, margin, flag, amax, f != 0);
   }
+  ring_fold<FMT, kBlock>(state, len, idx, margin, flag, amax, f != 0, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,7 +605,7 @@ hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, ui
   const uint4* xv = static_cast<const uint4*>(x);
 #define CALL(A, B)                                                                                  \
   hipLaunchKernelGGL((quant_delayed_kernel<A, B>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, q, scale, \
-                     amax, state, len, idx, margin, flag, partial);                                  \
+                     amax, state, len, idx, margin, flag, partial, partial + kMaxTensorPartials);    \
   return hipGetLastError()
   HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
 #undef CALL

@@ -146,6 +146,30 @@ def test_repeated_calls_with_shared_workspace(hq):
 
 # ---- delayed scaling ---------------------------------------------------------------
 
+def test_delayed_shared_workspace_varying_grids(hq):
+    """Delayed calls whose grids have 1, a few, hundreds and the maximum number
+    of blocks share one zero-filled workspace: each call's codes and ring match
+    the oracle, and the arrival counters are back at zero after every call."""
+    rng = np.random.default_rng(11)
+    shapes = [(1, 16), (8, 2048), (300, 1024), (2048, 4096), (64, 64)]
+    ws = torch.zeros(hq.hq_quantize_workspace_bytes(Q.PER_TENSOR, 1, 16), dtype=torch.uint8, device="cuda")
+    rings = {sh: (hq.Ring(4), Q.ring_new(4)) for sh in shapes}
+    flags = {sh: 0 for sh in shapes}
+    for t in range(3):
+        for sh in shapes:
+            ring, st = rings[sh]
+            bits = workloads.random_bf16(rng, sh, std=float(10.0 ** rng.integers(-2, 2)))
+            q, s, a = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, Q.PER_TENSOR, ring=ring, ring_idx=t % 4,
+                                         workspace=ws)
+            q_ref, s_ref, a_ref, st, flags[sh] = Q.quantize_delayed(bits, Q.BF16, fp8.E4M3, st, t % 4, 0, flags[sh])
+            rings[sh] = (ring, st)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(q), q_ref), (t, sh)
+            assert np.array_equal(host(ring.state).view(np.uint32), st.view(np.uint32)), (t, sh)
+            counters = host(ws)[4096:].view(np.uint32)
+            assert not counters.any(), (t, sh, np.nonzero(counters))
+
+
 def _ring_host(r):
     return host(r.state).copy(), int(host(r.flag)[0])
 
