@@ -9,14 +9,15 @@ from ._lib import (HQ_BF16, HQ_E4M3, HQ_E5M2, HQ_ERR_INVALID_ARGUMENT, HQ_ERR_LA
                    HQUnsupportedDevice, LIB_PATH, SIGNATURES, hq_ring, load)
 from .api import (Ring, gemm_workspace, hq_gemm_a8w8, hq_gemm_workspace_bytes, hq_grouped_gemm_a8w8,
                   hq_last_error, hq_preshuffle_weight, hq_preshuffled_bytes, hq_quantize_fp8,
-                  hq_quantize_workspace_bytes, hq_scale_count, hq_scale_ring_update)
+                  hq_quantize_fp8_layouts, hq_quantize_workspace_bytes, hq_scale_count,
+                  hq_scale_ring_update)
 
 __all__ = [
     "HQ_OK", "HQ_ERR_INVALID_ARGUMENT", "HQ_ERR_UNSUPPORTED_DEVICE", "HQ_ERR_LAUNCH",
     "HQ_E4M3", "HQ_E5M2", "HQ_F32", "HQ_BF16", "HQ_PER_TENSOR", "HQ_PER_TOKEN",
     "HQ_PER_CHANNEL", "HQError", "HQInvalidArgument", "HQUnsupportedDevice", "HQLaunchError",
     "LIB_PATH", "SIGNATURES", "hq_ring", "load", "Ring", "hq_scale_count",
-    "hq_quantize_workspace_bytes", "hq_preshuffled_bytes", "hq_quantize_fp8",
+    "hq_quantize_workspace_bytes", "hq_preshuffled_bytes", "hq_quantize_fp8", "hq_quantize_fp8_layouts",
     "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_workspace_bytes", "hq_gemm_a8w8",
     "hq_grouped_gemm_a8w8", "hq_last_error", "gemm_workspace",
 ]

@@ -17,7 +17,7 @@ from ._lib import (HQ_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANNEL, HQ_PER_TEN
 
 __all__ = [
     "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
-    "hq_quantize_fp8", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
+    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_grouped_gemm_a8w8", "hq_last_error",
 ]
 
@@ -101,6 +101,49 @@ def hq_quantize_fp8(x: torch.Tensor, fmt: int = HQ_E4M3, gran: int = HQ_PER_TOKE
                              _ptr(amax_out), ring_c, _ptr(workspace), ws_bytes, _stream(dev, stream))
     check(st)
     return q, scale_out, amax_out
+
+
+def hq_quantize_fp8_layouts(x: torch.Tensor, fmt: int = HQ_E4M3, *, scale_in: torch.Tensor | None = None,
+                            ring: Ring | None = None, ring_idx: int = 0, q=False, q_t=False, q_pre=False,
+                            q_t_pre=False, scale_out=None, amax_out=None, workspace=None, stream=None):
+    """Per-tensor quantization of a 2-D bf16/fp32 tensor into the requested
+    layouts in one pass. Each of q, q_t, q_pre, q_t_pre is False (skip), True
+    (allocate) or a uint8 tensor to write. Returns a dict with the written
+    layouts plus "scale" and "amax" (None with scale_in)."""
+    if x.dtype not in _XT:
+        raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    x = x.contiguous()
+    rows, cols = x.shape
+    lib = load()
+    dev = x.device
+    sizes = {"q": rows * cols, "q_t": rows * cols, "q_pre": max(int(lib.hq_preshuffled_bytes(rows, cols)), 0),
+             "q_t_pre": max(int(lib.hq_preshuffled_bytes(cols, rows)), 0)}
+    shapes = {"q": (rows, cols), "q_t": (cols, rows), "q_pre": (sizes["q_pre"],), "q_t_pre": (sizes["q_t_pre"],)}
+    outs = {}
+    for name, want in (("q", q), ("q_t", q_t), ("q_pre", q_pre), ("q_t_pre", q_t_pre)):
+        if want is True:
+            outs[name] = torch.empty(shapes[name], dtype=torch.uint8, device=dev)
+        elif want is not False and want is not None:
+            outs[name] = want
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax_out is None and scale_in is None:
+        amax_out = torch.empty(1, dtype=torch.float32, device=dev)
+    need = 0 if scale_in is not None else int(lib.hq_quantize_workspace_bytes(HQ_PER_TENSOR, rows, cols))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ring_c = ctypes.byref(ring.c_struct(ring_idx)) if ring is not None else None
+    st = lib.hq_quantize_fp8_layouts(_ptr(x), _XT[x.dtype], rows, cols, fmt, _ptr(scale_in), ring_c,
+                                     _ptr(outs.get("q")), _ptr(outs.get("q_t")), _ptr(outs.get("q_pre")),
+                                     _ptr(outs.get("q_t_pre")), _ptr(scale_out), _ptr(amax_out), _ptr(workspace),
+                                     ws_bytes, _stream(dev, stream))
+    check(st)
+    outs["scale"] = scale_out
+    outs["amax"] = amax_out
+    return outs
 
 
 def hq_scale_ring_update(ring: Ring, amax: torch.Tensor, fmt: int = HQ_E4M3, ring_idx: int = 0,

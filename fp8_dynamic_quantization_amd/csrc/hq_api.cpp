@@ -210,6 +210,74 @@ hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int
   return launched(e, "hq_quantize_fp8");
 }
 
+hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t cols, int fmt, const float* scale_in,
+                                  const hq_ring* ring, uint8_t* q, uint8_t* q_t, uint8_t* q_pre, uint8_t* q_t_pre,
+                                  float* scale_out, float* amax_out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
+  if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
+  if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
+  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
+  if (scale_in && ring) return fail(HQ_ERR_INVALID_ARGUMENT, "give scale_in or ring, not both");
+  if (ring) {
+    hq_status st = check_ring(ring);
+    if (st != HQ_OK) return st;
+  }
+  if (!q && !q_t && !q_pre && !q_t_pre) return fail(HQ_ERR_INVALID_ARGUMENT, "no output layout requested");
+  if ((q_t || q_t_pre) && rows % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "transposed outputs need rows %% 16 == 0, got %lld", (long long)rows);
+  if (scale_in && amax_out) return fail(HQ_ERR_INVALID_ARGUMENT, "amax_out is not reported with a given scale_in");
+  if (rows == 0) return ok();
+  if (!x || !scale_out) return fail(HQ_ERR_INVALID_ARGUMENT, "x and scale_out must be non-NULL");
+  if (!aligned(x, 16) || (q && !aligned(q, 16)) || (q_t && !aligned(q_t, 16)) || (q_pre && !aligned(q_pre, 16)) ||
+      (q_t_pre && !aligned(q_t_pre, 16)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "x and the code buffers must be 16-byte aligned");
+  if (!aligned(scale_out, 4) || (amax_out && !aligned(amax_out, 4)) || (scale_in && !aligned(scale_in, 4)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scale_in, scale_out and amax_out must be 4-byte aligned");
+  const size_t need = scale_in ? 0 : hq::kTensorWorkspaceBytes;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HQ_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                  workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "workspace must be 4-byte aligned");
+  }
+  const size_t numel = (size_t)rows * (size_t)cols;
+  const Range rg[] = {
+      {x, numel * (xt == HQ_BF16 ? 2 : 4), "x"},
+      {q, q ? numel : 0, "q"},
+      {q_t, q_t ? numel : 0, "q_t"},
+      {q_pre, q_pre ? (size_t)padded_bytes(rows, cols) : 0, "q_pre"},
+      {q_t_pre, q_t_pre ? (size_t)padded_bytes(cols, rows) : 0, "q_t_pre"},
+      {scale_in, scale_in ? 4u : 0u, "scale_in"},
+      {scale_out, 4, "scale_out"},
+      {amax_out, amax_out ? 4u : 0u, "amax_out"},
+      {workspace, need, "workspace"},
+      {ring ? ring->state : nullptr, ring ? ((size_t)ring->len + 2) * 4 : 0, "ring->state"},
+      {ring ? ring->nonfinite_flag : nullptr, ring && ring->nonfinite_flag ? 4u : 0u, "ring->nonfinite_flag"},
+  };
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 11, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  hq::LayoutOut o;
+  o.q = q;
+  o.qt = q_t;
+  o.qp = q_pre;
+  o.qtp = q_t_pre;
+  o.np_q = (int)((rows + 31) / 32 * 32);
+  o.kb_q = (int)((cols + 127) / 128);
+  o.np_t = (int)((cols + 31) / 32 * 32);
+  o.kb_t = (int)((rows + 127) / 128);
+  return launched(hq::launch_quant_layouts(x, xt, (int)rows, (int)cols, fmt, o, scale_in, scale_out, amax_out,
+                                           ring ? ring->state : nullptr, ring ? ring->len : 0, ring ? ring->idx : 0,
+                                           ring ? ring->margin : 0, ring ? ring->nonfinite_flag : nullptr, workspace,
+                                           stream),
+                  "hq_quantize_fp8_layouts");
+}
+
 hq_status hq_scale_ring_update(const hq_ring* ring, const float* amax, int fmt, hipStream_t stream) {
   if (!ring) return fail(HQ_ERR_INVALID_ARGUMENT, "ring is NULL");
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);

@@ -31,6 +31,23 @@ hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt,
 hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
                                 float* amax, float* state, int len, int idx, int margin, int32_t* flag, void* ws,
                                 hipStream_t st);
+// Per-tensor codes of a row-major [rows, cols] tensor in up to four layouts
+// (null pointers are skipped): row-major, transposed [cols, rows], and the
+// pre-shuffled weight layout of either (N = rows, K = cols, or N = cols,
+// K = rows; np_* = N padded to 32, kb_* = K blocks of 128).
+struct LayoutOut {
+  uint8_t* q;
+  uint8_t* qt;
+  uint8_t* qp;
+  uint8_t* qtp;
+  int np_q, kb_q;
+  int np_t, kb_t;
+};
+// Scale: scale_in (given), else the ring in state (delayed), else dynamic
+// (a partial-amax pass first, partials in ws).
+hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int fmt, const LayoutOut& o,
+                                const float* scale_in, float* scale_out, float* amax, float* state, int len, int idx,
+                                int margin, int32_t* flag, void* ws, hipStream_t st);
 hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_t* flag, const float* amax,
                               int fmt, hipStream_t st);
 

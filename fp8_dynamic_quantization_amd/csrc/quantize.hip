@@ -455,50 +455,27 @@ __global__ __launch_bounds__(64) void ring_update_kernel(float* state, int len, 
   ring_fold<FMT, 64>(state, len, idx, margin, flag, *amax, false, nullptr);
 }
 
-template <int XT, int FMT>
-__global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __restrict__ x, size_t nvec,
-                                                               uint8_t* __restrict__ q, float* __restrict__ scale_out,
-                                                               float* __restrict__ amax_out, float* state, int len,
-                                                               int idx, int margin, int32_t* flag,
-                                                               uint32_t* partial, uint32_t* arrivals) {
-  constexpr int E = VecTraits<XT>::kElems;
-  __shared__ uint32_t red[kBlock / 64];
+// The tail every delayed-scaling kernel shares: publish this block's partial
+// amax, count the block in, and let the last block fold the tensor amax into
+// the ring (and report s_t and the amax). Every thread of the block calls it.
+//
+// The partial goes out as a device-scope atomic store, which writes through
+// to the coherence point, and the count is issued only after that store has
+// completed (s_waitcnt), so a block that sees the final count finds every
+// partial there. No release fence: on this part an agent-scope fence writes
+// back the XCD's whole L2, which cost more than the quantization itself. The
+// last block reads the partials with device-scope atomic loads, which also go
+// to the coherence point, so it needs no acquire fence either. Counting is a
+// two-level tree: block b counts into arrival counter b % G; the last arrival
+// of each group resets that counter and counts into the ring's counter, and
+// the G-th arrival there is the last block overall.
+template <int FMT>
+__device__ void delayed_finish(uint32_t raw, uint32_t fin, float s_t, float* __restrict__ scale_out,
+                               float* __restrict__ amax_out, float* state, int len, int idx, int margin,
+                               int32_t* flag, uint32_t* partial, uint32_t* arrivals, uint32_t* red) {
   __shared__ bool is_last;
-  const float s_t = state[len];
-  const float r = 1.0f / s_t;
-  uint32_t raw = 0, fin = 0;
-  const size_t stride = (size_t)gridDim.x * kBlock * kUnroll;
-  for (size_t base = blockIdx.x * (size_t)kBlock * kUnroll + threadIdx.x; base < nvec; base += stride) {
-    uint4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (base + u * kBlock < nvec) v[u] = x[base + u * kBlock];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const size_t i = base + u * kBlock;
-      if (i < nvec) {
-        const uint32_t m = vec_absmax_raw<XT>(v[u]);
-        raw = max(raw, m);
-        fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
-        uint32_t w[E / 4];
-        vec_cast_checked<XT, FMT>(v[u], r, m, w);
-        store_codes<E>(q + i * E, w);
-      }
-    }
-  }
   const uint32_t braw = block_max_u32<kBlock>(raw, red);
   const uint32_t bfin = block_max_u32<kBlock>(fin, red);
-  // Publish the block's partial and count the block in. The partial goes out
-  // as a device-scope atomic store, which writes through to the coherence
-  // point, and the counter increment is issued only after that store has
-  // completed (s_waitcnt), so a block that sees the final count finds every
-  // partial there. No release fence: on this part an agent-scope fence writes
-  // back the XCD's whole L2, which cost more than the quantization itself.
-  // The last block reads the partials with device-scope atomic loads, which
-  // also go to the coherence point, so it needs no acquire fence either.
-  // Counting is a two-level tree: block b counts into arrival counter b % G;
-  // the last arrival of each group resets that counter and counts into the
-  // ring's counter, and the G-th arrival there is the last block overall.
   uint32_t* counter = reinterpret_cast<uint32_t*>(state) + len + 1;
   if (threadIdx.x == 0) {
     __hip_atomic_store(partial + blockIdx.x, bfin | (braw >= kInfBits ? kNonfiniteBit : 0u), __ATOMIC_RELAXED,
@@ -531,6 +508,150 @@ __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __re
     if (amax_out) amax_out[0] = amax;
   }
   ring_fold<FMT, kBlock>(state, len, idx, margin, flag, amax, f != 0, red);
+}
+
+template <int XT, int FMT>
+__global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __restrict__ x, size_t nvec,
+                                                               uint8_t* __restrict__ q, float* __restrict__ scale_out,
+                                                               float* __restrict__ amax_out, float* state, int len,
+                                                               int idx, int margin, int32_t* flag,
+                                                               uint32_t* partial, uint32_t* arrivals) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t red[kBlock / 64];
+  const float s_t = state[len];
+  const float r = 1.0f / s_t;
+  uint32_t raw = 0, fin = 0;
+  const size_t stride = (size_t)gridDim.x * kBlock * kUnroll;
+  for (size_t base = blockIdx.x * (size_t)kBlock * kUnroll + threadIdx.x; base < nvec; base += stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (base + u * kBlock < nvec) v[u] = x[base + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t i = base + u * kBlock;
+      if (i < nvec) {
+        const uint32_t m = vec_absmax_raw<XT>(v[u]);
+        raw = max(raw, m);
+        fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
+        uint32_t w[E / 4];
+        vec_cast_checked<XT, FMT>(v[u], r, m, w);
+        store_codes<E>(q + i * E, w);
+      }
+    }
+  }
+  delayed_finish<FMT>(raw, fin, s_t, scale_out, amax_out, state, len, idx, margin, flag, partial, arrivals, red);
+}
+
+// ---------------------------------------------------------------------------
+// per tensor, into several layouts in one pass
+// ---------------------------------------------------------------------------
+// The codes of a per-tensor quantization do not depend on where they are
+// stored, so one pass over X can write them row-major, transposed ([cols,
+// rows] row-major) and in the GEMM's pre-shuffled weight layout of either (the
+// fused quantize-plus-transpose of the hip-quant README, "Runtime codebooks and
+// GPU execution features"; for the backward GEMMs it replaces the transposed
+// copies and the separate pre-shuffle passes). A workgroup takes 128 x 128
+// tiles; thread t owns the 8 x 8 block of rows 8*(t/16) .. +7 and columns
+// 8*(t%16) .. +7, loads it once, casts it, and writes 8-byte pieces: rows of
+// the block to the row-major outputs, and (after an in-register byte
+// transpose) columns of the block to the transposed ones. Elements past the
+// tensor read as zero, so the zero padding of the pre-shuffled layouts is
+// written as zero codes.
+
+// Byte offset of weight element (n, k) in the pre-shuffled layout with
+// `kblocks` 128-deep K blocks: row n = 32G + 8g + 4p + r is slot 4g + r of
+// fragment 2G + p; fragment (nb, kb) holds 2048 bytes at (nb * kblocks + kb) *
+// 2048; column k_in of a slot sits at h*1024 + (q*16 + slot)*16 + b with
+// q = k_in/32, h = (k_in%32)/16, b = k_in%16.
+__device__ __forceinline__ size_t preshuffled_offset(int n, int k, int kblocks) {
+  const int nb = 2 * (n >> 5) + ((n >> 2) & 1), slot = 4 * ((n >> 3) & 3) + (n & 3);
+  const int kin = k & 127;
+  return ((size_t)nb * kblocks + (k >> 7)) * 2048 + ((kin >> 4) & 1) * 1024 + ((kin >> 5) * 16 + slot) * 16 +
+         (kin & 15);
+}
+
+enum { kScaleGiven = 0, kScaleRing = 1, kScaleDynamic = 2 };
+
+template <int XT, int FMT, int MODE>
+__global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
+    const uint4* __restrict__ x, int rows, int cols, LayoutOut o, const float* __restrict__ scale_in,
+    const uint32_t* __restrict__ dyn_partial, int ndyn, float* __restrict__ scale_out,
+    float* __restrict__ amax_out, float* state, int len, int idx, int margin, int32_t* flag, uint32_t* partial,
+    uint32_t* arrivals) {
+  constexpr int E = VecTraits<XT>::kElems;
+  constexpr int VPC = 8 / E;  // 16-byte vectors per 8 columns
+  __shared__ uint32_t red[kBlock / 64];
+  float s;
+  if (MODE == kScaleGiven) {
+    s = scale_in[0];
+  } else if (MODE == kScaleRing) {
+    s = state[len];
+  } else {
+    bool nonfinite;
+    const float amax = __uint_as_float(fold_partials(dyn_partial, ndyn, red, &nonfinite));
+    s = scale_from_amax<FMT>(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && amax_out) amax_out[0] = amax;
+  }
+  const float r = 1.0f / s;
+  if (MODE != kScaleRing && blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = s;
+  const int rg = threadIdx.x >> 4, cv = threadIdx.x & 15;
+  const int vpr = cols / E;
+  const int tiles_c = (cols + 127) / 128;
+  const int tiles = ((rows + 127) / 128) * tiles_c;
+  uint32_t raw = 0, fin = 0;
+  for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int r0 = (tile / tiles_c) * 128 + 8 * rg, c0 = (tile % tiles_c) * 128 + 8 * cv;
+    const bool col_ok = c0 < cols;  // cols % 16 == 0: an 8-column piece is all in or all out
+    uint4 v[8][VPC];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int u = 0; u < VPC; ++u)
+        v[j][u] = (col_ok && r0 + j < rows) ? x[(size_t)(r0 + j) * vpr + c0 / E + u] : make_uint4(0u, 0u, 0u, 0u);
+    uint2 c[8];  // codes: row j of the block, columns 0..3 in .x, 4..7 in .y
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t w[2];
+#pragma unroll
+      for (int u = 0; u < VPC; ++u) {
+        const uint32_t m = vec_absmax_raw<XT>(v[j][u]);
+        raw = max(raw, m);
+        fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[j][u]));
+        vec_cast_checked<XT, FMT>(v[j][u], r, m, w + u * (E / 4));
+      }
+      c[j] = make_uint2(w[0], w[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = r0 + j;
+      if (o.q && col_ok && row < rows) *reinterpret_cast<uint2*>(o.q + (size_t)row * cols + c0) = c[j];
+      if (o.qp && row < o.np_q) *reinterpret_cast<uint2*>(o.qp + preshuffled_offset(row, c0, o.kb_q)) = c[j];
+    }
+    if (o.qt || o.qtp) {
+      // t[i]: column i of the block, rows 0..3 in .x, 4..7 in .y
+      uint2 t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo |= (((i < 4 ? c[j].x : c[j].y) >> (8 * (i & 3))) & 0xffu) << (8 * j);
+          hi |= (((i < 4 ? c[j + 4].x : c[j + 4].y) >> (8 * (i & 3))) & 0xffu) << (8 * j);
+        }
+        t[i] = make_uint2(lo, hi);
+      }
+      // rows % 16 == 0 when a transposed output is asked for: an 8-row piece is all in or all out
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int col = c0 + i;
+        if (o.qt && col < cols && r0 < rows) *reinterpret_cast<uint2*>(o.qt + (size_t)col * rows + r0) = t[i];
+        if (o.qtp && col < o.np_t) *reinterpret_cast<uint2*>(o.qtp + preshuffled_offset(col, r0, o.kb_t)) = t[i];
+      }
+    }
+  }
+  if (MODE == kScaleRing)
+    delayed_finish<FMT>(raw, fin, s, scale_out, amax_out, state, len, idx, margin, flag, partial, arrivals, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -607,6 +728,42 @@ hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, ui
   hipLaunchKernelGGL((quant_delayed_kernel<A, B>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, q, scale, \
                      amax, state, len, idx, margin, flag, partial, partial + kMaxTensorPartials);    \
   return hipGetLastError()
+  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+#undef CALL
+}
+
+hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int fmt, const LayoutOut& o,
+                                const float* scale_in, float* scale_out, float* amax, float* state, int len, int idx,
+                                int margin, int32_t* flag, void* ws, hipStream_t st) {
+  const int tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
+  const dim3 grid(min(tiles, kMaxTensorPartials)), block(kBlock);
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint32_t* partial = static_cast<uint32_t*>(ws);
+  uint32_t* arrivals = partial ? partial + kMaxTensorPartials : nullptr;
+  const int mode = scale_in ? kScaleGiven : (state ? kScaleRing : kScaleDynamic);
+  int ndyn = 0;
+  if (mode == kScaleDynamic) {
+    const size_t nvec = (size_t)rows * cols / (xt == kBF16 ? 8 : 4);
+    ndyn = tensor_partial_blocks(nvec);
+    if (xt == kBF16)
+      hipLaunchKernelGGL((amax_partials_kernel<kBF16>), dim3(ndyn), dim3(kBlock), 0, st, xv, nvec, partial);
+    else
+      hipLaunchKernelGGL((amax_partials_kernel<kF32>), dim3(ndyn), dim3(kBlock), 0, st, xv, nvec, partial);
+  }
+#define CALL(A, B)                                                                                           \
+  do {                                                                                                       \
+    if (mode == kScaleGiven)                                                                                 \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleGiven>), grid, block, 0, st, xv, rows, cols, o,    \
+                         scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals); \
+    else if (mode == kScaleRing)                                                                             \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleRing>), grid, block, 0, st, xv, rows, cols, o,     \
+                         scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals); \
+    else                                                                                                     \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleDynamic>), grid, block, 0, st, xv, rows, cols, o,  \
+                         scale_in, partial, ndyn, scale_out, amax, state, len, idx, margin, flag, partial,    \
+                         arrivals);                                                                          \
+    return hipGetLastError();                                                                                \
+  } while (0)
   HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
 #undef CALL
 }

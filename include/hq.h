@@ -128,6 +128,43 @@ hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Per-tensor FP8 quantization of a row-major [rows, cols] tensor written, in
+ * one pass over x, to any of four layouts (the fused quantize-plus-transpose
+ * of the hip-quant README, "Runtime codebooks and GPU execution features").
+ * Per-tensor codes do not depend on where they are stored, so each layout
+ * holds exactly the codes hq_quantize_fp8 would give (transposed or
+ * reordered):
+ *   q        [rows, cols] row-major codes
+ *   q_t      [cols, rows] row-major codes of the transpose
+ *   q_pre    hq_preshuffle_weight of q     (a GEMM weight with N = rows, K = cols)
+ *   q_t_pre  hq_preshuffle_weight of q_t   (N = cols, K = rows)
+ * Any of them may be NULL; at least one must not be. The pre-shuffled forms
+ * are sized hq_preshuffled_bytes(rows, cols) and hq_preshuffled_bytes(cols,
+ * rows), padding included (written as zero codes). For the backward GEMMs of a
+ * linear layer this replaces the transposed copies and the pre-shuffle passes.
+ *
+ * The scale comes from exactly one source:
+ *   scale_in != NULL  a given per-tensor dequant scale s (device float32 [1]):
+ *                     q = cast(fl32(x * fl32(1/s))), no reduction (AstrAI
+ *                     ops.cu, linear_backward_fp8: the weight and input are
+ *                     quantized again with their forward scales, no ring);
+ *                     amax_out must be NULL; no workspace is used
+ *   ring != NULL      delayed scaling, exactly as hq_quantize_fp8 with a ring
+ *   both NULL         dynamic per-tensor, exactly as hq_quantize_fp8 with
+ *                     HQ_PER_TENSOR (a partial-amax pass, then this pass)
+ * scale_out (device float32 [1]) receives the scale used; amax_out (optional)
+ * the tensor amax. workspace: hq_quantize_workspace_bytes(HQ_PER_TENSOR, rows,
+ * cols) bytes for the ring and dynamic forms, under the same zero-fill-once
+ * rule as hq_quantize_fp8 (may be NULL with scale_in).
+ * Requires cols % 16 == 0, and rows % 16 == 0 when q_t or q_t_pre is asked
+ * for; 16-byte aligned x and code buffers; no output may overlap another
+ * buffer. rows == 0 returns HQ_OK without a launch. */
+hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t cols, int fmt,
+                                  const float* scale_in, const hq_ring* ring,
+                                  uint8_t* q, uint8_t* q_t, uint8_t* q_pre, uint8_t* q_t_pre,
+                                  float* scale_out, float* amax_out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Fold one amax sample into a ring and publish the next scale (the delayed
  * update of hq_quantize_fp8, as its own launch). `amax` is a device float32
  * scalar; a NaN or Inf sample leaves the ring unchanged and sets the flag. */

@@ -139,6 +139,24 @@ def quantize_dynamic(x: np.ndarray, dtype: int, fmt: int, gran: int):
     return q, s, amax
 
 
+def quantize_with_scale(x: np.ndarray, dtype: int, fmt: int, s):
+    """Per-tensor quantization with a given dequant scale s (no reduction
+    decides it): q = encode(fl32(x * fl32(1 / s))). This is the backward
+    re-quantization of AstrAI ``ops.cu`` (``linear_backward_fp8`` quantizes the
+    weight and the input again with their forward scales, no ring update).
+
+    Returns (q uint8, s float32 [1], amax float32 [1]) with amax over the finite
+    elements, as the other forms report it.
+    """
+    x32 = widen(x, dtype)
+    if x32.ndim != 2:
+        raise ValueError("x must be 2-D")
+    s = np.asarray(s, dtype=np.float32).reshape(1)
+    q = cast_scaled(x32, reciprocal(s), PER_TENSOR, fmt)
+    amax, _ = group_amax(x32, PER_TENSOR)
+    return q, s, amax
+
+
 # ---------------------------------------------------------------------------
 # delayed scaling: the amax-history ring
 # ---------------------------------------------------------------------------

@@ -147,6 +147,46 @@ def test_quantize_valid_call_reaches_device_gate(hq):
     assert "gfx950" in hq.hq_last_error() or "device" in hq.hq_last_error()
 
 
+def _layouts(hq, x=fake(0), xt=1, rows=64, cols=128, fmt=0, scale_in=None, ring=None, q=fake(1), q_t=None,
+             q_pre=None, q_t_pre=None, s=fake(2), a=None, ws=fake(4), wsb=1 << 20):
+    return hq.load().hq_quantize_fp8_layouts(x, xt, rows, cols, fmt, scale_in, ring, q, q_t, q_pre, q_t_pre, s, a,
+                                             ws, wsb, None)
+
+
+def test_layouts_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    assert _layouts(hq, xt=5) == E
+    assert _layouts(hq, fmt=3) == E
+    assert _layouts(hq, cols=40) == E                                  # not a multiple of 16
+    assert _layouts(hq, rows=-2) == E
+    assert _layouts(hq, q=None) == E                                   # no layout requested
+    assert "layout" in hq.hq_last_error()
+    assert _layouts(hq, rows=40, q_t=fake(5)) == E                     # transposed needs rows % 16 == 0
+    assert _layouts(hq, rows=40, q_t_pre=fake(5)) == E
+    r = hq.hq_ring(BASE + 6 * (1 << 32), 16, 0, 0, None)
+    assert _layouts(hq, scale_in=fake(7), ring=ctypes.byref(r)) == E   # two scale sources
+    assert _layouts(hq, scale_in=fake(7), a=fake(3)) == E              # amax with a given scale
+    assert _layouts(hq, ws=ctypes.c_void_p(0)) == E                    # dynamic needs a workspace
+    assert _layouts(hq, wsb=16) == E
+    assert _layouts(hq, x=fake(0, 8)) == E                             # misaligned
+    assert _layouts(hq, q_pre=fake(5, 4)) == E
+    assert _layouts(hq, q_t=fake(0, 4096)) == E                        # q_t overlaps x
+    assert _layouts(hq, q_pre=fake(1, 8192 - 16)) == E                 # q_pre overlaps q (64 x 128 codes)
+    assert _layouts(hq, scale_in=fake(2), ws=None, wsb=0) == E         # scale_in overlaps scale_out
+    bad = hq.hq_ring(BASE + 6 * (1 << 32), 16, 16, 0, None)
+    assert _layouts(hq, ring=ctypes.byref(bad)) == E
+    assert _layouts(hq, rows=0, x=ctypes.c_void_p(0)) == hq.HQ_OK      # empty: no-op
+
+
+@no_gpu
+def test_layouts_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    assert _layouts(hq, q_t=fake(5), q_pre=fake(6), q_t_pre=fake(8)) == U
+    assert _layouts(hq, scale_in=fake(7), ws=None, wsb=0) == U
+    r = hq.hq_ring(BASE + 9 * (1 << 32), 16, 3, 0, BASE + 10 * (1 << 32))
+    assert _layouts(hq, ring=ctypes.byref(r), a=fake(3)) == U
+
+
 def _gemm(hq, xq=fake(0), xf=0, wq=fake(1), wf=0, xs=fake(2), xsc=64, ws=fake(3), wsc=128, m=64, n=128,
           k=256, out=fake(4), work=None, work_bytes=0):
     return hq.load().hq_gemm_a8w8(xq, xf, wq, wf, xs, xsc, ws, wsc, m, n, k, out, work, work_bytes, None)

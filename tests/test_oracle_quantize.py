@@ -170,3 +170,42 @@ def test_planted_mistake_is_caught():
     dec_bad = np.sign(v) * mags[np.clip(trunc, 0, 0x7E)]
     bound = 0.5 * _ulp_fp8(v, fp8.E4M3) + 2.0 ** -22 * np.abs(v)
     assert not np.all(np.abs(dec_bad - v) <= bound)
+
+
+# ---- per-tensor quantization with a given scale (backward re-quantization) ----
+
+@pytest.mark.parametrize("fmt", [fp8.E4M3, fp8.E5M2])
+def test_given_scale_equal_to_dynamic_scale_reproduces_dynamic_codes(fmt):
+    rng = np.random.default_rng(31)
+    bits = workloads.random_bf16(rng, (33, 48), std=3.0)
+    q_dyn, s_dyn, a_dyn = Q.quantize_dynamic(bits, Q.BF16, fmt, Q.PER_TENSOR)
+    q, s, a = Q.quantize_with_scale(bits, Q.BF16, fmt, s_dyn)
+    assert np.array_equal(q, q_dyn)
+    assert s.view(np.uint32)[0] == s_dyn.view(np.uint32)[0]
+    assert a.view(np.uint32)[0] == a_dyn.view(np.uint32)[0]
+
+
+@pytest.mark.parametrize("fmt", [fp8.E4M3, fp8.E5M2])
+def test_given_scale_saturates_above_fmax_and_rounds_within_half_ulp_below(fmt):
+    """A scale a quarter of the dynamic one pushes the largest values past fmax:
+    they must encode to +-max, the rest to within half an FP8 ulp (plus the
+    float32 rounding of x * r) of x / s, measured with the decode table."""
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((16, 64)).astype(np.float32)
+    fmax = fp8.fmax(fmt)
+    s = np.float32(np.abs(x).max() / fmax / 4.0)
+    q, s_out, amax = Q.quantize_with_scale(x, Q.F32, fmt, s)
+    assert s_out[0] == s and amax[0] == np.float32(np.abs(x).max())
+    table = fp8.decode_table(fmt)
+    v = x.astype(np.float64) / float(s)
+    dec = table[q]
+    max_code = 0x7E if fmt == fp8.E4M3 else 0x7B
+    big = np.abs(v) > fmax * (1 + 2.0 ** -20)
+    assert big.any()
+    assert np.all(q[big] == np.where(v[big] > 0, max_code, 0x80 | max_code))
+    small = np.abs(v) < fmax * (1 - 2.0 ** -20)
+    mant = 3 if fmt == fp8.E4M3 else 2
+    emin = -6 if fmt == fp8.E4M3 else -14
+    e = np.floor(np.log2(np.maximum(np.abs(v[small]), 2.0 ** emin)))
+    half_ulp = np.ldexp(0.5, (e - mant).astype(np.int64))
+    assert np.all(np.abs(dec[small] - v[small]) <= half_ulp + 2.0 ** -22 * np.abs(v[small]))
