@@ -22,6 +22,9 @@ HQ_BF16 = 1
 HQ_PER_TENSOR = 0
 HQ_PER_TOKEN = 1
 HQ_PER_CHANNEL = 2
+HQ_BIAS_BF16 = 0
+HQ_BIAS_E4M3 = 1
+HQ_BIAS_E5M2 = 2
 
 
 class hq_ring(ctypes.Structure):
@@ -32,6 +35,11 @@ class hq_ring(ctypes.Structure):
         ("margin", ctypes.c_int32),
         ("nonfinite_flag", ctypes.c_void_p),
     ]
+
+
+class hq_epilogue(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_type", ctypes.c_int32), ("bias_scale", ctypes.c_void_p),
+                ("out_scale", ctypes.c_void_p), ("out_fmt", ctypes.c_int32)]
 
 
 class HQError(RuntimeError):
@@ -72,6 +80,8 @@ SIGNATURES = {
     "hq_preshuffle_weight": (_I, [_P, _I64, _I64, _P, _P]),
     "hq_gemm_workspace_bytes": (_I64, [_I64, _I64, _I64]),
     "hq_gemm_a8w8": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "hq_gemm_a8w8_epilogue": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, ctypes.POINTER(hq_epilogue),
+                                   _P, _P, _SZ, _P]),
     "hq_grouped_gemm_a8w8": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P]),
     "hq_last_error": (ctypes.c_char_p, []),
 }

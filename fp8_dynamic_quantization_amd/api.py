@@ -12,12 +12,13 @@ import ctypes
 
 import torch
 
-from ._lib import (HQ_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANNEL, HQ_PER_TENSOR,
-                   HQ_PER_TOKEN, check, hq_ring, load)
+from ._lib import (HQ_BF16, HQ_BIAS_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANNEL, HQ_PER_TENSOR,
+                   HQ_PER_TOKEN, check, hq_epilogue, hq_ring, load)
 
 __all__ = [
     "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
     "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
+    "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_last_error",
 ]
 
@@ -209,6 +210,37 @@ def hq_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_sca
     check(lib.hq_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
                            _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(xq.device, stream)))
+    return out
+
+
+def hq_gemm_a8w8_epilogue(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_scale: torch.Tensor,
+                          w_scale: torch.Tensor, n: int, *, bias: torch.Tensor | None = None,
+                          bias_type: int = HQ_BIAS_BF16, bias_scale: torch.Tensor | None = None,
+                          out_scale: torch.Tensor | None = None, out_fmt: int = HQ_E4M3, out=None,
+                          workspace=None, stream=None) -> torch.Tensor:
+    """hq_gemm_a8w8 with a bias (bf16 tensor, or uint8 FP8 codes with
+    bias_scale) added after the scales, and bf16 output or, with out_scale,
+    FP8 (out_fmt) codes of v / out_scale. Returns out (bf16 or uint8 [m, n])."""
+    xq = xq.contiguous()
+    m, k = xq.shape
+    x_scale = x_scale.contiguous()
+    w_scale = w_scale.contiguous()
+    if bias is not None:
+        bias = bias.contiguous()
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.uint8 if out_scale is not None else torch.bfloat16, device=xq.device)
+    lib = load()
+    if workspace is None:
+        workspace = gemm_workspace(xq.device, int(lib.hq_gemm_workspace_bytes(m, n, k)))
+    elif workspace is False:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ep = hq_epilogue(0 if bias is None else bias.data_ptr(), int(bias_type),
+                     0 if bias_scale is None else bias_scale.data_ptr(),
+                     0 if out_scale is None else out_scale.data_ptr(), int(out_fmt))
+    check(lib.hq_gemm_a8w8_epilogue(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                                    _ptr(w_scale), w_scale.numel(), m, n, k, ctypes.byref(ep), _ptr(out),
+                                    _ptr(workspace), ws_bytes, _stream(xq.device, stream)))
     return out
 
 

@@ -83,6 +83,41 @@ hipError_t launch_preshuffle(const uint8_t* wq, int n, int k, uint8_t* out, hipS
 }
 
 // ---------------------------------------------------------------------------
+// epilogue helpers (bias, FP8 output)
+// ---------------------------------------------------------------------------
+// The bias of output column `col` as float32: a bf16 value widened, or an FP8
+// code decoded (v_cvt_f32_fp8 / v_cvt_f32_bf8, exact) times the bias scale.
+__device__ __forceinline__ float bias_at(const GemmArgs& a, int col, float bscale) {
+  if (a.bias_kind == kBiasBF16) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.bias)[col] << 16);
+  const int code = static_cast<const uint8_t*>(a.bias)[col];
+  const float d = a.bias_kind == kBiasE4M3 ? __builtin_amdgcn_cvt_f32_fp8(code, 0) : __builtin_amdgcn_cvt_f32_bf8(code, 0);
+  return d * bscale;
+}
+
+// N (4 or 8) epilogue values to FP8 codes of fl32(v * r_out) (saturating RNE,
+// NaN -> 0x7F), stored as one N-byte write when `full`, else byte by byte up
+// to `left` columns.
+template <int N>
+__device__ __forceinline__ void store_fp8_out(uint8_t* dst, const float* v, float r_out, int fmt, bool full,
+                                              int left) {
+  uint32_t w[N / 4];
+#pragma unroll
+  for (int d = 0; d < N / 4; ++d) {
+    const float x0 = v[4 * d] * r_out, x1 = v[4 * d + 1] * r_out, x2 = v[4 * d + 2] * r_out, x3 = v[4 * d + 3] * r_out;
+    w[d] = fmt == kE4M3 ? cvt4<kE4M3>(x0, x1, x2, x3) : cvt4<kE5M2>(x0, x1, x2, x3);
+    w[d] = patch_nan4(w[d], x0, x1, x2, x3);
+  }
+  if (full) {
+    if constexpr (N == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint32_t*>(dst) = w[0];
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (e < left) dst[e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // GEMM tile
 // ---------------------------------------------------------------------------
 // Per 128-deep K step a wavefront issues BM/16 x TN/16 MFMAs. A is double-
@@ -98,7 +133,7 @@ struct BsCfg {
   static constexpr int kAVec = BM * 8 / kThreads;  // 16-byte A pieces per thread per stage
   static constexpr int kRowStep = kThreads / 8;    // rows between a thread's A pieces
   static constexpr int kABytes = BM * kBK;         // one LDS stage
-  static constexpr int kLdsBytes = 2 * kABytes + (BM + kBN) * 4;  // two A stages + epilogue scales
+  static constexpr int kLdsBytes = 2 * kABytes + (BM + 2 * kBN) * 4;  // two A stages + epilogue scales and bias
   static_assert(BM % 32 == 0 && TN % 32 == 0 && kWR % 16 == 0, "tile");
 };
 
@@ -152,6 +187,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   for (int t = tid; t < C::kBN; t += C::kThreads) {
     const int col = min(n0 + t, a.n - 1);
     s_ws[t] = a.w_scale_per_col ? ws[col] : ws[0];
+  }
+  float* s_bias = s_ws + C::kBN;
+  if (a.bias_kind != kBiasNone) {
+    const float bsc = a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0];
+    for (int t = tid; t < C::kBN; t += C::kThreads) s_bias[t] = bias_at(a, min(n0 + t, a.n - 1), bsc);
   }
 
   // MFMA-order reads: fragment i is rows i*16 .. i*16+15; lane l reads row
@@ -272,8 +312,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 
   // Epilogue: fragment pair (2*jp, 2*jp+1) gives lane l the 8 consecutive output
   // columns n0 + wave*TN + 32*jp + 8*(l/16) .. +7 of row m0 + 16*i + l%16.
-  // Scale in fp32, round to bf16 (v_cvt_pk_bf16_f32, nearest-even), store 16 bytes.
+  // Scale in fp32 (plus the bias), then either round to bf16
+  // (v_cvt_pk_bf16_f32, nearest-even) and store 16 bytes, or cast to FP8 codes
+  // and store 8 bytes.
   const bool vec_ok = (a.n & 7) == 0;
+  const float r_out = a.out_scale ? 1.0f / a.out_scale[0] : 0.0f;
   const int ccol = 8 * (lane >> 4);
   float wsc[C::kIN / 2][8];
 #pragma unroll
@@ -290,20 +333,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
       const int col0 = n0 + wave * TN + 32 * jp + ccol;
       if (col0 >= a.n) continue;
       const v4f p0 = acc[i][2 * jp], p1 = acc[i][2 * jp + 1];
-      const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-      uint32_t w[4];
+      float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f2v pr = {v[2 * e] * xsc * wsc[jp][2 * e], v[2 * e + 1] * xsc * wsc[jp][2 * e + 1]};
-        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * wsc[jp][e];
+      if (a.bias_kind != kBiasNone) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += s_bias[wave * TN + 32 * jp + ccol + e];
       }
-      uint16_t* dst = a.out + (size_t)row * a.n + col0;
-      if (vec_ok && col0 + 8 <= a.n) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      const size_t off = (size_t)row * a.n + col0;
+      const bool full = vec_ok && col0 + 8 <= a.n;
+      if (a.out_scale) {
+        store_fp8_out<8>(static_cast<uint8_t*>(a.out) + off, v, r_out, a.out_fmt, full, a.n - col0);
       } else {
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (col0 + e < a.n) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < 4; ++e) {
+          const f2v pr = {v[2 * e], v[2 * e + 1]};
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
+        }
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + off;
+        if (full) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col0 + e < a.n) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
       }
     }
   }
@@ -446,7 +501,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
   // Epilogue scales of every slice this lane may store, fetched before the K
   // loop so their latency hides behind it (indices clamped; masked on store).
   // Slice (f, i): row 16*i + l%16, columns col0(f) .. +3 (see the epilogue).
-  float xs_r[MB], ws_r[F][4];
+  float xs_r[MB], ws_r[F][4], b_r[F][4];
 #pragma unroll
   for (int i = 0; i < MB; ++i) xs_r[i] = a.x_scale[a.x_scale_per_row ? min(i * 16 + xr, a.m - 1) : 0];
 #pragma unroll
@@ -454,8 +509,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
     const int nb = nb0 + f;
     const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ws_r[f][e] = a.w_scale[a.w_scale_per_col ? min(col0 + e, a.n - 1) : 0];
+    for (int e = 0; e < 4; ++e) {
+      ws_r[f][e] = a.w_scale[a.w_scale_per_col ? min(col0 + e, a.n - 1) : 0];
+      b_r[f][e] = a.bias_kind == kBiasNone
+                      ? 0.0f
+                      : bias_at(a, min(col0 + e, a.n - 1), a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0]);
+    }
   }
+  const float r_out = a.out_scale ? 1.0f / a.out_scale[0] : 0.0f;
 
   v4f acc[F][MB];
 #pragma unroll
@@ -512,14 +573,27 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
     const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
     if (row >= a.m || col0 >= a.n) return;
     const float xsc = xs_r[i];
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = t[e] * xsc * ws_r[f][e];
+    if (a.bias_kind != kBiasNone) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += b_r[f][e];
+    }
+    const size_t off = (size_t)row * a.n + col0;
+    const bool full = (a.n & 3) == 0;
+    if (a.out_scale) {
+      store_fp8_out<4>(static_cast<uint8_t*>(a.out) + off, v, r_out, a.out_fmt, full, a.n - col0);
+      return;
+    }
     uint32_t w2[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const f2v pr = {t[2 * e] * xsc * ws_r[f][2 * e], t[2 * e + 1] * xsc * ws_r[f][2 * e + 1]};
+      const f2v pr = {v[2 * e], v[2 * e + 1]};
       w2[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
     }
-    uint16_t* dst = a.out + (size_t)row * a.n + col0;
-    if ((a.n & 3) == 0) {
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + off;
+    if (full) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(w2[0], w2[1]);
     } else {
       for (int e = 0; e < 4; ++e)

@@ -336,6 +336,14 @@ int64_t hq_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
                        int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m, int64_t n,
                        int64_t k, uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return hq_gemm_a8w8_epilogue(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count, m, n, k, nullptr,
+                               out, workspace, workspace_bytes, stream);
+}
+
+hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                                int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m,
+                                int64_t n, int64_t k, const hq_epilogue* ep, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, m, n, k);
   if (st != HQ_OK) return st;
   if (workspace_bytes > 0 && workspace == nullptr)
@@ -346,28 +354,52 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
     return fail(HQ_ERR_INVALID_ARGUMENT, "x_scale_count must be 1 or m (%lld), got %lld", (long long)m, (long long)x_scale_count);
   if (w_scale_count != 1 && w_scale_count != n)
     return fail(HQ_ERR_INVALID_ARGUMENT, "w_scale_count must be 1 or n (%lld), got %lld", (long long)n, (long long)w_scale_count);
+  const void* bias = ep ? ep->bias : nullptr;
+  const float* bias_scale = ep ? ep->bias_scale : nullptr;
+  const float* out_scale = ep ? ep->out_scale : nullptr;
+  int bias_kind = hq::kBiasNone;
+  if (bias) {
+    switch (ep->bias_type) {
+      case HQ_BIAS_BF16: bias_kind = hq::kBiasBF16; break;
+      case HQ_BIAS_E4M3: bias_kind = hq::kBiasE4M3; break;
+      case HQ_BIAS_E5M2: bias_kind = hq::kBiasE5M2; break;
+      default: return fail(HQ_ERR_INVALID_ARGUMENT, "unknown bias_type %d", ep->bias_type);
+    }
+    if ((bias_kind == hq::kBiasBF16) != (bias_scale == nullptr))
+      return fail(HQ_ERR_INVALID_ARGUMENT, "an FP8 bias requires bias_scale and a bf16 bias takes none");
+  } else if (bias_scale) {
+    return fail(HQ_ERR_INVALID_ARGUMENT, "bias_scale given without a bias");
+  }
+  if (out_scale && !valid_fmt(ep->out_fmt))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "out_fmt must be HQ_E4M3 or HQ_E5M2, got %d", ep->out_fmt);
   if (m == 0 || n == 0) return ok();
   if (!xq || !wq_pre || !x_scale || !w_scale || !out)
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scale, w_scale and out must be non-NULL");
   if (!aligned(xq, 16) || !aligned(wq_pre, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "xq and wq_pre must be 16-byte aligned");
   if (!aligned(out, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
-  if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return fail(HQ_ERR_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || (bias_scale && !aligned(bias_scale, 4)) ||
+      (out_scale && !aligned(out_scale, 4)) || (bias_kind == hq::kBiasBF16 && !aligned(bias, 2)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scales must be 4-byte aligned and a bf16 bias 2-byte aligned");
   const size_t ws_used = workspace_bytes > 0 ? workspace_bytes : 0;
   const Range rg[] = {
-      {out, (size_t)m * (size_t)n * 2, "out"},
+      {out, (size_t)m * (size_t)n * (out_scale ? 1 : 2), "out"},
       {workspace, ws_used, "workspace"},
       {xq, (size_t)m * (size_t)k, "xq"},
       {wq_pre, (size_t)padded_bytes(n, k), "wq_pre"},
       {x_scale, (size_t)x_scale_count * 4, "x_scale"},
       {w_scale, (size_t)w_scale_count * 4, "w_scale"},
+      {bias, bias ? (size_t)n * (bias_kind == hq::kBiasBF16 ? 2 : 1) : 0, "bias"},
+      {bias_scale, bias_scale ? 4u : 0u, "bias_scale"},
+      {out_scale, out_scale ? 4u : 0u, "out_scale"},
   };
   const char* other = nullptr;
-  const char* a = find_overlap(rg, 6, &other);
+  const char* a = find_overlap(rg, 9, &other);
   if (a && (strcmp(a, "out") == 0 || strcmp(a, "workspace") == 0))
     return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
   st = check_device();
   if (st != HQ_OK) return st;
-  hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1};
+  hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1,
+                 bias, bias_kind, bias_scale, out_scale, out_scale ? ep->out_fmt : 0};
   (void)hipGetLastError();
   return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), "hq_gemm_a8w8");
 }

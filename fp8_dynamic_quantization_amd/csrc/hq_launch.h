@@ -53,15 +53,26 @@ hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_
 
 hipError_t launch_preshuffle(const uint8_t* wq, int n, int k, uint8_t* out, hipStream_t st);
 
+// Epilogue bias kinds (GemmArgs::bias_kind).
+constexpr int kBiasNone = 0, kBiasBF16 = 1, kBiasE4M3 = 2, kBiasE5M2 = 3;
+
 struct GemmArgs {
   const uint8_t* xq;      // [m, k] row-major
   const uint8_t* wq_pre;  // pre-shuffled weight(s)
   const float* x_scale;   // [1] or [m]
   const float* w_scale;   // [1] or [n] (per expert in the grouped form)
-  uint16_t* out;          // bf16 [m, n]
+  void* out;              // bf16 [m, n]; FP8 codes [m, n] when out_scale is set
   int m, n, k;
   int x_scale_per_row;    // 0: x_scale[0] for every row
   int w_scale_per_col;    // 0: w_scale[0] (per expert) for every column
+  // Epilogue (all zero: bf16 output, no bias). v = fl32(fl32(acc * x_s) * w_s);
+  // with a bias v = fl32(v + bias[col]); out = bf16(v), or with out_scale the
+  // FP8 (out_fmt) code of fl32(v * fl32(1 / out_scale[0])).
+  const void* bias;        // [n]: bf16 bits or FP8 codes, per bias_kind
+  int bias_kind;           // kBias*
+  const float* bias_scale; // [1]: dequant scale of an FP8 bias
+  const float* out_scale;  // [1] or null
+  int out_fmt;             // kE4M3 / kE5M2 (with out_scale)
 };
 
 // Decode-shape (small M) launch plan: MB 16-row activation blocks, F weight

@@ -222,6 +222,46 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                        int64_t m, int64_t n, int64_t k, uint16_t* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Kinds of GEMM epilogue bias (AstrAI ops.cu, linear_forward_fp8: a bf16 bias
+ * as is, or a pre-quantized FP8 bias with its bias_scale). */
+typedef enum hq_bias { HQ_BIAS_BF16 = 0, HQ_BIAS_E4M3 = 1, HQ_BIAS_E5M2 = 2 } hq_bias;
+
+/* GEMM epilogue options (host struct):
+ *   bias        device [n], one value per output column: bf16 bits
+ *               (HQ_BIAS_BF16) or FP8 codes (HQ_BIAS_E4M3 / HQ_BIAS_E5M2);
+ *               NULL for no bias
+ *   bias_type   an hq_bias value
+ *   bias_scale  device float32 [1]: dequant scale of an FP8 bias (required
+ *               for FP8, must be NULL for bf16)
+ *   out_scale   device float32 [1]: when non-NULL the output is FP8 codes
+ *               (AstrAI ops.cu, mm_fp8: FP8 E4M3 output "requires out_scale,
+ *               the output quantization step"); NULL for bf16 output
+ *   out_fmt     HQ_E4M3 or HQ_E5M2, the FP8 output format (with out_scale) */
+typedef struct hq_epilogue {
+  const void* bias;
+  int32_t bias_type;
+  const float* bias_scale;
+  const float* out_scale;
+  int32_t out_fmt;
+} hq_epilogue;
+
+/* hq_gemm_a8w8 with an epilogue. Per output element, in float32:
+ *   v = fl32(fl32(acc * x_scale[m]) * w_scale[n])
+ *   v = fl32(v + b[n])        with a bias, b = bf16 value or fl32(dec(code) * bias_scale)
+ *   out[m, n] = bf16_rne(v), or with out_scale the saturating RNE FP8 code of
+ *               fl32(v * fl32(1 / out_scale))   (NaN -> 0x7F)
+ * `ep` is a host pointer (NULL = plain bf16 output, exactly hq_gemm_a8w8).
+ * `out` is bf16 [m, n] (2 bytes per element) or uint8 codes [m, n] with
+ * out_scale; 16-byte aligned, caller-owned, must not overlap any input. All
+ * other arguments, the workspace rule and the requirements are those of
+ * hq_gemm_a8w8. */
+hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                                const float* x_scale, int64_t x_scale_count,
+                                const float* w_scale, int64_t w_scale_count,
+                                int64_t m, int64_t n, int64_t k, const hq_epilogue* ep,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* Grouped (per-expert) scaled FP8 GEMM over row ranges (megablocks-hip grouped
  * GEMM notes: per-expert products of concatenated tokens, written over, never
  * accumulated into, the output). For each expert e with rows

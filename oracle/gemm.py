@@ -142,6 +142,48 @@ def grouped_gemm_a8w8(xq, xf: int, wq_experts, wf: int, x_scale, w_scale, offset
     return ref, at, covered
 
 
+# ---------------------------------------------------------------------------
+# epilogue variants (AstrAI ops.cu: linear_forward_fp8 adds a bias in the GEMM
+# epilogue, bf16 as is or FP8 codes times bias_scale; mm_fp8 can emit FP8
+# E4M3 output, which requires out_scale, "the output quantization step")
+# ---------------------------------------------------------------------------
+BIAS_BF16 = 0
+BIAS_E4M3 = 1
+BIAS_E5M2 = 2
+
+
+def bias_values(bias, kind: int, bias_scale=None) -> np.ndarray:
+    """The bias as float64: bf16 bit patterns widened exactly, or FP8 codes
+    decoded and multiplied by the float32 bias_scale in float32."""
+    if kind == BIAS_BF16:
+        if bias_scale is not None:
+            raise ValueError("a bf16 bias takes no bias_scale")
+        return bf16_bits_to_f64(bias)
+    fmt = {BIAS_E4M3: fp8.E4M3, BIAS_E5M2: fp8.E5M2}[kind]
+    dec = fp8.decode(np.asarray(bias, dtype=np.uint8), fmt).astype(np.float32)
+    return (dec * np.float32(np.asarray(bias_scale, dtype=np.float32).reshape(-1)[0])).astype(np.float32).astype(
+        np.float64)
+
+
+def epilogue_f32(acc, x_scale, w_scale, bias_f32=None, out_scale=None, out_fmt=None):
+    """The epilogue's float32 arithmetic on float32 accumulators acc [P]
+    (one per output element, with its row's x_scale and column's w_scale and
+    bias): v = fl32(fl32(acc * x_s) * w_s); with a bias v = fl32(v + b); then
+    the bf16 output (round to nearest even) or, with out_scale, the FP8 code
+    of fl32(v * fl32(1 / out_scale)) (the output quantization, read as the
+    input quantization reads its scale: a reciprocal once, then a multiply).
+    Returns uint16 bf16 bits or uint8 codes."""
+    v = (np.asarray(acc, dtype=np.float32) * np.asarray(x_scale, dtype=np.float32)).astype(np.float32)
+    v = (v * np.asarray(w_scale, dtype=np.float32)).astype(np.float32)
+    if bias_f32 is not None:
+        v = (v + np.asarray(bias_f32, dtype=np.float32)).astype(np.float32)
+    if out_scale is None:
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    r = (np.float32(1.0) / np.float32(np.asarray(out_scale, dtype=np.float32).reshape(-1)[0])).astype(np.float32)
+    return fp8.encode((v * r).astype(np.float32), out_fmt)
+
+
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Decode bf16 bit patterns (uint16) of a GEMM output to float64."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -260,6 +260,36 @@ def _grouped(hq, e=8, t=512, n=128, k=256, xsc=512, wsc=None, off=fake(5), out=f
                                           out, None)
 
 
+def _gemm_ep(hq, ep, out=fake(4), m=64, n=128, k=256):
+    return hq.load().hq_gemm_a8w8_epilogue(fake(0), 0, fake(1), 0, fake(2), m, fake(3), n, m, n, k,
+                                           ctypes.byref(ep) if ep is not None else None, out, None, 0, None)
+
+
+def test_gemm_epilogue_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    bias, bsc, osc = BASE + 5 * (1 << 32), BASE + 6 * (1 << 32), BASE + 7 * (1 << 32)
+    assert _gemm_ep(hq, hq.hq_epilogue(bias, 7, None, None, 0)) == E                 # unknown bias type
+    assert _gemm_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_E4M3, None, None, 0)) == E   # FP8 bias needs a scale
+    assert _gemm_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_BF16, bsc, None, 0)) == E    # bf16 bias takes none
+    assert _gemm_ep(hq, hq.hq_epilogue(None, 0, bsc, None, 0)) == E                  # scale without bias
+    assert _gemm_ep(hq, hq.hq_epilogue(None, 0, None, osc, 5)) == E                  # bad out_fmt
+    assert _gemm_ep(hq, hq.hq_epilogue(bias + 1, hq.HQ_BIAS_BF16, None, None, 0)) == E   # misaligned bf16 bias
+    assert _gemm_ep(hq, hq.hq_epilogue(None, 0, None, osc + 2, 0)) == E              # misaligned out_scale
+    # FP8 output is m*n bytes: out right after its end is fine, one byte earlier overlaps the bias
+    assert _gemm_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) + 64 * 128 - 1, hq.HQ_BIAS_E4M3, bsc, osc, 0)) == E
+    assert "overlaps" in hq.hq_last_error()
+
+
+@no_gpu
+def test_gemm_epilogue_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    bias, bsc, osc = BASE + 5 * (1 << 32), BASE + 6 * (1 << 32), BASE + 7 * (1 << 32)
+    assert _gemm_ep(hq, None) == U
+    assert _gemm_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_BF16, None, None, 0)) == U
+    assert _gemm_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_E5M2, bsc, osc, hq.HQ_E5M2)) == U
+    assert _gemm_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) + 64 * 128, hq.HQ_BIAS_E4M3, bsc, osc, 0)) == U
+
+
 def test_grouped_validation(hq):
     E = hq.HQ_ERR_INVALID_ARGUMENT
     assert _grouped(hq, e=0) == E

@@ -166,3 +166,49 @@ def test_workload_generators_are_deterministic():
     counts = np.diff(offsets)
     assert offsets[0] == 0 and offsets[-1] == 64
     assert counts[1] == 0 and counts[5] == 0
+
+
+# ---- epilogue variants (bias, FP8 output) ----------------------------------------
+
+def test_bias_values_closed_forms():
+    import torch
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0000, 0x8000], dtype=np.uint16)   # 1, -2, 0.25, 0, -0
+    assert np.array_equal(G.bias_values(bits, G.BIAS_BF16),
+                          torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy())
+    # E4M3: 0x38 = 1, 0x40 = 2, 0x30 = 0.5, 0xB8 = -1, 0x7E = 448; scale 0.25 keeps them exact
+    e4 = np.array([0x38, 0x40, 0x30, 0xB8, 0x7E], dtype=np.uint8)
+    assert G.bias_values(e4, G.BIAS_E4M3, np.float32(0.25)).tolist() == [0.25, 0.5, 0.125, -0.25, 112.0]
+    # E5M2: 0x3C = 1, 0x40 = 2, 0x7B = 57344, 0x01 = 2^-16
+    e5 = np.array([0x3C, 0x40, 0x7B, 0x01], dtype=np.uint8)
+    assert G.bias_values(e5, G.BIAS_E5M2, np.float32(2.0)).tolist() == [2.0, 4.0, 114688.0, 2.0 ** -15]
+    with pytest.raises(ValueError):
+        G.bias_values(bits, G.BIAS_BF16, np.float32(1.0))
+
+
+def test_epilogue_bf16_closed_forms():
+    # exact products, then one value exactly halfway between two bf16 numbers (ties to even)
+    acc = np.array([3.0, 5.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8], dtype=np.float32)
+    out = G.epilogue_f32(acc, np.float32(0.5), np.float32(4.0))
+    got = G.bf16_bits_to_f64(out)
+    assert got.tolist() == [6.0, 10.0, 2.0, 2.0 + 2.0 ** -5]
+    # bias added in float32 after the scales
+    out = G.epilogue_f32(np.array([1.0], np.float32), np.float32(1.0), np.float32(1.0), bias_f32=np.float32(-3.0))
+    assert G.bf16_bits_to_f64(out).tolist() == [-2.0]
+
+
+@pytest.mark.parametrize("fmt", [fp8.E4M3, fp8.E5M2])
+def test_epilogue_fp8_output_closed_forms(fmt):
+    table = fp8.decode_table(fmt)
+    finite = np.array([c for c in range(256) if np.isfinite(table[c])], dtype=np.uint8)
+    # every finite code value times a power-of-two out_scale comes back as its own code
+    out_scale = np.float32(0.125)
+    vals = (table[finite] * 0.125).astype(np.float32)
+    codes = G.epilogue_f32(vals, np.float32(1.0), np.float32(1.0), out_scale=out_scale, out_fmt=fmt)
+    want = finite.copy()
+    want[table[finite] == 0] = np.where(np.signbit(table[finite][table[finite] == 0]), 0x80, 0x00)
+    assert np.array_equal(codes, want)
+    # saturation and NaN
+    big = np.array([1e30, -1e30, np.nan], dtype=np.float32)
+    codes = G.epilogue_f32(big, np.float32(1.0), np.float32(1.0), out_scale=np.float32(1.0), out_fmt=fmt)
+    mx = 0x7E if fmt == fp8.E4M3 else 0x7B
+    assert codes.tolist() == [mx, 0x80 | mx, 0x7F]
