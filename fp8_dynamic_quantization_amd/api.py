@@ -17,7 +17,7 @@ from ._lib import (HQ_BF16, HQ_BIAS_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANN
 
 __all__ = [
     "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
-    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
+    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_stochastic", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_last_error",
 ]
@@ -100,6 +100,38 @@ def hq_quantize_fp8(x: torch.Tensor, fmt: int = HQ_E4M3, gran: int = HQ_PER_TOKE
     ring_c = ctypes.byref(ring.c_struct(ring_idx)) if ring is not None else None
     st = lib.hq_quantize_fp8(_ptr(x), _XT[x.dtype], rows, cols, fmt, gran, _ptr(q), _ptr(scale_out),
                              _ptr(amax_out), ring_c, _ptr(workspace), ws_bytes, _stream(dev, stream))
+    check(st)
+    return q, scale_out, amax_out
+
+
+def hq_quantize_fp8_stochastic(x: torch.Tensor, gran: int = HQ_PER_TOKEN, seed: int = 0, *,
+                               ring: Ring | None = None, ring_idx: int = 0, q=None, scale_out=None,
+                               amax_out=None, workspace=None, stream=None):
+    """E5M2 quantization with stochastic rounding (reproducible for a seed);
+    returns (q uint8, scale_out fp32, amax_out fp32) like hq_quantize_fp8."""
+    if x.dtype not in _XT:
+        raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    x = x.contiguous()
+    rows, cols = x.shape
+    lib = load()
+    count = max(int(lib.hq_scale_count(gran, rows, cols)), 0)
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scale_out is None:
+        scale_out = torch.empty(count, dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty(count, dtype=torch.float32, device=dev)
+    need = int(lib.hq_quantize_workspace_bytes(gran, rows, cols))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ring_c = ctypes.byref(ring.c_struct(ring_idx)) if ring is not None else None
+    st = lib.hq_quantize_fp8_stochastic(_ptr(x), _XT[x.dtype], rows, cols, gran, int(seed) & (2 ** 64 - 1), _ptr(q),
+                                        _ptr(scale_out), _ptr(amax_out), ring_c, _ptr(workspace), ws_bytes,
+                                        _stream(dev, stream))
     check(st)
     return q, scale_out, amax_out
 

@@ -150,9 +150,29 @@ int64_t hq_preshuffled_bytes(int64_t n, int64_t k) {
   return padded_bytes(n, k);
 }
 
+static hq_status quantize_impl(const void* x, int xt, int64_t rows, int64_t cols, int fmt, int gran, uint8_t* q,
+                               float* scale_out, float* amax_out, const hq_ring* ring, void* workspace,
+                               size_t workspace_bytes, bool sr, uint64_t seed, hipStream_t stream,
+                               const char* name);
+
 hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int fmt, int gran, uint8_t* q,
                           float* scale_out, float* amax_out, const hq_ring* ring, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
+  return quantize_impl(x, xt, rows, cols, fmt, gran, q, scale_out, amax_out, ring, workspace, workspace_bytes, false,
+                       0, stream, "hq_quantize_fp8");
+}
+
+hq_status hq_quantize_fp8_stochastic(const void* x, int xt, int64_t rows, int64_t cols, int gran, uint64_t seed,
+                                     uint8_t* q, float* scale_out, float* amax_out, const hq_ring* ring,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return quantize_impl(x, xt, rows, cols, HQ_E5M2, gran, q, scale_out, amax_out, ring, workspace, workspace_bytes,
+                       true, seed, stream, "hq_quantize_fp8_stochastic");
+}
+
+static hq_status quantize_impl(const void* x, int xt, int64_t rows, int64_t cols, int fmt, int gran, uint8_t* q,
+                               float* scale_out, float* amax_out, const hq_ring* ring, void* workspace,
+                               size_t workspace_bytes, bool sr, uint64_t seed, hipStream_t stream,
+                               const char* name) {
   if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
   if (gran != HQ_PER_TENSOR && gran != HQ_PER_TOKEN && gran != HQ_PER_CHANNEL)
@@ -199,15 +219,15 @@ hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols, int
   hipError_t e;
   if (ring) {
     e = hq::launch_quant_delayed(x, xt, numel, fmt, q, scale_out, amax_out, ring->state, ring->len, ring->idx,
-                                 ring->margin, ring->nonfinite_flag, workspace, stream);
+                                 ring->margin, ring->nonfinite_flag, workspace, sr, seed, stream);
   } else if (gran == HQ_PER_TOKEN) {
-    e = hq::launch_quant_rows(x, xt, (int)rows, (int)cols, fmt, q, scale_out, amax_out, stream);
+    e = hq::launch_quant_rows(x, xt, (int)rows, (int)cols, fmt, q, scale_out, amax_out, sr, seed, stream);
   } else if (gran == HQ_PER_TENSOR) {
-    e = hq::launch_quant_tensor(x, xt, numel, fmt, q, scale_out, amax_out, workspace, stream);
+    e = hq::launch_quant_tensor(x, xt, numel, fmt, q, scale_out, amax_out, workspace, sr, seed, stream);
   } else {
-    e = hq::launch_quant_cols(x, xt, (int)rows, (int)cols, fmt, q, scale_out, amax_out, workspace, stream);
+    e = hq::launch_quant_cols(x, xt, (int)rows, (int)cols, fmt, q, scale_out, amax_out, workspace, sr, seed, stream);
   }
-  return launched(e, "hq_quantize_fp8");
+  return launched(e, name);
 }
 
 hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t cols, int fmt, const float* scale_in,

@@ -128,6 +128,86 @@ __device__ __forceinline__ void vec_cast_checked(const uint4& v, float r, uint32
   else vec_cast<XT, FMT>(v, r, false, out);
 }
 
+// ---- stochastic rounding to E5M2 -------------------------------------------------
+// (hip-quant README, "Stochastic E5M2 Backward Gradients": round to one of the
+// two adjacent E5M2 values, up with probability proportional to the distance
+// from the lower one, from a stateless hash of (seed, element index).) The
+// hash is Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): element i uses
+// word i % 4 of Philox(counter = (i/4 low, i/4 high, 0, 0), key = seed) and
+// u = (word >> 8) * 2^-24. Every quantity the decision compares is exact in
+// float32, so the choice is deterministic given (seed, i).
+
+struct SrSeed {
+  uint32_t k0, k1;  // seed, low and high 32 bits
+};
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The four hash words of elements i .. i+3 (i a multiple of 4).
+__device__ __forceinline__ uint4 sr_words(SrSeed sd, size_t i) {
+  const uint64_t blk = (uint64_t)i >> 2;
+  return philox4x32_10(make_uint4((uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u), sd.k0, sd.k1);
+}
+
+// E5M2 code of the scaled value y with hash word `word`. lo <= |y| < hi are the
+// adjacent E5M2 magnitudes (ulp = hi - lo, a power of two: 2^(e-2) in binade
+// e >= -14, 2^-16 below); p = (|y| - lo) / ulp and u are exact, and the
+// magnitude is hi when u < p. |y| >= 57344 (Inf too) saturates, NaN -> 0x7F,
+// the sign is kept. The chosen value is exact in E5M2, so the nearest-even
+// conversion returns its code.
+__device__ __forceinline__ uint32_t e5m2_sr_code(float y, uint32_t word) {
+  const float a = fabsf(y);
+  if (!(a < 57344.0f)) return a != a ? 0x7Fu : ((__float_as_uint(y) >> 24) & 0x80u) | 0x7Bu;
+  float lo, ulp, inv;
+  if (a >= 6.103515625e-05f) {  // 2^-14: normal E5M2 range
+    const uint32_t b = __float_as_uint(a), e = b & 0x7F800000u;
+    lo = __uint_as_float(b & 0xFFE00000u);          // keep two mantissa bits
+    ulp = __uint_as_float(e - (2u << 23));           // 2^(e-2)
+    inv = __uint_as_float((256u << 23) - e);         // 2^(2-e)
+  } else {
+    lo = floorf(a * 65536.0f) * 1.52587890625e-05f;  // multiples of 2^-16
+    ulp = 1.52587890625e-05f;
+    inv = 65536.0f;
+  }
+  const float p = (a - lo) * inv;
+  const float u = (float)(word >> 8) * 5.9604644775390625e-08f;  // 2^-24
+  const float m = __builtin_copysignf(u < p ? lo + ulp : lo, y);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(m, 0.0f, 0, false) & 0xFFu;
+}
+
+// Four scaled values (elements i .. i+3) to four stochastic E5M2 codes.
+__device__ __forceinline__ uint32_t e5m2_sr4(float a, float b, float c, float d, SrSeed sd, size_t i) {
+  const uint4 w = sr_words(sd, i);
+  return e5m2_sr_code(a, w.x) | (e5m2_sr_code(b, w.y) << 8) | (e5m2_sr_code(c, w.z) << 16) |
+         (e5m2_sr_code(d, w.w) << 24);
+}
+
+// Cast a whole vector whose first element has flat index `elem`: nearest-even
+// (SR = false, vec_cast_checked) or stochastic E5M2 (SR = true).
+template <int XT, int FMT, bool SR>
+__device__ __forceinline__ void cast_vec(const uint4& v, float r, uint32_t raw, uint32_t* out, SrSeed sd,
+                                         size_t elem) {
+  if constexpr (!SR) {
+    vec_cast_checked<XT, FMT>(v, r, raw, out);
+  } else {
+    static_assert(FMT == kE5M2, "stochastic rounding produces E5M2");
+#pragma unroll
+    for (int d = 0; d < VecTraits<XT>::kElems / 4; ++d)
+      out[d] = e5m2_sr4(vec_elem<XT>(v, 4 * d) * r, vec_elem<XT>(v, 4 * d + 1) * r, vec_elem<XT>(v, 4 * d + 2) * r,
+                        vec_elem<XT>(v, 4 * d + 3) * r, sd, elem + 4 * d);
+  }
+}
+
 // ---- code stores -----------------------------------------------------------------
 
 typedef unsigned int hq_u2v __attribute__((ext_vector_type(2)));

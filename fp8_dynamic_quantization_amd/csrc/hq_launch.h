@@ -22,15 +22,16 @@ constexpr int kColChunkRows = 128;        // rows per partial in the per-column 
 int tensor_partial_blocks(size_t nvec);   // partials written by the per-tensor passes
 int col_chunks(int rows);                 // partial rows of the per-column pass
 
+// `sr`: stochastic rounding to E5M2 (fmt must be E5M2) with hash key `seed`.
 hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
-                             float* amax, hipStream_t st);
+                             float* amax, bool sr, uint64_t seed, hipStream_t st);
 hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
-                               float* amax, void* ws, hipStream_t st);
+                               float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st);
 hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
-                             float* amax, void* ws, hipStream_t st);
+                             float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st);
 hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
                                 float* amax, float* state, int len, int idx, int margin, int32_t* flag, void* ws,
-                                hipStream_t st);
+                                bool sr, uint64_t seed, hipStream_t st);
 // Per-tensor codes of a row-major [rows, cols] tensor in up to four layouts
 // (null pointers are skipped): row-major, transposed [cols, rows], and the
 // pre-shuffled weight layout of either (N = rows, K = cols, or N = cols,

@@ -38,10 +38,10 @@ constexpr uint32_t kNonfiniteBit = 0x80000000u;
 
 // NV > 0: each thread keeps up to NV vectors of the row in registers.
 // NV == 0: the row is streamed twice (first pass for amax, second for the cast).
-template <int XT, int FMT, int NV, int BLOCK>
+template <int XT, int FMT, int NV, int BLOCK, bool SR>
 __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
     const uint4* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
-    float* __restrict__ amax_out, int vpr) {
+    float* __restrict__ amax_out, int vpr, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   __shared__ uint32_t red[BLOCK / 64];
   const size_t row = blockIdx.x;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
       const int i = threadIdx.x + j * BLOCK;
       if (i < vpr) {
         uint32_t w[E / 4];
-        vec_cast_checked<XT, FMT>(v[j], r, raw[j], w);
+        cast_vec<XT, FMT, SR>(v[j], r, raw[j], w, sd, (row * vpr + i) * E);
         store_codes<E>(qr + (size_t)i * E, w);
       }
     }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
     for (int i = threadIdx.x; i < vpr; i += BLOCK) {
       const uint4 vv = xr[i];
       uint32_t w[E / 4];
-      vec_cast_checked<XT, FMT>(vv, r, vec_absmax_raw<XT>(vv), w);
+      cast_vec<XT, FMT, SR>(vv, r, vec_absmax_raw<XT>(vv), w, sd, (row * vpr + i) * E);
       store_codes<E>(qr + (size_t)i * E, w);
     }
   }
@@ -112,10 +112,10 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
 constexpr int kRowsPerBlock = 4;
 constexpr int kRowWavesPerCU = 12;  // measured best for 4096 x 4096 bf16 (9.2 vs 9.6 us at 16)
 
-template <int XT, int FMT, int NV>
+template <int XT, int FMT, int NV, bool SR>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
     const uint4* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
-    float* __restrict__ amax_out, int rows, int vpr) {
+    float* __restrict__ amax_out, int rows, int vpr, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   const int lane = threadIdx.x & 63;
   const int W = gridDim.x * kRowsPerBlock;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
       const int i = lane + 64 * j;
       if (i < vpr) {
         uint32_t w[E / 4];
-        vec_cast_checked<XT, FMT>(cur[j], r, raw[j], w);
+        cast_vec<XT, FMT, SR>(cur[j], r, raw[j], w, sd, ((size_t)row * vpr + i) * E);
         store_codes<E>(qr + (size_t)i * E, w);
       }
     }
@@ -169,27 +169,27 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
   }
 }
 
-template <int XT, int FMT>
+template <int XT, int FMT, bool SR>
 static hipError_t launch_rows_t(const void* x, int rows, int vpr, uint8_t* q, float* scale,
-                                float* amax, hipStream_t st) {
+                                float* amax, SrSeed sd, hipStream_t st) {
   const uint4* xv = static_cast<const uint4*>(x);
   const dim3 grid(rows);
   const int wblocks = min((rows + kRowsPerBlock - 1) / kRowsPerBlock, kNumCUs * kRowWavesPerCU / kRowsPerBlock);
   const dim3 wgrid(wblocks), wblock(64 * kRowsPerBlock);
   if (vpr <= 64) {
-    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 1>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 1, SR>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr, sd);
   } else if (vpr <= 128) {
-    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 2>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 2, SR>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr, sd);
   } else if (vpr <= 256) {
-    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 4>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 4, SR>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr, sd);
   } else if (vpr <= 512) {
-    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 8>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr);
+    hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 8, SR>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr, sd);
   } else if (vpr <= 1024) {
-    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 4, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 4, kBlock, SR>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr, sd);
   } else if (vpr <= 2048) {
-    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 8, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 8, kBlock, SR>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr, sd);
   } else {
-    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 0, kBlock>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr);
+    hipLaunchKernelGGL((quant_rows_kernel<XT, FMT, 0, kBlock, SR>), grid, dim3(kBlock), 0, st, xv, q, scale, amax, vpr, sd);
   }
   return hipGetLastError();
 }
@@ -238,11 +238,11 @@ __device__ __forceinline__ uint32_t fold_partials(const uint32_t* __restrict__ p
   return m;
 }
 
-template <int XT, int FMT>
+template <int XT, int FMT, bool SR>
 __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __restrict__ x, size_t nvec,
                                                               const uint32_t* __restrict__ partial, int npart,
                                                               uint8_t* __restrict__ q, float* __restrict__ scale,
-                                                              float* __restrict__ amax_out) {
+                                                              float* __restrict__ amax_out, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   __shared__ uint32_t red[kBlock / 64];
   bool nonfinite;
@@ -264,7 +264,8 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
       const size_t i = base + u * kBlock;
       if (i < nvec) {
         uint32_t w[E / 4];
-        if (nonfinite) vec_cast<XT, FMT>(v[u], r, true, w);
+        if constexpr (SR) cast_vec<XT, FMT, true>(v[u], r, 0u, w, sd, i * E);
+        else if (nonfinite) vec_cast<XT, FMT>(v[u], r, true, w);
         else vec_cast<XT, FMT>(v[u], r, false, w);
         store_codes<E>(q + i * E, w);
       }
@@ -330,11 +331,11 @@ __global__ __launch_bounds__(kBlock) void colmax_partials_kernel(const uint4* __
   }
 }
 
-template <int XT, int FMT>
+template <int XT, int FMT, bool SR>
 __global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restrict__ x, int rows, int vpr,
                                                             const uint32_t* __restrict__ partial, int nchunk,
                                                             uint8_t* __restrict__ q, float* __restrict__ scale,
-                                                            float* __restrict__ amax_out) {
+                                                            float* __restrict__ amax_out, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   __shared__ float rcp[kColVecs * E];
   __shared__ uint32_t flags[kColVecs * E];
@@ -405,8 +406,12 @@ __global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restr
       const float b = vec_elem<XT>(v[j], 4 * d + 1) * r[4 * d + 1];
       const float c = vec_elem<XT>(v[j], 4 * d + 2) * r[4 * d + 2];
       const float e = vec_elem<XT>(v[j], 4 * d + 3) * r[4 * d + 3];
-      w[d] = cvt4<FMT>(a, b, c, e);
-      if (patch) w[d] = patch_nan4(w[d], a, b, c, e);
+      if constexpr (SR) {
+        w[d] = e5m2_sr4(a, b, c, e, sd, ((size_t)row * vpr + vc) * E + 4 * d);
+      } else {
+        w[d] = cvt4<FMT>(a, b, c, e);
+        if (patch) w[d] = patch_nan4(w[d], a, b, c, e);
+      }
     }
     uint8_t* dst = q + ((size_t)row * vpr + vc) * E;
     store_codes<E>(dst, w);
@@ -510,12 +515,12 @@ __device__ void delayed_finish(uint32_t raw, uint32_t fin, float s_t, float* __r
   ring_fold<FMT, kBlock>(state, len, idx, margin, flag, amax, f != 0, red);
 }
 
-template <int XT, int FMT>
+template <int XT, int FMT, bool SR>
 __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __restrict__ x, size_t nvec,
                                                                uint8_t* __restrict__ q, float* __restrict__ scale_out,
                                                                float* __restrict__ amax_out, float* state, int len,
                                                                int idx, int margin, int32_t* flag,
-                                                               uint32_t* partial, uint32_t* arrivals) {
+                                                               uint32_t* partial, uint32_t* arrivals, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   __shared__ uint32_t red[kBlock / 64];
   const float s_t = state[len];
@@ -535,7 +540,7 @@ __global__ __launch_bounds__(kBlock) void quant_delayed_kernel(const uint4* __re
         raw = max(raw, m);
         fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
         uint32_t w[E / 4];
-        vec_cast_checked<XT, FMT>(v[u], r, m, w);
+        cast_vec<XT, FMT, SR>(v[u], r, m, w, sd, i * E);
         store_codes<E>(q + i * E, w);
       }
     }
@@ -670,65 +675,82 @@ int col_chunks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
 #define HQ_DISPATCH_XT_FMT(XT, FMT, CALL)                 \
   do {                                                    \
-    if ((XT) == kBF16 && (FMT) == kE4M3) { CALL(kBF16, kE4M3); } \
-    else if ((XT) == kBF16) { CALL(kBF16, kE5M2); }       \
-    else if ((FMT) == kE4M3) { CALL(kF32, kE4M3); }       \
-    else { CALL(kF32, kE5M2); }                           \
+    if ((XT) == kBF16 && (FMT) == kE4M3) { CALL(kBF16, kE4M3, false); } \
+    else if ((XT) == kBF16) { CALL(kBF16, kE5M2, false); }       \
+    else if ((FMT) == kE4M3) { CALL(kF32, kE4M3, false); }       \
+    else { CALL(kF32, kE5M2, false); }                           \
   } while (0)
 
+// As above, plus the stochastic-rounding (E5M2 only) instances when `sr`.
+#define HQ_DISPATCH_XT_FMT_SR(XT, FMT, SRF, CALL)                     \
+  do {                                                                \
+    if (SRF) {                                                        \
+      if ((XT) == kBF16) { CALL(kBF16, kE5M2, true); }                \
+      else { CALL(kF32, kE5M2, true); }                               \
+    } else {                                                          \
+      HQ_DISPATCH_XT_FMT(XT, FMT, CALL);                              \
+    }                                                                 \
+  } while (0)
+
+static SrSeed sr_seed(uint64_t seed) { return SrSeed{(uint32_t)seed, (uint32_t)(seed >> 32)}; }
+
 hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
-                             float* amax, hipStream_t st) {
+                             float* amax, bool sr, uint64_t seed, hipStream_t st) {
   const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
-#define CALL(A, B) return launch_rows_t<A, B>(x, rows, vpr, q, scale, amax, st)
-  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+  const SrSeed sd = sr_seed(seed);
+#define CALL(A, B, S) return launch_rows_t<A, B, S>(x, rows, vpr, q, scale, amax, sd, st)
+  HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
 }
 
 hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
-                               float* amax, void* ws, hipStream_t st) {
+                               float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st) {
   const size_t nvec = xt == kBF16 ? numel / 8 : numel / 4;
   const int nb = tensor_partial_blocks(nvec);
   uint32_t* partial = static_cast<uint32_t*>(ws);
   const uint4* xv = static_cast<const uint4*>(x);
+  const SrSeed sd = sr_seed(seed);
   size_t qb = (nvec + kBlock * kUnroll - 1) / (kBlock * kUnroll);
   if (qb > 2048) qb = 2048;
   if (qb < 1) qb = 1;
-#define CALL(A, B)                                                                                    \
-  hipLaunchKernelGGL((amax_partials_kernel<A>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, partial);     \
-  hipLaunchKernelGGL((quant_tensor_kernel<A, B>), dim3((unsigned)qb), dim3(kBlock), 0, st, xv, nvec, \
-                     (const uint32_t*)partial, nb, q, scale, amax);                                   \
+#define CALL(A, B, S)                                                                                    \
+  hipLaunchKernelGGL((amax_partials_kernel<A>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, partial);        \
+  hipLaunchKernelGGL((quant_tensor_kernel<A, B, S>), dim3((unsigned)qb), dim3(kBlock), 0, st, xv, nvec, \
+                     (const uint32_t*)partial, nb, q, scale, amax, sd);                                  \
   return hipGetLastError()
-  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+  HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
 }
 
 hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
-                             float* amax, void* ws, hipStream_t st) {
+                             float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st) {
   const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
   const dim3 grid((vpr + kColVecs - 1) / kColVecs, col_chunks(rows));
   uint32_t* partial = static_cast<uint32_t*>(ws);
   const uint4* xv = static_cast<const uint4*>(x);
-#define CALL(A, B)                                                                                  \
+  const SrSeed sd = sr_seed(seed);
+#define CALL(A, B, S)                                                                               \
   hipLaunchKernelGGL((colmax_partials_kernel<A>), grid, dim3(kBlock), 0, st, xv, rows, vpr, partial); \
-  hipLaunchKernelGGL((quant_cols_kernel<A, B>), grid, dim3(kBlock), 0, st, xv, rows, vpr,           \
-                     (const uint32_t*)partial, (int)grid.y, q, scale, amax);                        \
+  hipLaunchKernelGGL((quant_cols_kernel<A, B, S>), grid, dim3(kBlock), 0, st, xv, rows, vpr,        \
+                     (const uint32_t*)partial, (int)grid.y, q, scale, amax, sd);                    \
   return hipGetLastError()
-  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+  HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
 }
 
 hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
                                 float* amax, float* state, int len, int idx, int margin, int32_t* flag, void* ws,
-                                hipStream_t st) {
+                                bool sr, uint64_t seed, hipStream_t st) {
   const size_t nvec = xt == kBF16 ? numel / 8 : numel / 4;
   const int nb = tensor_partial_blocks(nvec);
   uint32_t* partial = static_cast<uint32_t*>(ws);
   const uint4* xv = static_cast<const uint4*>(x);
-#define CALL(A, B)                                                                                  \
-  hipLaunchKernelGGL((quant_delayed_kernel<A, B>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, q, scale, \
-                     amax, state, len, idx, margin, flag, partial, partial + kMaxTensorPartials);    \
+  const SrSeed sd = sr_seed(seed);
+#define CALL(A, B, S)                                                                                  \
+  hipLaunchKernelGGL((quant_delayed_kernel<A, B, S>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, q, scale, \
+                     amax, state, len, idx, margin, flag, partial, partial + kMaxTensorPartials, sd);    \
   return hipGetLastError()
-  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+  HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
 }
 
@@ -750,7 +772,7 @@ hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int f
     else
       hipLaunchKernelGGL((amax_partials_kernel<kF32>), dim3(ndyn), dim3(kBlock), 0, st, xv, nvec, partial);
   }
-#define CALL(A, B)                                                                                           \
+#define CALL(A, B, S_UNUSED)                                                                                  \
   do {                                                                                                       \
     if (mode == kScaleGiven)                                                                                 \
       hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleGiven>), grid, block, 0, st, xv, rows, cols, o,    \

@@ -128,6 +128,25 @@ hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* hq_quantize_fp8 to E5M2 with stochastic rounding (hip-quant README,
+ * "Stochastic E5M2 Backward Gradients": each value rounds to one of the two
+ * adjacent E5M2 values, up with probability proportional to its distance from
+ * the lower one, drawn from a stateless hash of (seed, element index), so the
+ * result is reproducible). Scales, granularities, the ring and every argument
+ * rule are those of hq_quantize_fp8 with fmt = HQ_E5M2; only the cast of
+ * y = fl32(x * r) differs:
+ *   u = (w >> 8) * 2^-24, w = word i % 4 of Philox-4x32-10 (Salmon et al.,
+ *       SC 2011) with counter (i/4 low 32 bits, i/4 high 32 bits, 0, 0) and
+ *       key (seed low, seed high), i = row-major flat index of the element
+ *   lo <= |y| < hi adjacent E5M2 magnitudes; the code's magnitude is hi when
+ *       u < (|y| - lo) / (hi - lo), else lo; the sign of y is kept
+ *   |y| >= 57344 or Inf saturates to +-57344, NaN gives 0x7F. */
+hq_status hq_quantize_fp8_stochastic(const void* x, int xt, int64_t rows, int64_t cols, int gran,
+                                     uint64_t seed, uint8_t* q, float* scale_out,
+                                     float* amax_out, const hq_ring* ring,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Per-tensor FP8 quantization of a row-major [rows, cols] tensor written, in
  * one pass over x, to any of four layouts (the fused quantize-plus-transpose
  * of the hip-quant README, "Runtime codebooks and GPU execution features").

@@ -147,6 +147,24 @@ def test_quantize_valid_call_reaches_device_gate(hq):
     assert "gfx950" in hq.hq_last_error() or "device" in hq.hq_last_error()
 
 
+def test_stochastic_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    lib = hq.load()
+
+    def call(gran=1, cols=128, ring=None, q=fake(1), ws=fake(4), wsb=1 << 20):
+        return lib.hq_quantize_fp8_stochastic(fake(0), 1, 64, cols, gran, 2 ** 63 + 5, q, fake(2), None, ring, ws,
+                                              wsb, None)
+    assert call(gran=4) == E
+    assert call(cols=24) == E
+    assert call(q=fake(0, 16)) == E                      # q overlaps x
+    r = hq.hq_ring(BASE + 5 * (1 << 32), 16, 0, 0, None)
+    assert call(gran=1, ring=ctypes.byref(r)) == E       # a ring needs per-tensor
+    assert call(gran=2, wsb=4) == E                      # per-channel workspace too small
+    if not _gpu_visible():
+        assert call() == hq.HQ_ERR_UNSUPPORTED_DEVICE
+        assert call(gran=0, ring=ctypes.byref(r)) == hq.HQ_ERR_UNSUPPORTED_DEVICE
+
+
 def _layouts(hq, x=fake(0), xt=1, rows=64, cols=128, fmt=0, scale_in=None, ring=None, q=fake(1), q_t=None,
              q_pre=None, q_t_pre=None, s=fake(2), a=None, ws=fake(4), wsb=1 << 20):
     return hq.load().hq_quantize_fp8_layouts(x, xt, rows, cols, fmt, scale_in, ring, q, q_t, q_pre, q_t_pre, s, a,
