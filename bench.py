@@ -252,6 +252,32 @@ def other_workloads(torch, hq, lib, reps):
                           "gbs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg}
     del gsets, gw, pre
 
+    # GEMM epilogue variants on the PTPC 4096^3 operands: bf16 bias, and FP8 E4M3 output with an output scale
+    x, w = workloads.ptpc_square(1)
+    gx, gxs, _ = hq.hq_quantize_fp8(torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16), E4M3,
+                                    hq.HQ_PER_TOKEN)
+    gw, gws, _ = hq.hq_quantize_fp8(torch.from_numpy(w.view("int16")).cuda().view(torch.bfloat16), E4M3,
+                                    hq.HQ_PER_TOKEN)
+    pre = hq.hq_preshuffle_weight(gw)
+    esets = [(gx.clone(), pre.clone()) for _ in range(4)]
+    bias = torch.randn(N, device="cuda").to(torch.bfloat16)
+    osc = torch.full((1,), 0.05, dtype=torch.float32, device="cuda")
+    ep_res = {}
+    for name, ep, obytes in (("bias_bf16_out_bf16", hq.hq_epilogue(bias.data_ptr(), hq.HQ_BIAS_BF16, None, None, 0), 2),
+                             ("out_e4m3", hq.hq_epilogue(None, 0, None, osc.data_ptr(), E4M3), 1)):
+        outs = [torch.empty(M * N * obytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+
+        def elaunch(i, h, ep=ep, outs=outs):
+            a_, p_ = esets[i % 4]
+            st = lib.hq_gemm_a8w8_epilogue(P(a_.data_ptr()), E4M3, P(p_.data_ptr()), E4M3, P(gxs.data_ptr()), M,
+                                           P(gws.data_ptr()), N, M, N, K, ctypes.byref(ep),
+                                           P(outs[i % 4].data_ptr()), None, 0, h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, elaunch, 8)
+        ep_res[name] = {"us": round(ms * 1e3, 3), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+    res["gemm_epilogue_ptpc4096"] = ep_res
+    del esets, gx, gw, pre
+
     # quantize of the PTPC X [4096, 4096] bf16 at the other two granularities
     x, _ = workloads.ptpc_square(1)
     xs_ = [torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16) for _ in range(8)]
@@ -317,6 +343,68 @@ def training_linear_timings(torch, hq, lib, copies=12):
                                          "us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
                                          "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del srcs, qs, rings
+    # Backward operands in one pass each (hq_quantize_fp8_layouts): G (E5M2, its ring) row-major for dgrad and
+    # transposed for wgrad; W and X (E5M2, their forward scales) straight into the pre-shuffled transposed
+    # layouts the two GEMMs take. Algorithmic bytes: input + one byte per code written.
+    sw = torch.full((1,), 0.02 * 4.5 / 448.0, dtype=torch.float32, device="cuda")
+    sx = torch.full((1,), 4.5 / 448.0, dtype=torch.float32, device="cuda")
+    for name, t, kw, nbytes in (
+            ("g_e5m2_ring_q_and_qt", dev[2], dict(q=True, q_t=True), 2),
+            ("w_e5m2_given_qt_pre", dev[1], dict(q_t_pre=True), 1),
+            ("x_e5m2_given_qt_pre", dev[0], dict(q_t_pre=True), 1)):
+        rows, cols = t.shape
+        srcs = [t.clone() for _ in range(copies)]
+        outs = [hq.hq_quantize_fp8_layouts(srcs[i], E5M2, scale_in=None if name.startswith("g") else
+                                           (sw if name.startswith("w") else sx),
+                                           ring=hq.Ring(16) if name.startswith("g") else None, **kw)
+                for i in range(copies)]
+        rings = [hq.Ring(16) for _ in range(copies)] if name.startswith("g") else None
+        ring_structs = [r.c_struct(0) for r in rings] if rings else None
+        wsb = int(lib.hq_quantize_workspace_bytes(TEN, rows, cols))
+        wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        so = torch.empty(1, dtype=torch.float32, device="cuda")
+
+        def llaunch(i, h, srcs=srcs, outs=outs, rows=rows, cols=cols, name=name, so=so, wsp=wsp, wsb=wsb,
+                    ring_structs=ring_structs):
+            o = outs[i % copies]
+            given = None if name.startswith("g") else (sw if name.startswith("w") else sx)
+            st = lib.hq_quantize_fp8_layouts(P(srcs[i % copies].data_ptr()), BF16, rows, cols, E5M2,
+                                             P(given.data_ptr()) if given is not None else None,
+                                             ctypes.byref(ring_structs[i % copies]) if ring_structs else None,
+                                             P(o["q"].data_ptr()) if "q" in o else None,
+                                             P(o["q_t"].data_ptr()) if "q_t" in o else None, None,
+                                             P(o["q_t_pre"].data_ptr()) if "q_t_pre" in o else None,
+                                             P(so.data_ptr()), None, P(wsp.data_ptr()) if given is None else None,
+                                             wsb if given is None else 0, h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, llaunch, 2 * copies)
+        alg = rows * cols * (2 + nbytes)
+        out[f"layouts_{name}"] = {"shape": f"[{rows},{cols}] bf16", "us": round(ms * 1e3, 3),
+                                  "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del srcs, outs
+    # G with stochastic rounding and its ring (hq_quantize_fp8_stochastic)
+    rows, cols = dev[2].shape
+    srcs = [dev[2].clone() for _ in range(copies)]
+    qs = [torch.empty((rows, cols), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    rings = [hq.Ring(16) for _ in range(copies)]
+    ring_structs = [r.c_struct(0) for r in rings]
+    wsb = int(lib.hq_quantize_workspace_bytes(TEN, rows, cols))
+    wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    so = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def slaunch(i, h):
+        st = lib.hq_quantize_fp8_stochastic(P(srcs[i % copies].data_ptr()), BF16, rows, cols, TEN, 1234 + i,
+                                            P(qs[i % copies].data_ptr()), P(so.data_ptr()), None,
+                                            ctypes.byref(ring_structs[i % copies]), P(wsp.data_ptr()), wsb, h)
+        assert st == 0, hq.hq_last_error()
+    ms = time_graph(torch, slaunch, 2 * copies)
+    alg = rows * cols * 3
+    out["quant_g_delayed_stochastic"] = {"shape": f"[{rows},{cols}] bf16 -> E5M2 (stochastic)",
+                                         "us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                                         "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del srcs, qs, rings
+
     # GEMM operands (made once, untimed): E4M3 X, W for the forward; E5M2 G, W^T, G^T, X^T for the backward
     def quant(t, fmt):
         return hq.hq_quantize_fp8(t, fmt, TEN)
@@ -428,7 +516,24 @@ def write_traffic(name, kernel_substr, fetch_dir, write_dir, copy_fetch_dir, cop
     return out
 
 
+def trace_window(directory, kernel_substr, skip, count):
+    """Mean / median duration (us) of dispatches skip .. skip+count-1, in
+    dispatch order, of the kernels whose name contains `kernel_substr`, from a
+    --kernel-trace run (selects one timing phase of this script)."""
+    rows = [r for r in _csv_rows(directory, "kernel_trace.csv") if kernel_substr in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    sel = rows[skip:skip + count]
+    if len(sel) < count:
+        raise SystemExit(f"only {len(rows)} dispatches of {kernel_substr!r}")
+    d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel)
+    return {"kernel": kernel_substr, "dispatches": f"{skip}..{skip + count - 1} of {len(rows)}",
+            "mean_us": round(sum(d) / len(d), 3), "median_us": round(d[len(d) // 2], 3)}
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-window":
+        print(json.dumps(trace_window(sys.argv[2], sys.argv[3], int(sys.argv[4]), int(sys.argv[5]))))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         print(summarize(sys.argv[2]))
         return
@@ -556,6 +661,10 @@ def main():
             "traffic": traffic_from_profile("gemm_ptpc4096"),
         },
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kms.items()},
+        "kernel_timing": {"method": "HIP graph of launches over the rotating sets on torch's current stream, "
+                                    "HIP events around the timed replays",
+                          "launches_per_replay": 2 * args.rotate, "untimed_replays": 1, "timed_replays": 5,
+                          "step_loop_launches_per_kernel": args.warmup + args.steps},
         "quantize": {
             "kernel": "per-token quantize of X (hq_quantize_fp8)",
             "bound": "hbm",
