@@ -17,7 +17,8 @@ from ._lib import (HQ_BF16, HQ_BIAS_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANN
 
 __all__ = [
     "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
-    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_stochastic", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
+    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_stochastic", "hq_quantize_fp8_blockwise",
+    "hq_gemm_a8w8_blockscaled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_last_error",
 ]
@@ -134,6 +135,45 @@ def hq_quantize_fp8_stochastic(x: torch.Tensor, gran: int = HQ_PER_TOKEN, seed: 
                                         _stream(dev, stream))
     check(st)
     return q, scale_out, amax_out
+
+
+def hq_quantize_fp8_blockwise(x: torch.Tensor, fmt: int = HQ_E4M3, block_size: int = 32, *, stochastic: bool = False,
+                              seed: int = 0, q=None, scales=None, amax_out=None, stream=None):
+    """Block-wise quantization: returns (q uint8 [rows, cols], scales fp32
+    [rows, ceil(cols / block_size)], amax fp32 of the same shape)."""
+    if x.dtype not in _XT:
+        raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    x = x.contiguous()
+    rows, cols = x.shape
+    nb = -(-cols // int(block_size))
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, nb), dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty((rows, nb), dtype=torch.float32, device=dev)
+    check(load().hq_quantize_fp8_blockwise(_ptr(x), _XT[x.dtype], rows, cols, fmt, int(block_size), int(bool(stochastic)),
+                                           int(seed) & (2 ** 64 - 1), _ptr(q), _ptr(scales), _ptr(amax_out),
+                                           _stream(dev, stream)))
+    return q, scales, amax_out
+
+
+def hq_gemm_a8w8_blockscaled(xq: torch.Tensor, xf: int, wq: torch.Tensor, wf: int, x_scales: torch.Tensor,
+                             w_scales: torch.Tensor, block_size: int = 32, out=None, stream=None) -> torch.Tensor:
+    """Block-scaled GEMM of row-major codes xq [m, k], wq [n, k] with block
+    scales [m, nb], [n, nb]; returns bf16 [m, n]."""
+    xq, wq = xq.contiguous(), wq.contiguous()
+    x_scales, w_scales = x_scales.contiguous(), w_scales.contiguous()
+    m, k = xq.shape
+    n = wq.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    check(load().hq_gemm_a8w8_blockscaled(_ptr(xq), xf, _ptr(wq), wf, _ptr(x_scales), _ptr(w_scales), int(block_size),
+                                          m, n, k, _ptr(out), _stream(xq.device, stream)))
+    return out
 
 
 def hq_quantize_fp8_layouts(x: torch.Tensor, fmt: int = HQ_E4M3, *, scale_in: torch.Tensor | None = None,

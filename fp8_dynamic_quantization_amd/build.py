@@ -21,12 +21,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhq.so")
 
-SOURCES = ["quantize.hip", "gemm.hip", "hq_api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "blockscaled.hip", "hq_api.cpp"]
 
 # Per-source flags. The GEMM keeps its MFMA accumulators in VGPRs and the
 # operand fragments in AGPRs: with 256 accumulator registers per wavefront the
 # default AGPR-accumulator allocation spills to scratch, this form does not.
-EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "blockscaled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

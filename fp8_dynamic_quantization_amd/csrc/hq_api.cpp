@@ -298,6 +298,41 @@ hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t c
                   "hq_quantize_fp8_layouts");
 }
 
+hq_status hq_quantize_fp8_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int fmt, int block_size,
+                                    int stochastic, uint64_t seed, uint8_t* q, float* scales, float* amax_out,
+                                    hipStream_t stream) {
+  if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
+  if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
+  if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "block_size must be 16, 32, 64 or 128, got %d", block_size);
+  if (stochastic && fmt != HQ_E5M2) return fail(HQ_ERR_INVALID_ARGUMENT, "stochastic rounding produces E5M2");
+  if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
+  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
+  if (rows == 0) return ok();
+  if (!x || !q || !scales) return fail(HQ_ERR_INVALID_ARGUMENT, "x, q and scales must be non-NULL");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "x and q must be 16-byte aligned");
+  if (!aligned(scales, 4) || (amax_out && !aligned(amax_out, 4)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scales and amax_out must be 4-byte aligned");
+  const size_t numel = (size_t)rows * (size_t)cols;
+  const size_t nscale = (size_t)rows * (size_t)((cols + block_size - 1) / block_size);
+  const Range rg[] = {
+      {x, numel * (xt == HQ_BF16 ? 2 : 4), "x"},
+      {q, numel, "q"},
+      {scales, nscale * 4, "scales"},
+      {amax_out, amax_out ? nscale * 4 : 0, "amax_out"},
+  };
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 4, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  return launched(hq::launch_quant_blocks(x, xt, (int)rows, (int)cols, fmt, block_size, stochastic != 0, seed, q,
+                                          scales, amax_out, stream),
+                  "hq_quantize_fp8_blockwise");
+}
+
 hq_status hq_scale_ring_update(const hq_ring* ring, const float* amax, int fmt, hipStream_t stream) {
   if (!ring) return fail(HQ_ERR_INVALID_ARGUMENT, "ring is NULL");
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
@@ -464,6 +499,37 @@ hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
                  w_scale_count != num_experts};
   (void)hipGetLastError();
   return launched(hq::launch_grouped_gemm(g, group_offsets, num_experts, xf, wf, stream), "hq_grouped_gemm_a8w8");
+}
+
+hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq, int wf, const float* x_scales,
+                                   const float* w_scales, int block_size, int64_t m, int64_t n, int64_t k,
+                                   uint16_t* out, hipStream_t stream) {
+  hq_status st = check_gemm_common(xf, wf, m, n, k);
+  if (st != HQ_OK) return st;
+  if (block_size != 32 && block_size != 64 && block_size != 128)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "block_size must be 32, 64 or 128, got %d", block_size);
+  if (m == 0 || n == 0) return ok();
+  if (!xq || !wq || !x_scales || !w_scales || !out)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq, x_scales, w_scales and out must be non-NULL");
+  if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "xq and wq must be 16-byte aligned");
+  if (!aligned(out, 2) || !aligned(x_scales, 4) || !aligned(w_scales, 4))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "out must be 2-byte and the scales 4-byte aligned");
+  const int64_t nb = (k + block_size - 1) / block_size;
+  const Range rg[] = {
+      {out, (size_t)m * (size_t)n * 2, "out"},
+      {xq, (size_t)m * (size_t)k, "xq"},
+      {wq, (size_t)n * (size_t)k, "wq"},
+      {x_scales, (size_t)m * (size_t)nb * 4, "x_scales"},
+      {w_scales, (size_t)n * (size_t)nb * 4, "w_scales"},
+  };
+  const char* other = nullptr;
+  const char* a = find_overlap(rg, 5, &other);
+  if (a && strcmp(a, "out") == 0) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
+  st = check_device();
+  if (st != HQ_OK) return st;
+  hq::BlockGemmArgs g{xq, wq, x_scales, w_scales, out, (int)m, (int)n, (int)k, (int)nb};
+  (void)hipGetLastError();
+  return launched(hq::launch_gemm_blockscaled(g, xf, wf, block_size, stream), "hq_gemm_a8w8_blockscaled");
 }
 
 }  // extern "C"

@@ -92,6 +92,21 @@ SkinnyPlan skinny_plan(int m, int n, int k);
 size_t gemm_workspace_bytes(int m, int n, int k);
 hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_t workspace_bytes, hipStream_t st);
 
+// Block-wise quantization: scales [rows, ceil(cols / bs)], bs in {16, 32, 64, 128}.
+hipError_t launch_quant_blocks(const void* x, int xt, int rows, int cols, int fmt, int bs, bool sr, uint64_t seed,
+                               uint8_t* q, float* scale, float* amax, hipStream_t st);
+
+// Block-scaled GEMM on row-major codes: xs [m, nb], ws [n, nb], nb = ceil(k / bs), bs in {32, 64, 128}.
+struct BlockGemmArgs {
+  const uint8_t* xq;  // [m, k]
+  const uint8_t* wq;  // [n, k]
+  const float* xs;    // [m, nb]
+  const float* ws;    // [n, nb]
+  uint16_t* out;      // bf16 [m, n]
+  int m, n, k, nb;
+};
+hipError_t launch_gemm_blockscaled(const BlockGemmArgs& a, int xf, int wf, int bs, hipStream_t st);
+
 // Grouped form: rows [offsets[e], offsets[e+1]) use expert e's weight at
 // wq_pre + e * preshuffled_bytes(n, k) and scales w_scale + e * (per_col ? n : 1).
 hipError_t launch_grouped_gemm(const GemmArgs& a, const int32_t* offsets, int experts, int xf, int wf,

@@ -184,6 +184,46 @@ hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t c
                                   float* scale_out, float* amax_out,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Block-wise FP8 quantization (hip-quant README, "Block-wise FP8 Scaling"):
+ * FP8 codes plus one float32 dequant scale per block of block_size consecutive
+ * elements along each row, value ~= code * block_scale. Each block follows the
+ * rule of hq_quantize_fp8 (amax over its finite elements, s = max(amax / fmax,
+ * 2^-126), q = saturating RNE cast of fl32(x * fl32(1/s))); the last block of a
+ * row holds cols mod block_size elements when that is not zero. With
+ * `stochastic` != 0 the cast is the stochastic E5M2 of
+ * hq_quantize_fp8_stochastic (fmt must be HQ_E5M2; element index = row-major
+ * flat index) - the README's quantize_e5m2_blockwise_stochastic.
+ *   x         device, [rows, cols] of `xt`, row-major, 16-byte aligned
+ *   q         device, [rows, cols] uint8 codes, 16-byte aligned
+ *   scales    device, float32 [rows, ceil(cols / block_size)] row-major
+ *   amax_out  device, optional, float32 of the same shape: the block amax
+ * Requires block_size in {16, 32, 64, 128}, cols % 16 == 0, 1 <= rows,
+ * cols < 2^31, rows * cols < 2^40; no output may overlap an input. rows == 0
+ * returns HQ_OK without a launch. */
+hq_status hq_quantize_fp8_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int fmt,
+                                    int block_size, int stochastic, uint64_t seed,
+                                    uint8_t* q, float* scales, float* amax_out,
+                                    hipStream_t stream);
+
+/* Block-scaled FP8 GEMM (hip-quant README, "Block-scaled Linear ...": the
+ * pre-quantized path consumes FP8 bytes and both block-scale tensors):
+ *   out[m, n] = bf16( sum_b x_scales[m, b] * w_scales[n, b] *
+ *                     sum_{k in block b} dec(XQ[m, k]) * dec(WQ[n, k]) )
+ * Each block's partial sum (float32 MFMAs) is folded into the float32 result
+ * with one fused multiply-add by the float32 product of the two scales.
+ *   xq        device, uint8 [m, k] codes in format xf, row-major, 16-byte aligned
+ *   wq        device, uint8 [n, k] codes in format wf, row-major (not
+ *             pre-shuffled), 16-byte aligned
+ *   x_scales  device, float32 [m, ceil(k / block_size)]
+ *   w_scales  device, float32 [n, ceil(k / block_size)]
+ *   out       device, bf16 bits [m, n], caller-owned, must not overlap an input
+ * Requires block_size in {32, 64, 128}, k % 16 == 0, 16 <= k < 2^24. m == 0 or
+ * n == 0 returns HQ_OK without a launch. */
+hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq, int wf,
+                                   const float* x_scales, const float* w_scales, int block_size,
+                                   int64_t m, int64_t n, int64_t k, uint16_t* out,
+                                   hipStream_t stream);
+
 /* Fold one amax sample into a ring and publish the next scale (the delayed
  * update of hq_quantize_fp8, as its own launch). `amax` is a device float32
  * scalar; a NaN or Inf sample leaves the ring unchanged and sets the flag. */

@@ -353,3 +353,60 @@ def test_python_binding_rejects_bad_dtype(hq):
     import torch
     with pytest.raises(ValueError):
         hq.hq_quantize_fp8(torch.zeros(4, 16, dtype=torch.float16))
+
+
+def _blockwise(hq, x=fake(0), xt=1, rows=64, cols=128, fmt=0, bs=32, sr=0, q=fake(1), s=fake(2), a=fake(3)):
+    return hq.load().hq_quantize_fp8_blockwise(x, xt, rows, cols, fmt, bs, sr, 2 ** 64 - 1, q, s, a, None)
+
+
+def test_blockwise_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    for bs in (0, 8, 48, 256):
+        assert _blockwise(hq, bs=bs) == E
+    assert _blockwise(hq, sr=1, fmt=hq.HQ_E4M3) == E     # stochastic rounding produces E5M2
+    assert _blockwise(hq, xt=7) == E
+    assert _blockwise(hq, cols=40) == E
+    assert _blockwise(hq, s=ctypes.c_void_p(0)) == E
+    assert _blockwise(hq, x=fake(0, 8)) == E
+    assert _blockwise(hq, s=fake(2, 2)) == E
+    # scales are [64, 4] floats = 1 KiB: amax 1020 bytes after it overlaps
+    assert _blockwise(hq, a=fake(2, 1020)) == E
+    assert "overlaps" in hq.hq_last_error()
+    assert _blockwise(hq, rows=0, x=ctypes.c_void_p(0)) == hq.HQ_OK
+
+
+@no_gpu
+def test_blockwise_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    for bs in (16, 32, 64, 128):
+        assert _blockwise(hq, bs=bs, cols=144) == U
+    assert _blockwise(hq, sr=1, fmt=hq.HQ_E5M2, a=None) == U
+    assert _blockwise(hq, a=fake(2, 1024)) == U
+
+
+def _gemm_bs(hq, xf=0, wf=0, bs=32, m=64, n=128, k=256, out=fake(4), xs=fake(2), ws=fake(3), xq=fake(0)):
+    return hq.load().hq_gemm_a8w8_blockscaled(xq, xf, fake(1), wf, xs, ws, bs, m, n, k, out, None)
+
+
+def test_gemm_blockscaled_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    for bs in (16, 48, 256):
+        assert _gemm_bs(hq, bs=bs) == E
+    assert _gemm_bs(hq, xf=2) == E
+    assert _gemm_bs(hq, k=100) == E
+    assert _gemm_bs(hq, xs=ctypes.c_void_p(0)) == E
+    assert _gemm_bs(hq, xq=fake(0, 4)) == E
+    assert _gemm_bs(hq, out=fake(4, 1)) == E
+    assert _gemm_bs(hq, out=fake(3, 64)) == E           # out overlaps w_scales
+    assert "overlaps" in hq.hq_last_error()
+    assert _gemm_bs(hq, m=0, xq=ctypes.c_void_p(0)) == hq.HQ_OK
+
+
+@no_gpu
+def test_gemm_blockscaled_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    for bs in (32, 64, 128):
+        assert _gemm_bs(hq, bs=bs, k=272) == U
+    # the two inputs may share memory (same codes for X and W)
+    assert hq.load().hq_gemm_a8w8_blockscaled(fake(0), 0, fake(0), 0, fake(2), fake(2), 32, 64, 64, 256, fake(4),
+                                              None) == U
