@@ -11,18 +11,18 @@
 //
 // GEMM design. Per-block float32 scales cannot ride on the MFMA's hardware
 // block scales (those are powers of two), so every block's partial sum is
-// formed on its own: 16x16x32 FP8 MFMAs (one per 32 elements of K) start from
-// a zero accumulator, and one FMA per output element folds the partial into
-// the running sum with the scale product xs * ws. The rescale costs two VALU
-// operations per output element per block, which for BS = 32 is more issue
-// time than the MFMAs themselves: this GEMM is bound by that arithmetic, not
-// by HBM or the matrix cores.
+// formed on its own from a zero accumulator, and one FMA per output element
+// folds the partial into the running sum with the scale product xs * ws. The
+// rescale costs two VALU operations per output element per block, which for
+// BS = 32 is more issue time than the MFMAs themselves: that GEMM is bound by
+// this arithmetic, not by HBM or the matrix cores.
 #include "hq_device.h"
 #include "hq_launch.h"
 
 namespace hq {
 
 typedef float bv4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // block-wise quantization
@@ -115,21 +115,37 @@ hipError_t launch_quant_blocks(const void* x, int xt, int rows, int cols, int fm
 // ---------------------------------------------------------------------------
 // block-scaled GEMM
 // ---------------------------------------------------------------------------
+// A 128 x 128 output tile per workgroup, two workgroups per CU (2 x 76 KB of
+// LDS), so one wavefront's rescaling arithmetic runs while another's MFMAs
+// issue. Each wavefront owns 64 rows x 16*NJ columns as 4 x NJ MFMA tiles of
+// 16 x 16: NJ = 2 (8 wavefronts, at most 128 registers each) for blocks of 32,
+// whose folds dominate, and NJ = 4 (4 wavefronts, at most 256 registers) for
+// blocks of 64 and 128, where the larger tile halves the LDS reads per MFMA
+// (measured: 235 vs 258 us at BS = 32, 197 vs 220 and 140 vs 162 us at BS = 64
+// and 128, 4096^3, full-range codes). K moves in steps of 128 through
+// double-buffered LDS (one barrier per step): the codes and block scales of
+// step kb + 1 are loaded into registers while step kb computes.
+//
+// The weight is the MFMA's A operand and the activation its B operand, so an
+// output lane holds one row m and four consecutive columns n (8-byte stores).
+// Blocks of 128 take one 16x16x128 MFMA per tile (hardware block scales left
+// at 1); blocks of 32 and 64 take one or two 16x16x32 MFMAs.
 namespace bsg {
 constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kPitch = 136;  // LDS row pitch in bytes: 8 bytes of padding spread 16 rows over all banks
-constexpr int kStage = kBM * kPitch;
+template <int NJ>
+constexpr int threads() { return 64 * 2 * (8 / NJ); }
 }  // namespace bsg
 
-// 16x16x32 FP8 MFMA with the activation (format XF) as A and the weight (WF)
-// as B: lane l gives A row l%16 and B column l%16, each with the 8 k values
-// 8*(l/16) .. +7; the result lane l holds column l%16, rows 4*(l/16) .. +3.
+// 16x16x32 FP8 MFMA, weight (format WF) as A and activation (XF) as B: lane l
+// gives A row l%16 and B column l%16, each with the 8 k values 8*(l/16) .. +7;
+// the result lane l holds B column l%16 (output row m) and A rows
+// 4*(l/16) .. +3 (output columns n).
 template <int XF, int WF>
-__device__ __forceinline__ bv4f mfma32(long a, long b, bv4f c) {
-  if constexpr (XF == kE4M3 && WF == kE4M3) return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
-  else if constexpr (XF == kE4M3) return __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(a, b, c, 0, 0, 0);
-  else if constexpr (WF == kE4M3) return __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(a, b, c, 0, 0, 0);
-  else return __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(a, b, c, 0, 0, 0);
+__device__ __forceinline__ bv4f mfma32(long w, long x, bv4f c) {
+  if constexpr (WF == kE4M3 && XF == kE4M3) return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w, x, c, 0, 0, 0);
+  else if constexpr (WF == kE4M3) return __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(w, x, c, 0, 0, 0);
+  else if constexpr (XF == kE4M3) return __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(w, x, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf8_bf8(w, x, c, 0, 0, 0);
 }
 
 // Tile order as the plain GEMM: workgroup b on XCD b % 8 takes a contiguous
@@ -146,68 +162,87 @@ __device__ __forceinline__ void bs_tile_coords(int b, int tiles_m, int tiles_n, 
   *tn = r / gm;
 }
 
-template <int XF, int WF, int BS>
-__global__ __launch_bounds__(256) void gemm_blockscaled_kernel(BlockGemmArgs a, int tiles_m, int tiles_n) {
+template <int XF, int WF, int BS, int NJ>
+__global__ __launch_bounds__(bsg::threads<NJ>()) __attribute__((amdgpu_waves_per_eu(NJ == 2 ? 4 : 2))) void gemm_blockscaled_kernel(BlockGemmArgs a, int tiles_m, int tiles_n) {
   using namespace bsg;
-  constexpr int NBS = kBK / BS;  // scale blocks per K step
-  constexpr int SUB = BS / 32;   // 16x16x32 MFMAs per block
-  constexpr int NSC = (kBM * NBS + 255) / 256;  // scale loads per thread per operand
-  __shared__ __attribute__((aligned(16))) uint8_t sa[2][kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t sb[2][kStage];
-  __shared__ float sxs[2][kBM * NBS];
-  __shared__ float sws[2][kBN * NBS];
+  constexpr int NBS = kBK / BS;                // scale blocks per K step
+  constexpr int SUB = BS / 32;                 // 16x16x32 MFMAs per block (BS < 128)
+  constexpr int kPitch = BS == 128 ? 144 : 136;  // LDS row pitch: 16-byte rows for the 128-wide reads
+  constexpr int kStage = kBM * kPitch;
+  constexpr int kThreads = threads<NJ>();
+  constexpr int NP = kBM * kBK / 16 / kThreads;  // 16-byte pieces per thread per operand
+  constexpr int NSC = (kBM * NBS + kThreads - 1) / kThreads;  // scale loads per thread per operand
+  __shared__ __attribute__((aligned(16))) uint8_t sx[2][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t sw[2][kStage];
+  __shared__ __attribute__((aligned(16))) float sxs[2][NBS][kBM];
+  __shared__ __attribute__((aligned(16))) float sws[2][NBS][kBN];
   int tm, tn;
   bs_tile_coords(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;  // 2 x 2 wavefronts of 64 x 64
+  const int wm = wave & 1, wn = wave >> 1;  // 64-row half, 16*NJ-column slice
   const int K = a.k, nkb = (K + kBK - 1) / kBK;
 
-  // staging: piece p = tid + 256 v of an operand stage is row p / 8, 16-byte chunk p % 8
-  uint4 ra[4], rb[4];
+  // staging: piece p = tid + kThreads * v of an operand stage is row p / 8, 16-byte
+  // chunk p % 8. Rows past M or N only feed outputs that are never stored, so
+  // their loads read a clamped row and are not zeroed; only the K tail of the
+  // last step (K % 128 != 0) must read as zero codes, and scales past the last
+  // block as zero. No load sits behind a branch.
+  uint4 rx[NP], rw[NP];
   float rxs[NSC], rws[NSC];
   auto load = [&](int kb) {
+    const bool tail = kb + 1 == nkb && (K & (kBK - 1)) != 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int p = tid + 256 * v, row = p >> 3, kk = kb * kBK + (p & 7) * 16;
-      ra[v] = (m0 + row < a.m && kk < K) ? *reinterpret_cast<const uint4*>(a.xq + (size_t)(m0 + row) * K + kk)
-                                         : make_uint4(0u, 0u, 0u, 0u);
-      rb[v] = (n0 + row < a.n && kk < K) ? *reinterpret_cast<const uint4*>(a.wq + (size_t)(n0 + row) * K + kk)
-                                         : make_uint4(0u, 0u, 0u, 0u);
+    for (int v = 0; v < NP; ++v) {
+      const int p = tid + kThreads * v, row = p >> 3, kk = kb * kBK + (p & 7) * 16;
+      const int kc = min(kk, K - 16);
+      const int xr = min(m0 + row, a.m - 1), wr = min(n0 + row, a.n - 1);
+      rx[v] = *reinterpret_cast<const uint4*>(a.xq + (size_t)xr * K + kc);
+      rw[v] = *reinterpret_cast<const uint4*>(a.wq + (size_t)wr * K + kc);
+      if (tail && kk >= K) {
+        rx[v] = make_uint4(0u, 0u, 0u, 0u);
+        rw[v] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int e = 0; e < NSC; ++e) {
-      const int idx = tid + 256 * e, row = idx / NBS, gb = kb * NBS + idx % NBS;
-      const bool in = idx < kBM * NBS && gb < a.nb;
-      rxs[e] = in && m0 + row < a.m ? a.xs[(size_t)(m0 + row) * a.nb + gb] : 0.0f;
-      rws[e] = in && n0 + row < a.n ? a.ws[(size_t)(n0 + row) * a.nb + gb] : 0.0f;
+      const int idx = tid + kThreads * e, row = idx / NBS, gb = kb * NBS + idx % NBS;
+      if (kBM * NBS % kThreads == 0 || idx < kBM * NBS) {  // whole wavefronts
+        const int gc = min(gb, a.nb - 1);
+        const int xr = min(m0 + row, a.m - 1), wr = min(n0 + row, a.n - 1);
+        rxs[e] = a.xs[(size_t)xr * a.nb + gc];
+        rws[e] = a.ws[(size_t)wr * a.nb + gc];
+        if (tail && gb >= a.nb) rxs[e] = rws[e] = 0.0f;
+      }
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int p = tid + 256 * v, off = (p >> 3) * kPitch + (p & 7) * 16;
-      *reinterpret_cast<uint4*>(&sa[buf][off]) = ra[v];
-      *reinterpret_cast<uint4*>(&sb[buf][off]) = rb[v];
+    for (int v = 0; v < NP; ++v) {
+      const int p = tid + kThreads * v, off = (p >> 3) * kPitch + (p & 7) * 16;
+      *reinterpret_cast<uint4*>(&sx[buf][off]) = rx[v];
+      *reinterpret_cast<uint4*>(&sw[buf][off]) = rw[v];
     }
 #pragma unroll
     for (int e = 0; e < NSC; ++e) {
-      const int idx = tid + 256 * e;
+      const int idx = tid + kThreads * e;
       if (idx < kBM * NBS) {
-        sxs[buf][idx] = rxs[e];
-        sws[buf][idx] = rws[e];
+        sxs[buf][idx % NBS][idx / NBS] = rxs[e];
+        sws[buf][idx % NBS][idx / NBS] = rws[e];
       }
     }
   };
 
-  bv4f acc[4][4];
+  bv4f acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = bv4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = bv4f{0.f, 0.f, 0.f, 0.f};
 
-  const int arow = wr * 64 + (lane & 15), brow = wc * 64 + (lane & 15), kofs = 8 * (lane >> 4);
+  const int xrow = wm * 64 + (lane & 15);           // + 16 i
+  const int wrow = wn * 16 * NJ + (lane & 15);      // + 16 j
+  const int wcol = wn * 16 * NJ + 4 * (lane >> 4);  // + 16 j + r: the lane's output columns
   load(0);
   store(0);
   __syncthreads();
@@ -216,77 +251,112 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_kernel(BlockGemmArgs a, 
     if (kb + 1 < nkb) load(kb + 1);
 #pragma unroll
     for (int b = 0; b < NBS; ++b) {
-      float wsv[4];
+      bv4f t[4][NJ];
+      if constexpr (BS == 128) {
+        const int kofs = 32 * (lane >> 4);
+        v8i fw[NJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wsv[j] = sws[buf][(brow + j * 16) * NBS + b];
-      // the wavefront's 4 x 4 tiles in two halves of two row tiles, so only 8
-      // partial sums are live at a time
-#pragma unroll
-      for (int ih = 0; ih < 2; ++ih) {
-        float xsv[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            xsv[i][r] = sxs[buf][(wr * 64 + (2 * ih + i) * 16 + 4 * (lane >> 4) + r) * NBS + b];
-        bv4f t[2][4];
-#pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-          long fa[2], fb[4];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            fa[i] = *reinterpret_cast<const long*>(
-                &sa[buf][(arow + (2 * ih + i) * 16) * kPitch + b * BS + s * 32 + kofs]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            fb[j] = *reinterpret_cast<const long*>(&sb[buf][(brow + j * 16) * kPitch + b * BS + s * 32 + kofs]);
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              t[i][j] = mfma32<XF, WF>(fa[i], fb[j], s == 0 ? bv4f{0.f, 0.f, 0.f, 0.f} : t[i][j]);
+        for (int j = 0; j < NJ; ++j) {
+          const uint8_t* pw = &sw[buf][(wrow + 16 * j) * kPitch + kofs];
+          const uint4 lo = *reinterpret_cast<const uint4*>(pw), hi = *reinterpret_cast<const uint4*>(pw + 16);
+          fw[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const uint8_t* px = &sx[buf][(xrow + 16 * i) * kPitch + kofs];
+          const uint4 lo = *reinterpret_cast<const uint4*>(px), hi = *reinterpret_cast<const uint4*>(px + 16);
+          const v8i fx = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
+            t[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fw[j], fx, bv4f{0.f, 0.f, 0.f, 0.f}, WF, XF,
+                                                                       0, 0, 0, 0);
+        }
+      } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[2 * ih + i][j][r] = fmaf(t[i][j][r], xsv[i][r] * wsv[j], acc[2 * ih + i][j][r]);
+        for (int s = 0; s < SUB; ++s) {
+          const int kofs = b * BS + s * 32 + 8 * (lane >> 4);
+          long fw[NJ], fx[4];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) fw[j] = *reinterpret_cast<const long*>(&sw[buf][(wrow + 16 * j) * kPitch + kofs]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fx[i] = *reinterpret_cast<const long*>(&sx[buf][(xrow + 16 * i) * kPitch + kofs]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              t[i][j] = mfma32<XF, WF>(fw[j], fx[i], s == 0 ? bv4f{0.f, 0.f, 0.f, 0.f} : t[i][j]);
+        }
+      }
+      // fold the block's partials: acc += t * (xs[m] * ws[n])
+      bv4f wsv[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) wsv[j] = *reinterpret_cast<const bv4f*>(&sws[buf][b][wcol + 16 * j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xsv = sxs[buf][b][xrow + 16 * i];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(t[i][j][r], xsv * wsv[j][r], acc[i][j][r]);
+      }
+      // one block's partials live at a time: the empty asm makes this block's
+      // folds complete here (the other wavefronts on the SIMD overlap their
+      // MFMAs with them)
+      if constexpr (NBS > 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (kb + 1 < nkb) store(buf ^ 1);
     __syncthreads();
   }
 
+  // epilogue: four consecutive columns per lane, as one 8-byte store where the
+  // row's columns allow it
+  const bool vec = (a.n % 4 == 0) && (reinterpret_cast<uintptr_t>(a.out) % 8 == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + xrow + 16 * i;
+    if (row >= a.m) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wc * 64 + j * 16 + (lane & 15);
-      if (col >= a.n) continue;
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wcol + 16 * j;
+      uint16_t* o = a.out + (size_t)row * a.n + col;
+      if (vec && col + 3 < a.n) {
+        uint2 pk;
+        pk.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+        pk.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(o) = pk;
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wr * 64 + i * 16 + 4 * (lane >> 4) + r;
-        if (row < a.m) a.out[(size_t)row * a.n + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+        for (int r = 0; r < 4; ++r)
+          if (col + r < a.n) o[r] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
       }
     }
+  }
 }
 
 hipError_t launch_gemm_blockscaled(const BlockGemmArgs& a, int xf, int wf, int bs, hipStream_t st) {
   const int tiles_m = (a.m + bsg::kBM - 1) / bsg::kBM, tiles_n = (a.n + bsg::kBN - 1) / bsg::kBN;
-  const dim3 grid(tiles_m * tiles_n), block(256);
-#define HQ_BSG(X_, W_)                                                                                          \
-  do {                                                                                                         \
-    if (bs == 32) hipLaunchKernelGGL((gemm_blockscaled_kernel<X_, W_, 32>), grid, block, 0, st, a, tiles_m, tiles_n); \
-    else if (bs == 64) hipLaunchKernelGGL((gemm_blockscaled_kernel<X_, W_, 64>), grid, block, 0, st, a, tiles_m, tiles_n); \
-    else hipLaunchKernelGGL((gemm_blockscaled_kernel<X_, W_, 128>), grid, block, 0, st, a, tiles_m, tiles_n); \
+  const dim3 grid(tiles_m * tiles_n);
+#define HQ_BSG_ONE(X_, W_, BS_, NJ_)                                                                       \
+  hipLaunchKernelGGL((gemm_blockscaled_kernel<X_, W_, BS_, NJ_>), grid, dim3(bsg::threads<NJ_>()), 0, st, a, \
+                     tiles_m, tiles_n)
+#define HQ_BSG(X_, W_)                             \
+  do {                                             \
+    if (bs == 32) HQ_BSG_ONE(X_, W_, 32, 2);       \
+    else if (bs == 64) HQ_BSG_ONE(X_, W_, 64, 4);  \
+    else HQ_BSG_ONE(X_, W_, 128, 4);               \
   } while (0)
   if (xf == kE4M3 && wf == kE4M3) HQ_BSG(kE4M3, kE4M3);
   else if (xf == kE4M3) HQ_BSG(kE4M3, kE5M2);
   else if (wf == kE4M3) HQ_BSG(kE5M2, kE4M3);
   else HQ_BSG(kE5M2, kE5M2);
 #undef HQ_BSG
+#undef HQ_BSG_ONE
   return hipGetLastError();
 }
 
