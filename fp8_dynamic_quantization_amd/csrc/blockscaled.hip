@@ -28,6 +28,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // block-wise quantization
 // ---------------------------------------------------------------------------
 // One wavefront per row (rows w, w + W, ...); lane l holds vectors l + 64j.
+// A row is taken in chunks of U vectors per lane, and the next chunk (of this
+// row or of the wavefront's next row) is loaded before the current one is
+// processed, so every lane keeps up to 2U loads in flight.
 // A block of BS elements is G = BS / E consecutive lanes (E elements per
 // 16-byte vector), so its amax is a shuffle reduction over G lanes. Lanes past
 // the row end reload the row's last vector, which lies in the row's last
@@ -39,44 +42,60 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint4* __restri
                                                            int rows, int vpr, int nb, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   constexpr int G = BS / E;  // lanes per block
-  constexpr int U = 4;       // vectors in flight per lane
+  constexpr int U = 8;       // vectors per lane per chunk
   static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "block of whole vectors, power-of-two lanes");
   const int lane = threadIdx.x & 63;
   const int W = gridDim.x * 4;
-  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += W) {
-    const uint4* xr = x + (size_t)row * vpr;
+  const int cpr = (vpr + 64 * U - 1) / (64 * U);  // chunks per row
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6), c = 0;
+  if (row >= rows) return;
+  auto load = [&](uint4 (&v)[U], int r, int ch) {
+    const uint4* xr = x + (size_t)r * vpr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = xr[min(lane + 64 * (ch * U + u), vpr - 1)];
+  };
+  uint4 cur[U];
+  load(cur, row, 0);
+  while (row < rows) {
+    int nrow = row, nc = c + 1;
+    if (nc == cpr) {
+      nc = 0;
+      nrow += W;
+    }
+    uint4 nxt[U];
+    if (nrow < rows) load(nxt, nrow, nc);  // wavefront-uniform
     uint8_t* qr = q + (size_t)row * vpr * E;
-    for (int j0 = 0; j0 * 64 < vpr; j0 += U) {
-      uint4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = xr[min(lane + 64 * (j0 + u), vpr - 1)];
+    for (int u = 0; u < U; ++u) {
+      const int j = c * U + u;
+      if (j * 64 >= vpr) break;  // wavefront-uniform
+      const int i = lane + 64 * j;
+      const uint32_t own = vec_absmax_raw<XT>(cur[u]);
+      uint32_t raw = own;
+      uint32_t fin = own < kInfBits ? own : vec_absmax_finite<XT>(cur[u]);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if ((j0 + u) * 64 >= vpr) break;  // wavefront-uniform
-        const int i = lane + 64 * (j0 + u);
-        const uint32_t own = vec_absmax_raw<XT>(v[u]);
-        uint32_t raw = own;
-        uint32_t fin = own < kInfBits ? own : vec_absmax_finite<XT>(v[u]);
-#pragma unroll
-        for (int off = 1; off < G; off <<= 1) {
-          raw = max(raw, (uint32_t)__shfl_xor((int)raw, off, 64));
-          fin = max(fin, (uint32_t)__shfl_xor((int)fin, off, 64));
+      for (int off = 1; off < G; off <<= 1) {
+        raw = max(raw, (uint32_t)__shfl_xor((int)raw, off, 64));
+        fin = max(fin, (uint32_t)__shfl_xor((int)fin, off, 64));
+      }
+      const float am = __uint_as_float(fin);
+      const float s = scale_from_amax<FMT>(am);
+      const float r = 1.0f / s;
+      if (i < vpr) {
+        if (lane % G == 0) {
+          const size_t si = (size_t)row * nb + (size_t)i * E / BS;
+          scale[si] = s;
+          if (amax_out) amax_out[si] = am;
         }
-        const float am = __uint_as_float(fin);
-        const float s = scale_from_amax<FMT>(am);
-        const float r = 1.0f / s;
-        if (i < vpr) {
-          if (lane % G == 0) {
-            const size_t si = (size_t)row * nb + (size_t)i * E / BS;
-            scale[si] = s;
-            if (amax_out) amax_out[si] = am;
-          }
-          uint32_t w[E / 4];
-          cast_vec<XT, FMT, SR>(v[u], r, own, w, sd, ((size_t)row * vpr + i) * E);
-          store_codes<E>(qr + (size_t)i * E, w);
-        }
+        uint32_t w[E / 4];
+        cast_vec<XT, FMT, SR>(cur[u], r, own, w, sd, ((size_t)row * vpr + i) * E);
+        store_codes<E>(qr + (size_t)i * E, w);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    row = nrow;
+    c = nc;
   }
 }
 
@@ -85,7 +104,8 @@ hipError_t launch_quant_blocks(const void* x, int xt, int rows, int cols, int fm
   const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
   const int nb = (cols + bs - 1) / bs;
   const SrSeed sd{(uint32_t)seed, (uint32_t)(seed >> 32)};
-  const dim3 grid(min((rows + 3) / 4, kNumCUs * 3)), block(256);
+  // 16 wavefronts per CU (measured best for [4096, 4096]: one row each)
+  const dim3 grid(min((rows + 3) / 4, kNumCUs * 4)), block(256);
   const uint4* xv = static_cast<const uint4*>(x);
 #define HQ_BLK(XT_, FMT_, BS_, SR_)                                                                            \
   hipLaunchKernelGGL((quant_blocks_kernel<XT_, FMT_, BS_, SR_>), grid, block, 0, st, xv, q, scale, amax, rows, vpr, \
