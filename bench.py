@@ -301,8 +301,61 @@ def other_workloads(torch, hq, lib, reps):
     res["quantize_x_other_granularities"] = {"shape": "X bf16 [4096,4096] -> E4M3", **qv}
     del xs_, q
 
+    res["blockwise_ptpc4096"] = blockwise_timings(torch, hq, lib)
     res["training_linear"] = training_linear_timings(torch, hq, lib)
     return res
+
+
+def blockwise_timings(torch, hq, lib):
+    """Block-wise path on the PTPC operands: X bf16 [4096, 4096] quantized in
+    blocks of 32 and 128 along K (codes + one float32 scale and amax per block),
+    and the block-scaled GEMM 4096^3 at blocks of 32, 64 and 128 on the codes
+    of X and W quantized at that block size. Rotating sets as elsewhere."""
+    import workloads
+    P = ctypes.c_void_p
+    E4M3, BF16 = hq.HQ_E4M3, hq.HQ_BF16
+    x, w = workloads.ptpc_square(1)
+    xd = [torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16) for _ in range(8)]
+    q = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in range(8)]
+    quant = {}
+    for bs in (32, 128):
+        nb = K // bs
+        so = [torch.empty((M, nb), dtype=torch.float32, device="cuda") for _ in range(8)]
+        ao = [torch.empty((M, nb), dtype=torch.float32, device="cuda") for _ in range(8)]
+
+        def qlaunch(i, h, bs=bs, so=so, ao=ao):
+            st = lib.hq_quantize_fp8_blockwise(P(xd[i % 8].data_ptr()), BF16, M, K, E4M3, bs, 0, 0,
+                                               P(q[i % 8].data_ptr()), P(so[i % 8].data_ptr()),
+                                               P(ao[i % 8].data_ptr()), h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, qlaunch, 16)
+        alg = M * K * 3 + 2 * M * nb * 4
+        quant[f"bs{bs}"] = {"us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}
+    del q
+    wd = torch.from_numpy(w.view("int16")).cuda().view(torch.bfloat16)
+    gemm = {}
+    for bs in (32, 64, 128):
+        xq, xs, _ = hq.hq_quantize_fp8_blockwise(xd[0], E4M3, bs)
+        wq, ws, _ = hq.hq_quantize_fp8_blockwise(wd, E4M3, bs)
+        sets = [(xq.clone(), wq.clone(), xs.clone(), ws.clone(), torch.empty((M, N), dtype=torch.bfloat16,
+                                                                               device="cuda")) for _ in range(4)]
+
+        def glaunch(i, h, bs=bs, sets=sets):
+            a_, b_, c_, d_, o_ = sets[i % 4]
+            st = lib.hq_gemm_a8w8_blockscaled(P(a_.data_ptr()), E4M3, P(b_.data_ptr()), E4M3, P(c_.data_ptr()),
+                                              P(d_.data_ptr()), bs, M, N, K, P(o_.data_ptr()), h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, glaunch, 8)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        # the fold: one multiply and one FMA per output element per block, wave64
+        # FP32 VALU at 16 lanes x 4 SIMDs x 256 CUs x 2.4 GHz
+        valu_floor_us = 2.0 * M * N * (K // bs) / (16 * 4 * 256 * 2.4e9) * 1e6
+        gemm[f"bs{bs}"] = {"us": round(ms * 1e3, 3), "tflops": round(tf, 1), "frac_mfma": round(tf / FP8_PEAK_TFLOPS, 4),
+                           "fold_valu_floor_us": round(valu_floor_us, 1)}
+        del sets
+    return {"shape": "X, W bf16 [4096, 4096] (PTPC operands), E4M3, blocks along K", "quantize_x": quant,
+            "gemm_4096": gemm}
 
 
 def training_linear_timings(torch, hq, lib, copies=12):

@@ -27,6 +27,23 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // block-wise quantization
 // ---------------------------------------------------------------------------
+// Max over aligned groups of G lanes (G a power of two up to 64); every lane
+// of a group gets the group's max. Within a row of 16 lanes the partners come
+// from DPP lane moves (quad permutations swapping neighbours and pairs, then
+// the half-row and row mirrors, which pair each quad with the one it is
+// mirrored onto); wider groups finish with cross-row shuffles.
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+  if constexpr (G >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false));
+  if constexpr (G >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap2, 0xF, 0xF, false));
+  if constexpr (G >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowHalfMirror, 0xF, 0xF, false));
+  if constexpr (G >= 16) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowMirror, 0xF, 0xF, false));
+  if constexpr (G >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  if constexpr (G >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+  return v;
+}
+
 // One wavefront per row (rows w, w + W, ...); lane l holds vectors l + 64j.
 // A row is taken in chunks of U vectors per lane, and the next chunk (of this
 // row or of the wavefront's next row) is loaded before the current one is
@@ -43,8 +60,11 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint4* __restri
   constexpr int E = VecTraits<XT>::kElems;
   constexpr int G = BS / E;  // lanes per block
   constexpr int U = 8;       // vectors per lane per chunk
+  constexpr int CB = 64 * U * E / BS;  // blocks per chunk
   static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "block of whole vectors, power-of-two lanes");
-  const int lane = threadIdx.x & 63;
+  // a chunk's scales and maxima, gathered per wavefront for coalesced stores
+  __shared__ float sb[4][2][CB];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int W = gridDim.x * 4;
   const int cpr = (vpr + 64 * U - 1) / (64 * U);  // chunks per row
   int row = blockIdx.x * 4 + (threadIdx.x >> 6), c = 0;
@@ -71,27 +91,43 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint4* __restri
       if (j * 64 >= vpr) break;  // wavefront-uniform
       const int i = lane + 64 * j;
       const uint32_t own = vec_absmax_raw<XT>(cur[u]);
-      uint32_t raw = own;
-      uint32_t fin = own < kInfBits ? own : vec_absmax_finite<XT>(cur[u]);
-#pragma unroll
-      for (int off = 1; off < G; off <<= 1) {
-        raw = max(raw, (uint32_t)__shfl_xor((int)raw, off, 64));
-        fin = max(fin, (uint32_t)__shfl_xor((int)fin, off, 64));
+      uint32_t fin = own;
+      if (__any(own >= kInfBits)) {  // rare: some vector holds an Inf or NaN
+        if (own >= kInfBits) fin = vec_absmax_finite<XT>(cur[u]);
       }
+      fin = group_max_u32<G>(fin);
       const float am = __uint_as_float(fin);
       const float s = scale_from_amax<FMT>(am);
       const float r = 1.0f / s;
       if (i < vpr) {
         if (lane % G == 0) {
-          const size_t si = (size_t)row * nb + (size_t)i * E / BS;
-          scale[si] = s;
-          if (amax_out) amax_out[si] = am;
+          const int t = (lane + 64 * u) * E / BS;  // block within the chunk
+          sb[wv][0][t] = s;
+          sb[wv][1][t] = am;
         }
         uint32_t w[E / 4];
         cast_vec<XT, FMT, SR>(cur[u], r, own, w, sd, ((size_t)row * vpr + i) * E);
         store_codes<E>(qr + (size_t)i * E, w);
       }
     }
+    // LDS operations of one wavefront complete in order: the chunk's entries
+    // are in place for the reads below, and those reads finish before the
+    // next chunk overwrites them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int b0 = c * CB;
+#pragma unroll
+    for (int t = lane; t < CB; t += 64) {
+      if (b0 + t < nb) {
+        const size_t si = (size_t)row * nb + b0 + t;
+        __builtin_nontemporal_store(sb[wv][0][t], scale + si);
+        if (amax_out) __builtin_nontemporal_store(sb[wv][1][t], amax_out + si);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     row = nrow;
