@@ -140,7 +140,7 @@ size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols) {
   switch (gran) {
     case HQ_PER_TENSOR: return hq::kTensorWorkspaceBytes;
     case HQ_PER_TOKEN: return 0;
-    case HQ_PER_CHANNEL: return (size_t)hq::col_chunks((int)rows) * (size_t)cols * 4;
+    case HQ_PER_CHANNEL: return hq::kTensorWorkspaceBytes + (size_t)hq::col_chunks((int)rows) * (size_t)cols * 4;
     default: return 0;
   }
 }

@@ -16,7 +16,14 @@ constexpr int kMaxTensorPartials = 1024;  // blocks of the per-tensor partial pa
 // blocks' device-scope increments (17 us instead of 6 us for 8M elements).
 constexpr int kArrivalGroups = 32;
 constexpr int kArrivalStride = 32;        // uint32 words between arrival counters (128 bytes)
-constexpr size_t kTensorWorkspaceBytes = (size_t)kMaxTensorPartials * 4 + (size_t)kArrivalGroups * kArrivalStride * 4;
+// The single-pass per-tensor kernel's grid barrier follows the arrival
+// counters, one 128-byte line each: a 64-bit word (generation in the high
+// half, the last call's tensor amax bits in the low half) and the top arrival
+// counter.
+constexpr int kBarGen = 0, kBarTop = kArrivalStride, kBarWords = 2 * kArrivalStride;
+constexpr size_t kArrivalOffsetWords = kMaxTensorPartials;
+constexpr size_t kBarrierOffsetWords = kArrivalOffsetWords + (size_t)kArrivalGroups * kArrivalStride;
+constexpr size_t kTensorWorkspaceBytes = (kBarrierOffsetWords + kBarWords) * 4;
 constexpr int kColChunkRows = 128;        // rows per partial in the per-column pass
 
 int tensor_partial_blocks(size_t nvec);   // partials written by the per-tensor passes

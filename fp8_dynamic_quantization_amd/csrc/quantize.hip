@@ -30,6 +30,7 @@ namespace hq {
 
 constexpr int kBlock = 256;
 constexpr int kUnroll = 4;  // vectors in flight per thread in the grid-stride kernels
+constexpr int kPartialUnroll = 8;  // in the per-tensor partial-max pass
 constexpr uint32_t kNonfiniteBit = 0x80000000u;
 
 // ---------------------------------------------------------------------------
@@ -201,21 +202,29 @@ static hipError_t launch_rows_t(const void* x, int rows, int vpr, uint8_t* q, fl
 template <int XT>
 __global__ __launch_bounds__(kBlock) void amax_partials_kernel(const uint4* __restrict__ x, size_t nvec,
                                                                uint32_t* __restrict__ partial) {
+  constexpr int U = kPartialUnroll;
   __shared__ uint32_t red[kBlock / 64];
   uint32_t raw = 0, fin = 0;
-  const size_t stride = (size_t)gridDim.x * kBlock * kUnroll;
-  for (size_t base = blockIdx.x * (size_t)kBlock * kUnroll + threadIdx.x; base < nvec; base += stride) {
-    uint4 v[kUnroll];
+  const size_t stride = (size_t)gridDim.x * kBlock * U;
+  for (size_t base = blockIdx.x * (size_t)kBlock * U + threadIdx.x; base < nvec; base += stride) {
+    uint4 v[U];
+    uint32_t m[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       if (base + u * kBlock < nvec) v[u] = x[base + u * kBlock];
+    uint32_t mm = 0;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (base + u * kBlock < nvec) {
-        const uint32_t m = vec_absmax_raw<XT>(v[u]);
-        raw = max(raw, m);
-        fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[u]));
-      }
+    for (int u = 0; u < U; ++u) {
+      m[u] = base + u * kBlock < nvec ? vec_absmax_raw<XT>(v[u]) : 0u;
+      mm = max(mm, m[u]);
+    }
+    raw = max(raw, mm);
+    if (__any(mm >= kInfBits)) {  // rare: filter the non-finite elements out
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        fin = max(fin, m[u] < kInfBits ? m[u] : vec_absmax_finite<XT>(v[u]));
+    } else {
+      fin = max(fin, mm);
     }
   }
   const uint32_t braw = block_max_u32<kBlock>(raw, red);
@@ -274,6 +283,121 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
 }
 
 // ---------------------------------------------------------------------------
+// per tensor (dynamic), single pass
+// ---------------------------------------------------------------------------
+// Every thread keeps its V vectors (i = global thread + k * threads) in
+// registers while the grid agrees on the tensor amax, so X is read once. Each
+// block publishes its maximum as its own partial word (a device-scope atomic
+// store; one word per block, since atomics on one shared word serialise), waits
+// for the store to complete, and counts in through the two-level arrival tree
+// of the delayed path. The last arrival reduces the partials and publishes the
+// tensor amax together with the next generation in one 64-bit word (generation
+// in the high half, read by every block at its start); the other blocks poll
+// that word, so one load both releases them and hands them the amax. Then every
+// block casts its registers. The launcher only uses this kernel when the whole
+// grid fits on the device at once (occupancy query), so every block is
+// resident and the wait ends; as a guard the poll gives up after
+// kBarrierSpinTicks of the 100 MHz real-time clock and the block then reports
+// a NaN scale instead of waiting further.
+constexpr uint64_t kBarrierSpinTicks = 50000000;  // 0.5 s
+constexpr int kFusedBlocks = 512;  // two per CU (measured: 12.8 us for bf16 [4096, 4096], 13.7 at 1024)
+
+template <int XT, int FMT, bool SR, int V>
+__global__ __launch_bounds__(kBlock) void quant_tensor_fused_kernel(const uint4* __restrict__ x, size_t nvec,
+                                                                    uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                                    float* __restrict__ amax_out, uint32_t* partial,
+                                                                    uint32_t* arrivals, uint32_t* bar, SrSeed sd) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t red[kBlock / 64];
+  __shared__ uint32_t sh[3];  // generation at the start; last arrival?; amax bits, or ~0u when the wait gave up
+  uint64_t* word = reinterpret_cast<uint64_t*>(bar + kBarGen);
+  if (threadIdx.x == 0)
+    sh[0] = (uint32_t)(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  const size_t base = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  uint4 v[V];
+  uint32_t m[V];
+  // indices past the end reload the last vector (a real element: it cannot
+  // change the max, and its codes are not stored)
+#pragma unroll
+  for (int k = 0; k < V; ++k) v[k] = x[min(base + k * stride, nvec - 1)];
+  uint32_t mm = 0;
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    m[k] = vec_absmax_raw<XT>(v[k]);
+    mm = max(mm, m[k]);
+  }
+  uint32_t fin = mm;
+  if (__any(mm >= kInfBits)) {  // rare: filter the non-finite elements out
+    fin = 0;
+#pragma unroll
+    for (int k = 0; k < V; ++k) fin = max(fin, m[k] < kInfBits ? m[k] : vec_absmax_finite<XT>(v[k]));
+  }
+  const uint32_t bfin = block_max_u32<kBlock>(fin, red);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(partial + blockIdx.x, bfin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t groups = min(gridDim.x, (uint32_t)kArrivalGroups);
+    const uint32_t g = blockIdx.x % groups;
+    const uint32_t members = (gridDim.x - g + groups - 1) / groups;
+    uint32_t* sub = arrivals + g * kArrivalStride;
+    bool last = false;
+    if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+      __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __hip_atomic_fetch_add(bar + kBarTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    }
+    sh[1] = last;
+  }
+  __syncthreads();
+  const uint32_t g0 = sh[0];
+  if (sh[1]) {
+    // the last arrival: every partial is in place
+    uint32_t pm = 0;
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += kBlock)
+      pm = max(pm, __hip_atomic_load(partial + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    pm = block_max_u32<kBlock>(pm, red);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(bar + kBarTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word, ((uint64_t)(g0 + 1u) << 32) | pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh[2] = pm;
+    }
+  } else if (threadIdx.x == 0) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    uint32_t got = ~0u;
+    for (;;) {
+      const uint64_t w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(w >> 32) != g0) {
+        got = (uint32_t)w;
+        break;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierSpinTicks) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    sh[2] = got;
+  }
+  __syncthreads();
+  const uint32_t pm = sh[2];
+  const bool gave_up = pm == ~0u;
+  const float amax = __uint_as_float(pm);
+  const float s = gave_up ? __uint_as_float(0x7fc00000u) : scale_from_amax<FMT>(amax);
+  const float r = 1.0f / s;
+  if (threadIdx.x == 0 && (blockIdx.x == 0 || gave_up)) {
+    scale[0] = s;
+    if (amax_out) amax_out[0] = amax;
+  }
+  // (the codes need no tensor-wide non-finite flag: the cast patches NaN per vector)
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const size_t i = base + k * stride;
+    if (i < nvec) {
+      uint32_t w[E / 4];
+      cast_vec<XT, FMT, SR>(v[k], r, m[k], w, sd, i * E);
+      store_codes<E>(q + i * E, w);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // per column (dynamic)
 // ---------------------------------------------------------------------------
 // Tile: 32 vectors across (256 bf16 / 128 fp32 columns) x kColRows rows.
@@ -305,13 +429,42 @@ __global__ __launch_bounds__(kBlock) void colmax_partials_kernel(const uint4* __
       const int r = r0 + ty + 8 * j;
       v[j] = x[(size_t)(r < rows ? r : r0) * vpr + vc];
     }
+    // raw maxima first (bf16: two 16-bit magnitudes per max); the finite-only
+    // pass runs only where a raw max is Inf/NaN
+    uint32_t any_nf = 0;
+    if constexpr (XT == kBF16) {
+      typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+      us2 p[4] = {us2{0, 0}, us2{0, 0}, us2{0, 0}, us2{0, 0}};
 #pragma unroll
-    for (int j = 0; j < kColPer; ++j) {
+      for (int j = 0; j < kColPer; ++j) {
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint32_t a = __float_as_uint(vec_elem<XT>(v[j], e)) & 0x7fffffffu;
-        m[e] = max(m[e], a < kInfBits ? a : 0u);
-        nf |= (a >= kInfBits ? 1u : 0u) << e;
+        for (int d = 0; d < 4; ++d) p[d] = __builtin_elementwise_max(p[d], __builtin_bit_cast(us2, w[d] & 0x7fff7fffu));
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        m[2 * d] = (uint32_t)p[d][0] << 16;
+        m[2 * d + 1] = (uint32_t)p[d][1] << 16;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kColPer; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) m[e] = max(m[e], __float_as_uint(vec_elem<XT>(v[j], e)) & 0x7fffffffu);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) any_nf |= m[e] >= kInfBits ? 1u : 0u;
+    if (__any(any_nf)) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) m[e] = 0;
+#pragma unroll
+      for (int j = 0; j < kColPer; ++j) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t a = __float_as_uint(vec_elem<XT>(v[j], e)) & 0x7fffffffu;
+          m[e] = max(m[e], a < kInfBits ? a : 0u);
+          nf |= (a >= kInfBits ? 1u : 0u) << e;
+        }
       }
     }
   }
@@ -703,6 +856,55 @@ hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt,
 #undef CALL
 }
 
+// Blocks of the single-pass kernel that one device holds at once, for this
+// instantiation (its register use sets the occupancy; cached per process).
+template <int XT, int FMT, bool SR, int V>
+static int fused_capacity() {
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_tensor_fused_kernel<XT, FMT, SR, V>, kBlock, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      n = 0;
+    }
+    per_cu = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return per_cu * cus;
+}
+
+// Single pass when the tensor fits in the registers of at most kFusedBlocks
+// blocks, and the device can hold the whole grid at once; the two-pass path
+// otherwise.
+template <int XT, int FMT, bool SR, int V>
+static bool try_fused(const uint4* xv, size_t nvec, uint8_t* q, float* scale, float* amax, uint32_t* ws, SrSeed sd,
+                      hipStream_t st, hipError_t* err) {
+  constexpr size_t kPerBlock = (size_t)kBlock * V;
+  const size_t grid = (nvec + kPerBlock - 1) / kPerBlock;
+  if (grid > (size_t)kFusedBlocks || (int)grid > fused_capacity<XT, FMT, SR, V>()) return false;
+  hipLaunchKernelGGL((quant_tensor_fused_kernel<XT, FMT, SR, V>), dim3((unsigned)grid), dim3(kBlock), 0, st, xv, nvec,
+                     q, scale, amax, ws, ws + kArrivalOffsetWords, ws + kBarrierOffsetWords, sd);
+  *err = hipGetLastError();
+  return true;
+}
+
+template <int XT, int FMT, bool SR>
+static bool launch_fused(const uint4* xv, size_t nvec, uint8_t* q, float* scale, float* amax, uint32_t* ws, SrSeed sd,
+                         hipStream_t st, hipError_t* err) {
+  constexpr size_t kB = (size_t)kFusedBlocks * kBlock;
+  if (nvec <= kB * 4) return try_fused<XT, FMT, SR, 4>(xv, nvec, q, scale, amax, ws, sd, st, err);
+  if (nvec <= kB * 8) return try_fused<XT, FMT, SR, 8>(xv, nvec, q, scale, amax, ws, sd, st, err);
+  // (the stochastic cast at 16 vectors per thread would spill its registers)
+  if (!SR && nvec <= kB * 16) return try_fused<XT, FMT, SR, SR ? 8 : 16>(xv, nvec, q, scale, amax, ws, sd, st, err);
+  return false;
+}
+
 hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
                                float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st) {
   const size_t nvec = xt == kBF16 ? numel / 8 : numel / 4;
@@ -713,7 +915,9 @@ hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uin
   size_t qb = (nvec + kBlock * kUnroll - 1) / (kBlock * kUnroll);
   if (qb > 2048) qb = 2048;
   if (qb < 1) qb = 1;
+  hipError_t err = hipSuccess;
 #define CALL(A, B, S)                                                                                    \
+  if (launch_fused<A, B, S>(xv, nvec, q, scale, amax, partial, sd, st, &err)) return err;               \
   hipLaunchKernelGGL((amax_partials_kernel<A>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, partial);        \
   hipLaunchKernelGGL((quant_tensor_kernel<A, B, S>), dim3((unsigned)qb), dim3(kBlock), 0, st, xv, nvec, \
                      (const uint32_t*)partial, nb, q, scale, amax, sd);                                  \
@@ -726,7 +930,9 @@ hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt,
                              float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st) {
   const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
   const dim3 grid((vpr + kColVecs - 1) / kColVecs, col_chunks(rows));
-  uint32_t* partial = static_cast<uint32_t*>(ws);
+  // the column partials follow the per-tensor region, so one workspace can
+  // serve every granularity without disturbing the per-tensor counters
+  uint32_t* partial = static_cast<uint32_t*>(ws) + kTensorWorkspaceBytes / 4;
   const uint4* xv = static_cast<const uint4*>(x);
   const SrSeed sd = sr_seed(seed);
 #define CALL(A, B, S)                                                                               \
@@ -748,7 +954,7 @@ hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, ui
   const SrSeed sd = sr_seed(seed);
 #define CALL(A, B, S)                                                                                  \
   hipLaunchKernelGGL((quant_delayed_kernel<A, B, S>), dim3(nb), dim3(kBlock), 0, st, xv, nvec, q, scale, \
-                     amax, state, len, idx, margin, flag, partial, partial + kMaxTensorPartials, sd);    \
+                     amax, state, len, idx, margin, flag, partial, partial + kArrivalOffsetWords, sd);   \
   return hipGetLastError()
   HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
@@ -761,7 +967,7 @@ hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int f
   const dim3 grid(min(tiles, kMaxTensorPartials)), block(kBlock);
   const uint4* xv = static_cast<const uint4*>(x);
   uint32_t* partial = static_cast<uint32_t*>(ws);
-  uint32_t* arrivals = partial ? partial + kMaxTensorPartials : nullptr;
+  uint32_t* arrivals = partial ? partial + kArrivalOffsetWords : nullptr;
   const int mode = scale_in ? kScaleGiven : (state ? kScaleRing : kScaleDynamic);
   int ndyn = 0;
   if (mode == kScaleDynamic) {

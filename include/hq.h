@@ -83,10 +83,12 @@ typedef struct hq_ring {
 int64_t hq_scale_count(int gran, int64_t rows, int64_t cols);
 
 /* Bytes of device workspace hq_quantize_fp8 needs for this granularity and
- * shape: 0 for HQ_PER_TOKEN, 8 KB of block partials and arrival counters for
- * HQ_PER_TENSOR (dynamic or delayed), ceil(rows/128) * cols * 4 for
- * HQ_PER_CHANNEL. Returns 0 for invalid arguments (hq_quantize_fp8 then
- * reports the error). */
+ * shape: 0 for HQ_PER_TOKEN; for HQ_PER_TENSOR (dynamic or delayed) a fixed
+ * 8448-byte region of block partials, arrival counters and the single-pass
+ * grid barrier; for HQ_PER_CHANNEL that region plus ceil(rows/128) * cols * 4 bytes
+ * of column partials after it (so one workspace sized for the largest call
+ * serves every granularity). Returns 0 for invalid arguments (hq_quantize_fp8
+ * then reports the error). */
 size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
 
 /* Dynamic (or delayed) FP8 quantization of a row-major [rows, cols] tensor.
@@ -114,11 +116,14 @@ size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
  *   amax_out   device, optional (NULL), float32 [scale_count]: the group amax
  *   ring       host pointer to an hq_ring, or NULL for dynamic scaling
  *   workspace  device, at least hq_quantize_workspace_bytes(gran, rows, cols)
- *              bytes (may be NULL when that is 0). For delayed scaling its
- *              arrival counters must be zero before the first call: zero-fill
- *              it once; every call leaves them at zero again. Dynamic calls
- *              need no initialised contents. Calls that share a workspace
- *              must not run concurrently.
+ *              bytes (may be NULL when that is 0). Zero-fill it once before
+ *              its first call: its counters (delayed scaling, and the grid
+ *              barrier of the single-pass per-tensor kernel) start from zero,
+ *              and every call leaves them ready for the next. Calls that share
+ *              a workspace must not run concurrently. Dynamic per-tensor
+ *              quantization of up to 2^24 bf16 (2^23 float32) elements runs as
+ *              one pass over x, whose blocks agree on the amax through the
+ *              workspace; larger tensors take a partial-max pass first.
  * Requires cols % 16 == 0 (16-byte vector rows), 1 <= rows, cols < 2^31,
  * rows * cols < 2^40. rows == 0 returns HQ_OK without a launch. Outputs must not
  * overlap inputs. */

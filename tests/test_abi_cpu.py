@@ -83,8 +83,11 @@ def test_preshuffled_bytes_matches_layout(hq):
 def test_workspace_bytes(hq):
     assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_TOKEN, 4096, 4096) == 0
     assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 4096, 4096) > 0
-    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 4096, 4096) == 32 * 4096 * 4
-    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 1, 64) == 64 * 4
+    region = hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 1, 16)
+    assert region == hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 4096, 4096)
+    # per-channel: the per-tensor region, then ceil(rows/128) * cols column partials
+    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 4096, 4096) == region + 32 * 4096 * 4
+    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 1, 64) == region + 64 * 4
     assert hq.hq_quantize_workspace_bytes(9, 4, 4) == 0
 
 

@@ -128,11 +128,14 @@ def test_grouped_moe_full(hq):
 
 
 def test_repeated_calls_with_shared_workspace(hq):
-    """Per-tensor and per-channel reuse one workspace across calls of different
-    sizes; each result must be independent of the previous call."""
+    """Per-tensor and per-channel reuse one workspace (zero-filled once) across
+    calls of different sizes, single-pass and two-pass per-tensor grids
+    included; each result must be independent of the previous call."""
     rng = np.random.default_rng(5)
-    shapes = [(512, 1024), (16, 64), (300, 2048), (1, 16)]
-    ws = torch.empty(max(hq.hq_quantize_workspace_bytes(g, *s) for s in shapes for g in GRANS),
+    # float32 vectors: 131072 and 153600 (single pass, 4 per thread), 2^21
+    # (single pass, 512 blocks of 16 per thread), 2^21 + 2^11 (two passes)
+    shapes = [(512, 1024), (16, 64), (300, 2048), (1, 16), (2048, 4096), (1028, 8192)]
+    ws = torch.zeros(max(hq.hq_quantize_workspace_bytes(g, *s) for s in shapes for g in GRANS),
                      dtype=torch.uint8, device="cuda")
     for it in range(2):
         for shape in shapes:
@@ -142,6 +145,42 @@ def test_repeated_calls_with_shared_workspace(hq):
                 q_ref, s_ref, a_ref = Q.quantize_dynamic(x, Q.F32, fp8.E4M3, gran)
                 assert np.array_equal(host(q), q_ref)
                 assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_single_pass_per_tensor_barrier_state(hq):
+    """Dynamic per-tensor calls of up to 2^24 bf16 elements run as one pass whose
+    blocks agree on the amax through the workspace. After every call the arrival
+    counters and the top counter are back at zero; the 64-bit barrier word holds
+    the number of single-pass calls so far in its high half and the last such
+    call's amax bits in its low half. A tensor one row too large for the single
+    pass (two passes) and a delayed call in between leave the word alone."""
+    rng = np.random.default_rng(23)
+    region = hq.hq_quantize_workspace_bytes(Q.PER_TENSOR, 1, 16)
+    ws = torch.zeros(region, dtype=torch.uint8, device="cuda")
+    arrivals = slice(4096, 8192)        # 1024 partial words, then 32 arrival lines
+    word_lo, word_hi, top = 2048, 2049, 2048 + 32  # uint32 indices of the barrier lines
+    gen, last_amax = 0, 0
+    ring, st, flag = hq.Ring(4), Q.ring_new(4), 0
+    steps = [(1, 16), (300, 1024), (4096, 4096), (4097, 4096), "delayed", (64, 2048), (4096, 4096), (1, 16)]
+    for t, sh in enumerate(steps):
+        if sh == "delayed":
+            bits = workloads.random_bf16(rng, (128, 256))
+            q, _, _ = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, Q.PER_TENSOR, ring=ring, ring_idx=0, workspace=ws)
+            q_ref, _, _, st, flag = Q.quantize_delayed(bits, Q.BF16, fp8.E4M3, st, 0, 0, flag)
+        else:
+            bits = workloads.random_bf16(rng, sh, std=float(10.0 ** rng.integers(-2, 3)))
+            q, s, a = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, Q.PER_TENSOR, workspace=ws)
+            q_ref, s_ref, a_ref = Q.quantize_dynamic(bits, Q.BF16, fp8.E4M3, Q.PER_TENSOR)
+            assert host(s).view(np.uint32)[0] == s_ref.view(np.uint32)[0], (t, sh)
+            assert host(a).view(np.uint32)[0] == a_ref.view(np.uint32)[0], (t, sh)
+            if sh[0] * sh[1] <= 1 << 24:
+                gen, last_amax = gen + 1, int(a_ref.view(np.uint32)[0])
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), q_ref), (t, sh)
+        w = host(ws).view(np.uint32)
+        assert not host(ws)[arrivals].any(), (t, sh)
+        assert w[top] == 0, (t, sh)
+        assert (int(w[word_hi]), int(w[word_lo])) == (gen, last_amax), (t, sh)
 
 
 # ---- delayed scaling ---------------------------------------------------------------
