@@ -228,10 +228,23 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t* w) {
 
 // ---- reductions ----------------------------------------------------------------
 
+// Max over the 64 lanes of a wavefront, returned to every lane. DPP lane moves
+// only (no LDS round trips): within each row of 16 lanes, the quad swaps and
+// the half-row and row mirrors leave the row max in every lane; the row
+// broadcasts then fold row 0 into row 1 and row 2 into row 3 (lane 15 of a row
+// to the next row), and rows 0-1 into rows 2-3 (lane 31), so lane 63 ends with
+// the wavefront max, read back as a uniform value.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
+  constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+  constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kQuadSwap1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kQuadSwap2, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kRowHalfMirror, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kRowMirror, 0xF, 0xF, false));
+  // rows outside the row mask keep `old` (= v), so max leaves them unchanged
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kRowBcast15, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kRowBcast31, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Block-wide max of a uint32; every thread gets the result. `lds` needs
