@@ -344,7 +344,7 @@ def blockwise_timings(torch, hq, lib):
         def glaunch(i, h, bs=bs, sets=sets):
             a_, b_, c_, d_, o_ = sets[i % 4]
             st = lib.hq_gemm_a8w8_blockscaled(P(a_.data_ptr()), E4M3, P(b_.data_ptr()), E4M3, P(c_.data_ptr()),
-                                              P(d_.data_ptr()), bs, M, N, K, P(o_.data_ptr()), h)
+                                              P(d_.data_ptr()), bs, M, N, K, None, P(o_.data_ptr()), h)
             assert st == 0, hq.hq_last_error()
         ms = time_graph(torch, glaunch, 8)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12

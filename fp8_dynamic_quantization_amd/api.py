@@ -162,17 +162,22 @@ def hq_quantize_fp8_blockwise(x: torch.Tensor, fmt: int = HQ_E4M3, block_size: i
 
 
 def hq_gemm_a8w8_blockscaled(xq: torch.Tensor, xf: int, wq: torch.Tensor, wf: int, x_scales: torch.Tensor,
-                             w_scales: torch.Tensor, block_size: int = 32, out=None, stream=None) -> torch.Tensor:
+                             w_scales: torch.Tensor, block_size: int = 32, bias=None, out=None,
+                             stream=None) -> torch.Tensor:
     """Block-scaled GEMM of row-major codes xq [m, k], wq [n, k] with block
-    scales [m, nb], [n, nb]; returns bf16 [m, n]."""
+    scales [m, nb], [n, nb] and an optional bf16 bias [n]; returns bf16 [m, n]."""
     xq, wq = xq.contiguous(), wq.contiguous()
     x_scales, w_scales = x_scales.contiguous(), w_scales.contiguous()
     m, k = xq.shape
     n = wq.shape[0]
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.numel() != n:
+            raise ValueError("bias must be bf16 with n elements")
+        bias = bias.contiguous()
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
     check(load().hq_gemm_a8w8_blockscaled(_ptr(xq), xf, _ptr(wq), wf, _ptr(x_scales), _ptr(w_scales), int(block_size),
-                                          m, n, k, _ptr(out), _stream(xq.device, stream)))
+                                          m, n, k, _ptr(bias), _ptr(out), _stream(xq.device, stream)))
     return out
 
 

@@ -370,8 +370,19 @@ __global__ __launch_bounds__(bsg::threads<NJ>()) __attribute__((amdgpu_waves_per
     __syncthreads();
   }
 
-  // epilogue: four consecutive columns per lane, as one 8-byte store where the
-  // row's columns allow it
+  // epilogue: the bias (output units) added in float32, then four consecutive
+  // columns per lane as one 8-byte store where the row's columns allow it
+  if (a.bias) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = min(n0 + wcol + 16 * j + r, a.n - 1);
+        const float b = __uint_as_float((uint32_t)a.bias[col] << 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j][r] += b;
+      }
+  }
   const bool vec = (a.n % 4 == 0) && (reinterpret_cast<uintptr_t>(a.out) % 8 == 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -503,7 +503,7 @@ hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
 
 hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq, int wf, const float* x_scales,
                                    const float* w_scales, int block_size, int64_t m, int64_t n, int64_t k,
-                                   uint16_t* out, hipStream_t stream) {
+                                   const uint16_t* bias, uint16_t* out, hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, m, n, k);
   if (st != HQ_OK) return st;
   if (block_size != 32 && block_size != 64 && block_size != 128)
@@ -512,8 +512,8 @@ hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq,
   if (!xq || !wq || !x_scales || !w_scales || !out)
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq, x_scales, w_scales and out must be non-NULL");
   if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "xq and wq must be 16-byte aligned");
-  if (!aligned(out, 2) || !aligned(x_scales, 4) || !aligned(w_scales, 4))
-    return fail(HQ_ERR_INVALID_ARGUMENT, "out must be 2-byte and the scales 4-byte aligned");
+  if (!aligned(out, 2) || !aligned(x_scales, 4) || !aligned(w_scales, 4) || (bias && !aligned(bias, 2)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "out and bias must be 2-byte and the scales 4-byte aligned");
   const int64_t nb = (k + block_size - 1) / block_size;
   const Range rg[] = {
       {out, (size_t)m * (size_t)n * 2, "out"},
@@ -521,13 +521,14 @@ hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq,
       {wq, (size_t)n * (size_t)k, "wq"},
       {x_scales, (size_t)m * (size_t)nb * 4, "x_scales"},
       {w_scales, (size_t)n * (size_t)nb * 4, "w_scales"},
+      {bias, bias ? (size_t)n * 2 : 0, "bias"},
   };
   const char* other = nullptr;
-  const char* a = find_overlap(rg, 5, &other);
+  const char* a = find_overlap(rg, 6, &other);
   if (a && strcmp(a, "out") == 0) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
   st = check_device();
   if (st != HQ_OK) return st;
-  hq::BlockGemmArgs g{xq, wq, x_scales, w_scales, out, (int)m, (int)n, (int)k, (int)nb};
+  hq::BlockGemmArgs g{xq, wq, x_scales, w_scales, bias, out, (int)m, (int)n, (int)k, (int)nb};
   (void)hipGetLastError();
   return launched(hq::launch_gemm_blockscaled(g, xf, wf, block_size, stream), "hq_gemm_a8w8_blockscaled");
 }

@@ -109,6 +109,7 @@ struct BlockGemmArgs {
   const uint8_t* wq;  // [n, k]
   const float* xs;    // [m, nb]
   const float* ws;    // [n, nb]
+  const uint16_t* bias;  // bf16 [n], or null
   uint16_t* out;      // bf16 [m, n]
   int m, n, k, nb;
 };

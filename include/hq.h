@@ -211,23 +211,26 @@ hq_status hq_quantize_fp8_blockwise(const void* x, int xt, int64_t rows, int64_t
                                     hipStream_t stream);
 
 /* Block-scaled FP8 GEMM (hip-quant README, "Block-scaled Linear ...": the
- * pre-quantized path consumes FP8 bytes and both block-scale tensors):
+ * pre-quantized path consumes FP8 bytes, both block-scale tensors and an
+ * optional bias):
  *   out[m, n] = bf16( sum_b x_scales[m, b] * w_scales[n, b] *
- *                     sum_{k in block b} dec(XQ[m, k]) * dec(WQ[n, k]) )
+ *                     sum_{k in block b} dec(XQ[m, k]) * dec(WQ[n, k])  + bias[n] )
  * Each block's partial sum (float32 MFMAs) is folded into the float32 result
- * with one fused multiply-add by the float32 product of the two scales.
+ * with one fused multiply-add by the float32 product of the two scales; the
+ * bias (bf16, output units) is then added in float32.
  *   xq        device, uint8 [m, k] codes in format xf, row-major, 16-byte aligned
  *   wq        device, uint8 [n, k] codes in format wf, row-major (not
  *             pre-shuffled), 16-byte aligned
  *   x_scales  device, float32 [m, ceil(k / block_size)]
  *   w_scales  device, float32 [n, ceil(k / block_size)]
+ *   bias      device, bf16 bits [n], 2-byte aligned, or NULL for none
  *   out       device, bf16 bits [m, n], caller-owned, must not overlap an input
  * Requires block_size in {32, 64, 128}, k % 16 == 0, 16 <= k < 2^24. m == 0 or
  * n == 0 returns HQ_OK without a launch. */
 hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq, int wf,
                                    const float* x_scales, const float* w_scales, int block_size,
-                                   int64_t m, int64_t n, int64_t k, uint16_t* out,
-                                   hipStream_t stream);
+                                   int64_t m, int64_t n, int64_t k, const uint16_t* bias,
+                                   uint16_t* out, hipStream_t stream);
 
 /* Fold one amax sample into a ring and publish the next scale (the delayed
  * update of hq_quantize_fp8, as its own launch). `amax` is a device float32

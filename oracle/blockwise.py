@@ -20,6 +20,9 @@ Readings where the README leaves a step open:
       bf16.
   B3  Stochastic block-wise E5M2 (quantize_e5m2_blockwise_stochastic) is the
       block scale of B1 with the stochastic cast of oracle/stochastic.py.
+  B4  The optional bias of the block-scaled linear is bf16, one value per
+      output column, in output units: it is added to the block sum (in
+      float32 on the device), before the bf16 rounding of the output.
 """
 from __future__ import annotations
 
@@ -59,8 +62,8 @@ def quantize_blockwise(x: np.ndarray, dtype: int, fmt: int, block_size: int, sto
     return q, s, amax
 
 
-def gemm_blockscaled(xq, xf: int, wq, wf: int, x_scales, w_scales, block_size: int) -> np.ndarray:
-    """float64 reference [M, N] of reading B2."""
+def gemm_blockscaled(xq, xf: int, wq, wf: int, x_scales, w_scales, block_size: int, bias=None) -> np.ndarray:
+    """float64 reference [M, N] of readings B2 and B4 (bias: bf16 bits [N] or None)."""
     a = fp8.decode(xq, xf)
     b = fp8.decode(wq, wf)
     m, k = a.shape
@@ -72,11 +75,14 @@ def gemm_blockscaled(xq, xf: int, wq, wf: int, x_scales, w_scales, block_size: i
     for blk in range(nb):
         sl = slice(blk * block_size, min(k, (blk + 1) * block_size))
         out += (a[:, sl] @ b[:, sl].T) * xs[:, blk, None] * ws[None, :, blk]
+    if bias is not None:
+        out += G.bf16_bits_to_f64(bias)[None, :]
     return out
 
 
-def gemm_blockscaled_rows(xq, xf: int, wq, wf: int, x_scales, w_scales, block_size: int, pairs):
-    """Reference and sum of |terms| at selected (m, n) positions."""
+def gemm_blockscaled_rows(xq, xf: int, wq, wf: int, x_scales, w_scales, block_size: int, pairs, bias=None):
+    """Reference and sum of |terms| (the bias one of them) at selected (m, n)
+    positions."""
     ta, tb = fp8.decode_table(xf), fp8.decode_table(wf)
     xq = np.asarray(xq, dtype=np.uint8)
     wq = np.asarray(wq, dtype=np.uint8)
@@ -91,7 +97,11 @@ def gemm_blockscaled_rows(xq, xf: int, wq, wf: int, x_scales, w_scales, block_si
     blk = np.arange(k) // block_size
     sc = xs[pairs[:, 0]][:, blk] * ws[pairs[:, 1]][:, blk]
     t = a * b * sc
-    return t.sum(axis=1), np.abs(t).sum(axis=1)
+    ref, at = t.sum(axis=1), np.abs(t).sum(axis=1)
+    if bias is not None:
+        bv = G.bf16_bits_to_f64(bias)[pairs[:, 1]]
+        ref, at = ref + bv, at + np.abs(bv)
+    return ref, at
 
 
 def tolerance_blockscaled(ref, absterms, nblocks: int):

@@ -387,8 +387,8 @@ def test_blockwise_valid_calls_reach_device_gate(hq):
     assert _blockwise(hq, a=fake(2, 1024)) == U
 
 
-def _gemm_bs(hq, xf=0, wf=0, bs=32, m=64, n=128, k=256, out=fake(4), xs=fake(2), ws=fake(3), xq=fake(0)):
-    return hq.load().hq_gemm_a8w8_blockscaled(xq, xf, fake(1), wf, xs, ws, bs, m, n, k, out, None)
+def _gemm_bs(hq, xf=0, wf=0, bs=32, m=64, n=128, k=256, out=fake(4), xs=fake(2), ws=fake(3), xq=fake(0), bias=None):
+    return hq.load().hq_gemm_a8w8_blockscaled(xq, xf, fake(1), wf, xs, ws, bs, m, n, k, bias, out, None)
 
 
 def test_gemm_blockscaled_validation(hq):
@@ -402,6 +402,8 @@ def test_gemm_blockscaled_validation(hq):
     assert _gemm_bs(hq, out=fake(4, 1)) == E
     assert _gemm_bs(hq, out=fake(3, 64)) == E           # out overlaps w_scales
     assert "overlaps" in hq.hq_last_error()
+    assert _gemm_bs(hq, bias=fake(5, 1)) == E           # misaligned bias
+    assert _gemm_bs(hq, bias=fake(4, 64)) == E          # out overlaps the bias
     assert _gemm_bs(hq, m=0, xq=ctypes.c_void_p(0)) == hq.HQ_OK
 
 
@@ -410,6 +412,7 @@ def test_gemm_blockscaled_valid_calls_reach_device_gate(hq):
     U = hq.HQ_ERR_UNSUPPORTED_DEVICE
     for bs in (32, 64, 128):
         assert _gemm_bs(hq, bs=bs, k=272) == U
+    assert _gemm_bs(hq, bias=fake(5)) == U
     # the two inputs may share memory (same codes for X and W)
-    assert hq.load().hq_gemm_a8w8_blockscaled(fake(0), 0, fake(0), 0, fake(2), fake(2), 32, 64, 64, 256, fake(4),
-                                              None) == U
+    assert hq.load().hq_gemm_a8w8_blockscaled(fake(0), 0, fake(0), 0, fake(2), fake(2), 32, 64, 64, 256, None,
+                                              fake(4), None) == U

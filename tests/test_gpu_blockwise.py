@@ -262,3 +262,48 @@ def test_blockscaled_equals_plain_gemm_for_uniform_scales(hq):
     tol = B.tolerance_blockscaled(ref, at, nb)
     for o in (out, plain):
         assert np.all(np.abs(G.bf16_bits_to_f64(host(o)) - ref) <= tol)
+
+
+def _bf16_bias(rng, n, scale):
+    return workloads.to_bf16_bits((rng.standard_normal(n) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("shape", [(130, 260, 272), (300, 520, 1040)])
+@pytest.mark.parametrize("bs", [32, 128])
+def test_blockscaled_gemm_bias_narrow_strict(hq, shape, bs):
+    """Reading B4: the bf16 bias added to the block sum before the output
+    rounding; ragged N covers the bias of the last, partial column tile."""
+    m, n, k = shape
+    rng = np.random.default_rng(_seed(shape, bs, "bias"))
+    xq, wq = narrow_codes(rng, (m, k), fp8.E4M3), narrow_codes(rng, (n, k), fp8.E5M2)
+    nb = B.block_count(k, bs)
+    xs, ws = _block_scales(rng, m, nb), _block_scales(rng, n, nb)
+    bias = _bf16_bias(rng, n, 50.0)
+    out = hq.hq_gemm_a8w8_blockscaled(dev_u8(xq), fp8.E4M3, dev_u8(wq), fp8.E5M2, dev_f32(xs), dev_f32(ws), bs,
+                                      bias=dev_bf16(bias))
+    torch.cuda.synchronize()
+    ii, jj = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+    pairs = np.stack([ii.reshape(-1), jj.reshape(-1)], axis=1)
+    got = G.bf16_bits_to_f64(host(out)[pairs[:, 0], pairs[:, 1]])
+    ref, at = B.gemm_blockscaled_rows(xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, bs, pairs, bias=bias)
+    bad = np.nonzero(np.abs(got - ref) > B.tolerance_blockscaled(ref, at, nb))[0]
+    assert bad.size == 0, f"{bad.size} outside; first at {pairs[bad[0]].tolist()}: got {got[bad[0]]}, ref {ref[bad[0]]}"
+
+
+def test_blockscaled_gemm_bias_exact(hq):
+    """Exact partials, power-of-two scales and integer biases: every sum is exact
+    in float32, so the output is the bf16 rounding of the oracle value, bit for
+    bit."""
+    rng = np.random.default_rng(41)
+    m, n, k, bs = 48, 100, 128, 64
+    xq, wq = narrow_codes(rng, (m, k), fp8.E4M3), narrow_codes(rng, (n, k), fp8.E4M3)
+    xs = np.ldexp(1.0, rng.integers(-2, 2, (m, 2))).astype(np.float32)
+    ws = np.ldexp(1.0, rng.integers(-2, 2, (n, 2))).astype(np.float32)
+    bias = workloads.to_bf16_bits(rng.integers(-64, 65, n).astype(np.float32))
+    out = hq.hq_gemm_a8w8_blockscaled(dev_u8(xq), fp8.E4M3, dev_u8(wq), fp8.E4M3, dev_f32(xs), dev_f32(ws), bs,
+                                      bias=dev_bf16(bias))
+    torch.cuda.synchronize()
+    ref = B.gemm_blockscaled(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs, bias=bias)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(host(out), want)

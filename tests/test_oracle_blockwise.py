@@ -108,3 +108,42 @@ def test_gemm_exact_rationals(k, bs):
                           Fraction(float(xs[i, c // bs])) * Fraction(float(ws[j, c // bs])))
             assert abs(Fraction(float(ref[i, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 300)
             assert rows[i * n + j] == pytest.approx(float(exact), rel=2.0 ** -45, abs=1e-300)
+
+
+def _bf16_value(bits16: int) -> float:
+    import struct
+    return struct.unpack("<f", struct.pack("<I", int(bits16) << 16))[0]
+
+
+def test_gemm_bias_exact_rationals():
+    """Reading B4: the bias is one more term in output units, exactly."""
+    rng = np.random.default_rng(31)
+    ta, tb = fp8.decode_table(fp8.E4M3), fp8.decode_table(fp8.E4M3)
+    fa = np.array([c for c in range(256) if np.isfinite(ta[c])], dtype=np.uint8)
+    m, n, k, bs = 2, 5, 64, 32
+    xq, wq = rng.choice(fa, (m, k)), rng.choice(fa, (n, k))
+    xs = rng.uniform(1e-3, 1.0, (m, 2)).astype(np.float32)
+    ws = rng.uniform(1e-3, 1.0, (n, 2)).astype(np.float32)
+    bias = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+    bias[(bias & 0x7F80) == 0x7F80] = 0x3F80  # finite values only (1.0 for Inf/NaN patterns)
+    ref = B.gemm_blockscaled(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs, bias=bias)
+    rows, at = B.gemm_blockscaled_rows(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs,
+                                       np.array([[i, j] for i in range(m) for j in range(n)]), bias=bias)
+    for i in range(m):
+        for j in range(n):
+            exact = Fraction(_bf16_value(bias[j]))
+            for c in range(k):
+                exact += (Fraction(float(ta[xq[i, c]])) * Fraction(float(tb[wq[j, c]])) *
+                          Fraction(float(xs[i, c // bs])) * Fraction(float(ws[j, c // bs])))
+            assert abs(Fraction(float(ref[i, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 300)
+            assert rows[i * n + j] == pytest.approx(float(exact), rel=2.0 ** -45, abs=1e-300)
+            assert at[i * n + j] >= abs(_bf16_value(bias[j]))
+
+
+def test_gemm_zero_codes_return_the_bias():
+    bias = np.array([0x3F80, 0xC040, 0x0000, 0x8000, 0x4B00], dtype=np.uint16)  # 1, -3, 0, -0, 2^23
+    xq = np.zeros((3, 96), np.uint8)
+    wq = np.zeros((5, 96), np.uint8)
+    xs, ws = np.ones((3, 3), np.float32), np.ones((5, 3), np.float32)
+    ref = B.gemm_blockscaled(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, 32, bias=bias)
+    assert np.array_equal(ref, np.tile([1.0, -3.0, 0.0, 0.0, 2.0 ** 23], (3, 1)))
