@@ -408,29 +408,32 @@ constexpr int kColVecs = 32;
 constexpr int kColRows = kColChunkRows;
 constexpr int kColPer = kColRows / 8;  // vectors per thread
 
+// The thread's kColPer vectors of its tile (rows r0 + ty + 8j of vector column
+// vc). Rows past the end reload the chunk's first row (a real element of the
+// same column, so it cannot change the column max; its codes are not stored).
 template <int XT>
-__global__ __launch_bounds__(kBlock) void colmax_partials_kernel(const uint4* __restrict__ x, int rows, int vpr,
-                                                                 uint32_t* __restrict__ partial) {
+__device__ __forceinline__ void col_tile_load(const uint4* __restrict__ x, int rows, int vpr, int r0, int vc, int ty,
+                                              uint4 (&v)[kColPer]) {
+#pragma unroll
+  for (int j = 0; j < kColPer; ++j) {
+    const int r = r0 + ty + 8 * j;
+    v[j] = x[(size_t)(r < rows ? r : r0) * vpr + vc];
+  }
+}
+
+// Column maxima of the tile: the thread's kColPer rows go into
+// tile[ty][tx * E + e] (finite max in bits 0..30, non-finite seen in bit 31).
+// Raw maxima first (bf16: two 16-bit magnitudes per max); the finite-only pass
+// runs only where a raw max is Inf/NaN. Ends with a block barrier.
+template <int XT>
+__device__ __forceinline__ void col_tile_maxima(const uint4 (&v)[kColPer], bool valid, int tx, int ty,
+                                                uint32_t (*tile)[kColVecs * VecTraits<XT>::kElems]) {
   constexpr int E = VecTraits<XT>::kElems;
-  __shared__ uint32_t tile[8][kColVecs * E];
-  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
-  const int vc = blockIdx.x * kColVecs + tx;
-  const int r0 = blockIdx.y * kColRows;
   uint32_t m[E];
   uint32_t nf = 0;  // bit e: column e of this vector saw an Inf/NaN
 #pragma unroll
   for (int e = 0; e < E; ++e) m[e] = 0;
-  if (vc < vpr) {
-    // rows past the end reload the chunk's first row (a real element of the
-    // same column, so it cannot change the column max)
-    uint4 v[kColPer];
-#pragma unroll
-    for (int j = 0; j < kColPer; ++j) {
-      const int r = r0 + ty + 8 * j;
-      v[j] = x[(size_t)(r < rows ? r : r0) * vpr + vc];
-    }
-    // raw maxima first (bf16: two 16-bit magnitudes per max); the finite-only
-    // pass runs only where a raw max is Inf/NaN
+  if (valid) {
     uint32_t any_nf = 0;
     if constexpr (XT == kBF16) {
       typedef unsigned short us2 __attribute__((ext_vector_type(2)));
@@ -468,66 +471,63 @@ __global__ __launch_bounds__(kBlock) void colmax_partials_kernel(const uint4* __
       }
     }
   }
-  // finite max in bits 0..30, non-finite seen in bit 31
 #pragma unroll
   for (int e = 0; e < E; ++e) tile[ty][tx * E + e] = m[e] | (((nf >> e) & 1u) ? kNonfiniteBit : 0u);
   __syncthreads();
-  for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
-    uint32_t acc = 0, flag = 0;
-#pragma unroll
-    for (int l = 0; l < 8; ++l) {
-      acc = max(acc, tile[l][c] & ~kNonfiniteBit);
-      flag |= tile[l][c] & kNonfiniteBit;
-    }
-    const int col = blockIdx.x * kColVecs * E + c;
-    if (col < vpr * E) partial[(size_t)blockIdx.y * vpr * E + col] = acc | flag;
-  }
 }
 
-template <int XT, int FMT, bool SR>
-__global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restrict__ x, int rows, int vpr,
-                                                            const uint32_t* __restrict__ partial, int nchunk,
-                                                            uint8_t* __restrict__ q, float* __restrict__ scale,
-                                                            float* __restrict__ amax_out, SrSeed sd) {
-  constexpr int E = VecTraits<XT>::kElems;
-  __shared__ float rcp[kColVecs * E];
-  __shared__ uint32_t flags[kColVecs * E];
-  const int cols = vpr * E;
-  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
-  const int vc = blockIdx.x * kColVecs + tx;
-  const int r0 = blockIdx.y * kColRows;
-  // the chunk's input loads go out first; the column scales are folded while
-  // they are in flight
-  uint4 v[kColPer];
-  if (vc < vpr) {
+// Partial word of tile column c: the 8 row lanes folded.
+template <int E>
+__device__ __forceinline__ uint32_t col_tile_word(uint32_t (*tile)[kColVecs * E], int c) {
+  uint32_t acc = 0, flag = 0;
 #pragma unroll
-    for (int j = 0; j < kColPer; ++j) {
-      const int r = r0 + ty + 8 * j;
-      v[j] = x[(size_t)(r < rows ? r : r0) * vpr + vc];
+  for (int l = 0; l < 8; ++l) {
+    acc = max(acc, tile[l][c] & ~kNonfiniteBit);
+    flag |= tile[l][c] & kNonfiniteBit;
+  }
+  return acc | flag;
+}
+
+// Fold column `col`'s nchunk partial words (8 loads in flight per round); ATOMIC
+// reads them with device-scope loads (written by other blocks of this launch).
+template <bool ATOMIC>
+__device__ __forceinline__ uint32_t col_fold_partials(const uint32_t* partial, int nchunk, int cols, int col) {
+  auto ld = [&](int k) -> uint32_t {
+    const uint32_t* p = partial + (size_t)k * cols + col;
+    if constexpr (ATOMIC) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+  };
+  uint32_t acc = 0, flag = 0;
+  int k = 0;
+  for (; k + 8 <= nchunk; k += 8) {
+    uint32_t p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = ld(k + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc = max(acc, p[u] & ~kNonfiniteBit);
+      flag |= p[u] & kNonfiniteBit;
     }
   }
+  for (; k < nchunk; ++k) {
+    const uint32_t p = ld(k);
+    acc = max(acc, p & ~kNonfiniteBit);
+    flag |= p & kNonfiniteBit;
+  }
+  return acc | flag;
+}
+
+// The tile's column scales from their folded words: rcp and flags in LDS, the
+// scales and amax written by the blocks of row chunk 0. Ends with a block barrier.
+template <int FMT, int E, bool ATOMIC>
+__device__ __forceinline__ void col_tile_scales(const uint32_t* partial, int nchunk, int cols, float* __restrict__ scale,
+                                                float* __restrict__ amax_out, float* rcp, uint32_t* flags) {
   for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
     const int col = blockIdx.x * kColVecs * E + c;
-    uint32_t acc = 0, flag = 0;
+    uint32_t word = 0;
     if (col < cols) {
-      // 8 independent partial loads in flight per round
-      int k = 0;
-      for (; k + 8 <= nchunk; k += 8) {
-        uint32_t p[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) p[u] = partial[(size_t)(k + u) * cols + col];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          acc = max(acc, p[u] & ~kNonfiniteBit);
-          flag |= p[u] & kNonfiniteBit;
-        }
-      }
-      for (; k < nchunk; ++k) {
-        const uint32_t p = partial[(size_t)k * cols + col];
-        acc = max(acc, p & ~kNonfiniteBit);
-        flag |= p & kNonfiniteBit;
-      }
-      const float amax = __uint_as_float(acc);
+      word = col_fold_partials<ATOMIC>(partial, nchunk, cols, col);
+      const float amax = __uint_as_float(word & ~kNonfiniteBit);
       const float s = scale_from_amax<FMT>(amax);
       rcp[c] = 1.0f / s;
       if (blockIdx.y == 0) {
@@ -537,10 +537,17 @@ __global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restr
     } else {
       rcp[c] = 0.0f;
     }
-    flags[c] = flag;
+    flags[c] = word & kNonfiniteBit;
   }
   __syncthreads();
-  if (vc >= vpr) return;
+}
+
+// Cast the thread's kColPer vectors with their columns' reciprocals.
+template <int XT, int FMT, bool SR>
+__device__ __forceinline__ void col_tile_cast(const uint4 (&v)[kColPer], int rows, int vpr, int r0, int vc, int tx,
+                                              int ty, const float* rcp, const uint32_t* flags, uint8_t* __restrict__ q,
+                                              SrSeed sd) {
+  constexpr int E = VecTraits<XT>::kElems;
   bool patch = false;
   float r[E];
 #pragma unroll
@@ -566,9 +573,123 @@ __global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restr
         if (patch) w[d] = patch_nan4(w[d], a, b, c, e);
       }
     }
-    uint8_t* dst = q + ((size_t)row * vpr + vc) * E;
-    store_codes<E>(dst, w);
+    store_codes<E>(q + ((size_t)row * vpr + vc) * E, w);
   }
+}
+
+template <int XT>
+__global__ __launch_bounds__(kBlock) void colmax_partials_kernel(const uint4* __restrict__ x, int rows, int vpr,
+                                                                 uint32_t* __restrict__ partial) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t tile[8][kColVecs * E];
+  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
+  const int vc = blockIdx.x * kColVecs + tx;
+  const int r0 = blockIdx.y * kColRows;
+  uint4 v[kColPer];
+  if (vc < vpr) col_tile_load<XT>(x, rows, vpr, r0, vc, ty, v);
+  col_tile_maxima<XT>(v, vc < vpr, tx, ty, tile);
+  for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
+    const int col = blockIdx.x * kColVecs * E + c;
+    if (col < vpr * E) partial[(size_t)blockIdx.y * vpr * E + col] = col_tile_word<E>(tile, c);
+  }
+}
+
+template <int XT, int FMT, bool SR>
+__global__ __launch_bounds__(kBlock) void quant_cols_kernel(const uint4* __restrict__ x, int rows, int vpr,
+                                                            const uint32_t* __restrict__ partial, int nchunk,
+                                                            uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                            float* __restrict__ amax_out, SrSeed sd) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ float rcp[kColVecs * E];
+  __shared__ uint32_t flags[kColVecs * E];
+  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
+  const int vc = blockIdx.x * kColVecs + tx;
+  const int r0 = blockIdx.y * kColRows;
+  // the chunk's input loads go out first; the column scales are folded while
+  // they are in flight
+  uint4 v[kColPer];
+  if (vc < vpr) col_tile_load<XT>(x, rows, vpr, r0, vc, ty, v);
+  col_tile_scales<FMT, E, false>(partial, nchunk, vpr * E, scale, amax_out, rcp, flags);
+  if (vc >= vpr) return;
+  col_tile_cast<XT, FMT, SR>(v, rows, vpr, r0, vc, tx, ty, rcp, flags, q, sd);
+}
+
+// Per column in one pass: the same tiles, held in registers while the grid
+// agrees on the column maxima. Each block stores its tile's column partials
+// (device-scope atomic stores, then s_waitcnt), the block counts in through the
+// arrival tree, the last arrival advances the generation half of the barrier
+// word and the others poll it (as in quant_tensor_fused_kernel; same residency
+// condition and bounded poll). Then every block folds its own columns'
+// partials from all row chunks, with device-scope loads, and casts.
+template <int XT, int FMT, bool SR>
+__global__ __launch_bounds__(kBlock) void quant_cols_fused_kernel(const uint4* __restrict__ x, int rows, int vpr,
+                                                                  uint32_t* partial, uint32_t* arrivals, uint32_t* bar,
+                                                                  uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                                  float* __restrict__ amax_out, SrSeed sd) {
+  constexpr int E = VecTraits<XT>::kElems;
+  __shared__ uint32_t tile[8][kColVecs * E];
+  __shared__ float rcp[kColVecs * E];
+  __shared__ uint32_t flags[kColVecs * E];
+  __shared__ uint32_t sh[2];  // generation at the start; 1 when the wait gave up
+  uint64_t* word = reinterpret_cast<uint64_t*>(bar + kBarGen);
+  const int tx = threadIdx.x % kColVecs, ty = threadIdx.x / kColVecs;
+  const int vc = blockIdx.x * kColVecs + tx;
+  const int r0 = blockIdx.y * kColRows;
+  const int cols = vpr * E;
+  if (threadIdx.x == 0)
+    sh[0] = (uint32_t)(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
+  uint4 v[kColPer];
+  if (vc < vpr) col_tile_load<XT>(x, rows, vpr, r0, vc, ty, v);
+  col_tile_maxima<XT>(v, vc < vpr, tx, ty, tile);
+  for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
+    const int col = blockIdx.x * kColVecs * E + c;
+    if (col < cols)
+      __hip_atomic_store(partial + (size_t)blockIdx.y * cols + col, col_tile_word<E>(tile, c), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t g0 = sh[0];
+    const uint32_t nblocks = gridDim.x * gridDim.y;
+    const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
+    const uint32_t groups = min(nblocks, (uint32_t)kArrivalGroups);
+    const uint32_t g = b % groups;
+    const uint32_t members = (nblocks - g + groups - 1) / groups;
+    uint32_t* sub = arrivals + g * kArrivalStride;
+    bool last = false;
+    if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+      __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __hip_atomic_fetch_add(bar + kBarTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    }
+    uint32_t gave_up = 0;
+    if (last) {
+      __hip_atomic_store(bar + kBarTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word, (uint64_t)(g0 + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while ((uint32_t)(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) == g0) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierSpinTicks) {
+          gave_up = 1u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    sh[1] = gave_up;
+  }
+  __syncthreads();
+  if (sh[1]) {
+    // the wait gave up: report NaN scales for this tile's columns instead of codes
+    for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
+      const int col = blockIdx.x * kColVecs * E + c;
+      if (col < cols) scale[col] = __uint_as_float(0x7fc00000u);
+    }
+    return;
+  }
+  col_tile_scales<FMT, E, true>(partial, gridDim.y, cols, scale, amax_out, rcp, flags);
+  if (vc >= vpr) return;
+  col_tile_cast<XT, FMT, SR>(v, rows, vpr, r0, vc, tx, ty, rcp, flags, q, sd);
 }
 
 // ---------------------------------------------------------------------------
@@ -926,6 +1047,28 @@ hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uin
 #undef CALL
 }
 
+// Blocks of the single-pass per-column kernel one device holds at once.
+template <int XT, int FMT, bool SR>
+static int cols_fused_capacity() {
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_cols_fused_kernel<XT, FMT, SR>, kBlock, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      n = 0;
+    }
+    per_cu = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return per_cu * cus;
+}
+
 hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
                              float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st) {
   const int vpr = xt == kBF16 ? cols / 8 : cols / 4;
@@ -935,10 +1078,17 @@ hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt,
   uint32_t* partial = static_cast<uint32_t*>(ws) + kTensorWorkspaceBytes / 4;
   const uint4* xv = static_cast<const uint4*>(x);
   const SrSeed sd = sr_seed(seed);
-#define CALL(A, B, S)                                                                               \
-  hipLaunchKernelGGL((colmax_partials_kernel<A>), grid, dim3(kBlock), 0, st, xv, rows, vpr, partial); \
-  hipLaunchKernelGGL((quant_cols_kernel<A, B, S>), grid, dim3(kBlock), 0, st, xv, rows, vpr,        \
-                     (const uint32_t*)partial, (int)grid.y, q, scale, amax, sd);                    \
+  uint32_t* region = static_cast<uint32_t*>(ws);
+  const bool one_pass = (size_t)grid.x * grid.y <= (size_t)kFusedBlocks;
+#define CALL(A, B, S)                                                                                       \
+  if (one_pass && (int)(grid.x * grid.y) <= cols_fused_capacity<A, B, S>()) {                               \
+    hipLaunchKernelGGL((quant_cols_fused_kernel<A, B, S>), grid, dim3(kBlock), 0, st, xv, rows, vpr, partial, \
+                       region + kArrivalOffsetWords, region + kBarrierOffsetWords, q, scale, amax, sd);      \
+    return hipGetLastError();                                                                               \
+  }                                                                                                         \
+  hipLaunchKernelGGL((colmax_partials_kernel<A>), grid, dim3(kBlock), 0, st, xv, rows, vpr, partial);        \
+  hipLaunchKernelGGL((quant_cols_kernel<A, B, S>), grid, dim3(kBlock), 0, st, xv, rows, vpr,               \
+                     (const uint32_t*)partial, (int)grid.y, q, scale, amax, sd);                           \
   return hipGetLastError()
   HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL

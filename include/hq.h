@@ -121,9 +121,11 @@ size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
  *              barrier of the single-pass per-tensor kernel) start from zero,
  *              and every call leaves them ready for the next. Calls that share
  *              a workspace must not run concurrently. Dynamic per-tensor
- *              quantization of up to 2^24 bf16 (2^23 float32) elements runs as
- *              one pass over x, whose blocks agree on the amax through the
- *              workspace; larger tensors take a partial-max pass first.
+ *              quantization of up to 2^24 bf16 (2^23 float32) elements, and
+ *              per-channel quantization whose tiles of 128 rows x 256 bf16
+ *              (128 float32) columns number at most 512, run as one pass over
+ *              x whose blocks agree on the maxima through the workspace;
+ *              other sizes take a partial-max pass first.
  * Requires cols % 16 == 0 (16-byte vector rows), 1 <= rows, cols < 2^31,
  * rows * cols < 2^40. rows == 0 returns HQ_OK without a launch. Outputs must not
  * overlap inputs. */

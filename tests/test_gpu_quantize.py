@@ -147,23 +147,33 @@ def test_repeated_calls_with_shared_workspace(hq):
                 assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
 
 
-def test_single_pass_per_tensor_barrier_state(hq):
+def test_single_pass_barrier_state(hq):
     """Dynamic per-tensor calls of up to 2^24 bf16 elements run as one pass whose
     blocks agree on the amax through the workspace. After every call the arrival
     counters and the top counter are back at zero; the 64-bit barrier word holds
     the number of single-pass calls so far in its high half and the last such
     call's amax bits in its low half. A tensor one row too large for the single
-    pass (two passes) and a delayed call in between leave the word alone."""
+    pass (two passes) and a delayed call in between leave the word alone. A
+    single-pass per-channel call (bf16, at most 512 tiles of 128 rows x 256
+    columns) advances the generation with an empty amax half; its column
+    partials follow the per-tensor region."""
     rng = np.random.default_rng(23)
-    region = hq.hq_quantize_workspace_bytes(Q.PER_TENSOR, 1, 16)
-    ws = torch.zeros(region, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(hq.hq_quantize_workspace_bytes(Q.PER_CHANNEL, 4096, 4096), dtype=torch.uint8, device="cuda")
     arrivals = slice(4096, 8192)        # 1024 partial words, then 32 arrival lines
     word_lo, word_hi, top = 2048, 2049, 2048 + 32  # uint32 indices of the barrier lines
     gen, last_amax = 0, 0
     ring, st, flag = hq.Ring(4), Q.ring_new(4), 0
-    steps = [(1, 16), (300, 1024), (4096, 4096), (4097, 4096), "delayed", (64, 2048), (4096, 4096), (1, 16)]
+    steps = [(1, 16), (300, 1024), (4096, 4096), (4097, 4096), "delayed", (64, 2048), ("col", 4096, 4096),
+             (4096, 4096), ("col", 300, 2048), (1, 16)]
     for t, sh in enumerate(steps):
-        if sh == "delayed":
+        if sh[0] == "col":
+            bits = workloads.random_bf16(rng, sh[1:], std=float(10.0 ** rng.integers(-2, 3)))
+            q, s, a = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, Q.PER_CHANNEL, workspace=ws)
+            q_ref, s_ref, a_ref = Q.quantize_dynamic(bits, Q.BF16, fp8.E4M3, Q.PER_CHANNEL)
+            assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32)), (t, sh)
+            assert np.array_equal(host(a).view(np.uint32), a_ref.view(np.uint32)), (t, sh)
+            gen, last_amax = gen + 1, 0
+        elif sh == "delayed":
             bits = workloads.random_bf16(rng, (128, 256))
             q, _, _ = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, Q.PER_TENSOR, ring=ring, ring_idx=0, workspace=ws)
             q_ref, _, _, st, flag = Q.quantize_delayed(bits, Q.BF16, fp8.E4M3, st, 0, 0, flag)
