@@ -23,6 +23,8 @@
 //
 // Partial maxima are stored as float32 magnitude bits in bits 0..30 with bit 31
 // set when the block saw a non-finite element.
+#include <atomic>
+
 #include "hq_device.h"
 #include "hq_launch.h"
 
@@ -981,7 +983,9 @@ hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt,
 // instantiation (its register use sets the occupancy; cached per process).
 template <int XT, int FMT, bool SR, int V>
 static int fused_capacity() {
-  static int per_cu = -1;
+  // cached per instantiation; concurrent first calls compute the same value
+  static std::atomic<int> cached{-1};
+  int per_cu = cached.load(std::memory_order_relaxed);
   if (per_cu < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_tensor_fused_kernel<XT, FMT, SR, V>, kBlock, 0) !=
@@ -990,6 +994,7 @@ static int fused_capacity() {
       n = 0;
     }
     per_cu = n;
+    cached.store(n, std::memory_order_relaxed);
   }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -1050,7 +1055,8 @@ hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uin
 // Blocks of the single-pass per-column kernel one device holds at once.
 template <int XT, int FMT, bool SR>
 static int cols_fused_capacity() {
-  static int per_cu = -1;
+  static std::atomic<int> cached{-1};
+  int per_cu = cached.load(std::memory_order_relaxed);
   if (per_cu < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_cols_fused_kernel<XT, FMT, SR>, kBlock, 0) !=
@@ -1059,6 +1065,7 @@ static int cols_fused_capacity() {
       n = 0;
     }
     per_cu = n;
+    cached.store(n, std::memory_order_relaxed);
   }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
