@@ -79,6 +79,8 @@ SIGNATURES = {
     "hq_gemm_a8w8_blockscaled": (_I, [_P, _I, _P, _I, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P]),
     "hq_quantize_fp8_layouts": (_I, [_P, _I, _I64, _I64, _I, _P, ctypes.POINTER(hq_ring), _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P]),
+    "hq_quantize_fp8_layouts_stochastic": (_I, [_P, _I, _I64, _I64, ctypes.c_uint64, _P, ctypes.POINTER(hq_ring), _P,
+                                                _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "hq_scale_ring_update": (_I, [ctypes.POINTER(hq_ring), _P, _I, _P]),
     "hq_preshuffled_bytes": (_I64, [_I64, _I64]),
     "hq_preshuffle_weight": (_I, [_P, _I64, _I64, _P, _P]),

@@ -17,7 +17,8 @@ from ._lib import (HQ_BF16, HQ_BIAS_BF16, HQ_E4M3, HQ_E5M2, HQ_F32, HQ_PER_CHANN
 
 __all__ = [
     "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
-    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_stochastic", "hq_quantize_fp8_blockwise",
+    "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_layouts_stochastic", "hq_quantize_fp8_stochastic",
+    "hq_quantize_fp8_blockwise",
     "hq_gemm_a8w8_blockscaled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_last_error",
@@ -188,6 +189,20 @@ def hq_quantize_fp8_layouts(x: torch.Tensor, fmt: int = HQ_E4M3, *, scale_in: to
     layouts in one pass. Each of q, q_t, q_pre, q_t_pre is False (skip), True
     (allocate) or a uint8 tensor to write. Returns a dict with the written
     layouts plus "scale" and "amax" (None with scale_in)."""
+    return _layouts(x, fmt, None, scale_in, ring, ring_idx, q, q_t, q_pre, q_t_pre, scale_out, amax_out, workspace,
+                    stream)
+
+
+def hq_quantize_fp8_layouts_stochastic(x: torch.Tensor, seed: int, *, scale_in: torch.Tensor | None = None,
+                                       ring: Ring | None = None, ring_idx: int = 0, q=False, q_t=False, q_pre=False,
+                                       q_t_pre=False, scale_out=None, amax_out=None, workspace=None, stream=None):
+    """hq_quantize_fp8_layouts with stochastic rounding to E5M2 keyed by `seed`."""
+    return _layouts(x, HQ_E5M2, int(seed) & (2 ** 64 - 1), scale_in, ring, ring_idx, q, q_t, q_pre, q_t_pre,
+                    scale_out, amax_out, workspace, stream)
+
+
+def _layouts(x, fmt, seed, scale_in, ring, ring_idx, q, q_t, q_pre, q_t_pre, scale_out, amax_out, workspace,
+             stream):
     if x.dtype not in _XT:
         raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
     if x.dim() != 2:
@@ -214,10 +229,13 @@ def hq_quantize_fp8_layouts(x: torch.Tensor, fmt: int = HQ_E4M3, *, scale_in: to
         workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ring_c = ctypes.byref(ring.c_struct(ring_idx)) if ring is not None else None
-    st = lib.hq_quantize_fp8_layouts(_ptr(x), _XT[x.dtype], rows, cols, fmt, _ptr(scale_in), ring_c,
-                                     _ptr(outs.get("q")), _ptr(outs.get("q_t")), _ptr(outs.get("q_pre")),
-                                     _ptr(outs.get("q_t_pre")), _ptr(scale_out), _ptr(amax_out), _ptr(workspace),
-                                     ws_bytes, _stream(dev, stream))
+    tail = (_ptr(outs.get("q")), _ptr(outs.get("q_t")), _ptr(outs.get("q_pre")), _ptr(outs.get("q_t_pre")),
+            _ptr(scale_out), _ptr(amax_out), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    if seed is None:
+        st = lib.hq_quantize_fp8_layouts(_ptr(x), _XT[x.dtype], rows, cols, fmt, _ptr(scale_in), ring_c, *tail)
+    else:
+        st = lib.hq_quantize_fp8_layouts_stochastic(_ptr(x), _XT[x.dtype], rows, cols, seed, _ptr(scale_in), ring_c,
+                                                    *tail)
     check(st)
     outs["scale"] = scale_out
     outs["amax"] = amax_out

@@ -230,10 +230,10 @@ static hq_status quantize_impl(const void* x, int xt, int64_t rows, int64_t cols
   return launched(e, name);
 }
 
-hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t cols, int fmt, const float* scale_in,
-                                  const hq_ring* ring, uint8_t* q, uint8_t* q_t, uint8_t* q_pre, uint8_t* q_t_pre,
-                                  float* scale_out, float* amax_out, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream) {
+static hq_status layouts_impl(const void* x, int xt, int64_t rows, int64_t cols, int fmt, const float* scale_in,
+                              const hq_ring* ring, uint8_t* q, uint8_t* q_t, uint8_t* q_pre, uint8_t* q_t_pre,
+                              float* scale_out, float* amax_out, void* workspace, size_t workspace_bytes, bool sr,
+                              uint64_t seed, hipStream_t stream, const char* name) {
   if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
   if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
@@ -294,8 +294,24 @@ hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t c
   return launched(hq::launch_quant_layouts(x, xt, (int)rows, (int)cols, fmt, o, scale_in, scale_out, amax_out,
                                            ring ? ring->state : nullptr, ring ? ring->len : 0, ring ? ring->idx : 0,
                                            ring ? ring->margin : 0, ring ? ring->nonfinite_flag : nullptr, workspace,
-                                           stream),
-                  "hq_quantize_fp8_layouts");
+                                           sr, seed, stream),
+                  name);
+}
+
+hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t cols, int fmt, const float* scale_in,
+                                  const hq_ring* ring, uint8_t* q, uint8_t* q_t, uint8_t* q_pre, uint8_t* q_t_pre,
+                                  float* scale_out, float* amax_out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  return layouts_impl(x, xt, rows, cols, fmt, scale_in, ring, q, q_t, q_pre, q_t_pre, scale_out, amax_out, workspace,
+                      workspace_bytes, false, 0, stream, "hq_quantize_fp8_layouts");
+}
+
+hq_status hq_quantize_fp8_layouts_stochastic(const void* x, int xt, int64_t rows, int64_t cols, uint64_t seed,
+                                             const float* scale_in, const hq_ring* ring, uint8_t* q, uint8_t* q_t,
+                                             uint8_t* q_pre, uint8_t* q_t_pre, float* scale_out, float* amax_out,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return layouts_impl(x, xt, rows, cols, HQ_E5M2, scale_in, ring, q, q_t, q_pre, q_t_pre, scale_out, amax_out,
+                      workspace, workspace_bytes, true, seed, stream, "hq_quantize_fp8_layouts_stochastic");
 }
 
 hq_status hq_quantize_fp8_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int fmt, int block_size,

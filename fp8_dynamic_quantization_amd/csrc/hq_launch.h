@@ -55,7 +55,7 @@ struct LayoutOut {
 // (a partial-amax pass first, partials in ws).
 hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int fmt, const LayoutOut& o,
                                 const float* scale_in, float* scale_out, float* amax, float* state, int len, int idx,
-                                int margin, int32_t* flag, void* ws, hipStream_t st);
+                                int margin, int32_t* flag, void* ws, bool sr, uint64_t seed, hipStream_t st);
 hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_t* flag, const float* amax,
                               int fmt, hipStream_t st);
 

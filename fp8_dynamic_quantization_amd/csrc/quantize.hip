@@ -854,12 +854,12 @@ __device__ __forceinline__ size_t preshuffled_offset(int n, int k, int kblocks) 
 
 enum { kScaleGiven = 0, kScaleRing = 1, kScaleDynamic = 2 };
 
-template <int XT, int FMT, int MODE>
+template <int XT, int FMT, int MODE, bool SR>
 __global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
     const uint4* __restrict__ x, int rows, int cols, LayoutOut o, const float* __restrict__ scale_in,
     const uint32_t* __restrict__ dyn_partial, int ndyn, float* __restrict__ scale_out,
     float* __restrict__ amax_out, float* state, int len, int idx, int margin, int32_t* flag, uint32_t* partial,
-    uint32_t* arrivals) {
+    uint32_t* arrivals, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   constexpr int VPC = 8 / E;  // 16-byte vectors per 8 columns
   __shared__ uint32_t red[kBlock / 64];
@@ -899,7 +899,9 @@ __global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
         const uint32_t m = vec_absmax_raw<XT>(v[j][u]);
         raw = max(raw, m);
         fin = max(fin, m < kInfBits ? m : vec_absmax_finite<XT>(v[j][u]));
-        vec_cast_checked<XT, FMT>(v[j][u], r, m, w + u * (E / 4));
+        // stochastic rounding keys on the element's row-major index in x, so
+        // every layout of an element gets the same code
+        cast_vec<XT, FMT, SR>(v[j][u], r, m, w + u * (E / 4), sd, (size_t)(r0 + j) * cols + c0 + u * E);
       }
       c[j] = make_uint2(w[0], w[1]);
     }
@@ -1119,13 +1121,14 @@ hipError_t launch_quant_delayed(const void* x, int xt, size_t numel, int fmt, ui
 
 hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int fmt, const LayoutOut& o,
                                 const float* scale_in, float* scale_out, float* amax, float* state, int len, int idx,
-                                int margin, int32_t* flag, void* ws, hipStream_t st) {
+                                int margin, int32_t* flag, void* ws, bool sr, uint64_t seed, hipStream_t st) {
   const int tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
   const dim3 grid(min(tiles, kMaxTensorPartials)), block(kBlock);
   const uint4* xv = static_cast<const uint4*>(x);
   uint32_t* partial = static_cast<uint32_t*>(ws);
   uint32_t* arrivals = partial ? partial + kArrivalOffsetWords : nullptr;
   const int mode = scale_in ? kScaleGiven : (state ? kScaleRing : kScaleDynamic);
+  const SrSeed sd = sr_seed(seed);
   int ndyn = 0;
   if (mode == kScaleDynamic) {
     const size_t nvec = (size_t)rows * cols / (xt == kBF16 ? 8 : 4);
@@ -1135,21 +1138,21 @@ hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int f
     else
       hipLaunchKernelGGL((amax_partials_kernel<kF32>), dim3(ndyn), dim3(kBlock), 0, st, xv, nvec, partial);
   }
-#define CALL(A, B, S_UNUSED)                                                                                  \
+#define CALL(A, B, S)                                                                                  \
   do {                                                                                                       \
     if (mode == kScaleGiven)                                                                                 \
-      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleGiven>), grid, block, 0, st, xv, rows, cols, o,    \
-                         scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals); \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleGiven, S>), grid, block, 0, st, xv, rows, cols, o,    \
+                         scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals, sd); \
     else if (mode == kScaleRing)                                                                             \
-      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleRing>), grid, block, 0, st, xv, rows, cols, o,     \
-                         scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals); \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleRing, S>), grid, block, 0, st, xv, rows, cols, o,     \
+                         scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals, sd); \
     else                                                                                                     \
-      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleDynamic>), grid, block, 0, st, xv, rows, cols, o,  \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleDynamic, S>), grid, block, 0, st, xv, rows, cols, o,  \
                          scale_in, partial, ndyn, scale_out, amax, state, len, idx, margin, flag, partial,    \
-                         arrivals);                                                                          \
+                         arrivals, sd);                                                                      \
     return hipGetLastError();                                                                                \
   } while (0)
-  HQ_DISPATCH_XT_FMT(xt, fmt, CALL);
+  HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
 }
 

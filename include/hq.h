@@ -191,6 +191,20 @@ hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t c
                                   float* scale_out, float* amax_out,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The layouts call with stochastic rounding to E5M2 (hip-quant README,
+ * "Stochastic E5M2 Backward Gradients": a gradient is the tensor rounded
+ * stochastically, and the backward pass needs it row-major for one GEMM and
+ * transposed for the other). Codes are those of hq_quantize_fp8_stochastic:
+ * element (r, c) of x draws from its row-major index r * cols + c, so every
+ * layout of an element carries the same code, and with a dynamic scale the
+ * row-major codes equal hq_quantize_fp8_stochastic's per-tensor codes for the
+ * same seed. Other arguments, the scale modes and the requirements are those
+ * of hq_quantize_fp8_layouts with fmt = HQ_E5M2. */
+hq_status hq_quantize_fp8_layouts_stochastic(const void* x, int xt, int64_t rows, int64_t cols, uint64_t seed,
+                                             const float* scale_in, const hq_ring* ring, uint8_t* q, uint8_t* q_t,
+                                             uint8_t* q_pre, uint8_t* q_t_pre, float* scale_out, float* amax_out,
+                                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Block-wise FP8 quantization (hip-quant README, "Block-wise FP8 Scaling"):
  * FP8 codes plus one float32 dequant scale per block of block_size consecutive
  * elements along each row, value ~= code * block_scale. Each block follows the

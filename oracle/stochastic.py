@@ -117,3 +117,16 @@ def quantize_delayed_stochastic(x: np.ndarray, dtype: int, state: np.ndarray, id
     amax, nonfinite = Q.group_amax(x32, Q.PER_TENSOR)
     new_state, new_flag = Q.ring_update(st, idx, margin, amax[0], bool(nonfinite[0]), fp8.E5M2, flag)
     return q, np.array([s_t], dtype=np.float32), amax, new_state, new_flag
+
+
+def quantize_with_scale_stochastic(x: np.ndarray, dtype: int, s, seed: int):
+    """Given-scale E5M2 quantization with stochastic rounding (the given-scale
+    mode of the fused layouts, reading R18, with the cast of reading S2):
+    y = fl32(x * fl32(1/s)), element i draws u from its row-major index.
+    Returns (q, s as float32 [1])."""
+    x32 = Q.widen(x, dtype)
+    s = np.asarray(s, dtype=np.float32).reshape(1)
+    r = Q.reciprocal(s)
+    y = (x32 * r[0]).astype(np.float32)
+    u = uniforms(seed, np.arange(y.size, dtype=np.uint64)).reshape(y.shape)
+    return encode_e5m2_stochastic(y, u), s

@@ -416,3 +416,18 @@ def test_gemm_blockscaled_valid_calls_reach_device_gate(hq):
     # the two inputs may share memory (same codes for X and W)
     assert hq.load().hq_gemm_a8w8_blockscaled(fake(0), 0, fake(0), 0, fake(2), fake(2), 32, 64, 64, 256, None,
                                               fake(4), None) == U
+
+
+def test_layouts_stochastic_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    lib = hq.load()
+
+    def call(rows=64, cols=128, q_t=None, scale_in=None, ws=fake(4), wsb=1 << 20):
+        return lib.hq_quantize_fp8_layouts_stochastic(fake(0), 1, rows, cols, 2 ** 64 - 1, scale_in, None, fake(1),
+                                                      q_t, None, None, fake(2), None, ws, wsb, None)
+    assert call(cols=24) == E
+    assert call(rows=40, q_t=fake(3)) == E               # transposed output needs rows % 16 == 0
+    assert call(wsb=16) == E                             # dynamic scale needs the workspace
+    if not _gpu_visible():
+        assert call() == hq.HQ_ERR_UNSUPPORTED_DEVICE
+        assert call(scale_in=fake(5), ws=None, wsb=0) == hq.HQ_ERR_UNSUPPORTED_DEVICE

@@ -149,3 +149,58 @@ def test_training_backward_operands_fused(hq):
     check_gemm(host(dx), gq, fp8.E5M2, wt, fp8.E5M2, gs, sw, pairs=pairs)
     pairs = np.stack([rng.integers(0, n, 4000), rng.integers(0, k, 4000)], axis=1)
     check_gemm(host(dw), gt, fp8.E5M2, xt, fp8.E5M2, gs, sx, pairs=pairs)
+
+
+# ---- stochastic rounding (E5M2) -----------------------------------------------------
+
+from oracle import stochastic as S  # noqa: E402
+
+
+@pytest.mark.parametrize("shape", [(64, 128), (144, 4112), (1040, 272)])
+@pytest.mark.parametrize("dtype", [Q.BF16, Q.F32])
+def test_stochastic_dynamic_all_layouts(hq, shape, dtype):
+    """Dynamic scale: every layout carries the oracle's stochastic codes (drawn
+    from the row-major index of x), equal to hq_quantize_fp8_stochastic's
+    per-tensor codes for the same seed."""
+    rng = np.random.default_rng(shape[0] + shape[1] + dtype + 1000)
+    x, xd = _input(rng, shape, dtype)
+    seed = 0xC0FFEE + shape[0]
+    out = hq.hq_quantize_fp8_layouts_stochastic(xd, seed, **ALL)
+    q2, s2, _ = hq.hq_quantize_fp8_stochastic(xd, Q.PER_TENSOR, seed)
+    torch.cuda.synchronize()
+    q_ref, s_ref, a_ref = S.quantize_stochastic(x, dtype, Q.PER_TENSOR, seed)
+    _check_layouts(out, q_ref)
+    assert np.array_equal(host(q2), q_ref)
+    assert host(out["scale"]).view(np.uint32)[0] == s_ref.view(np.uint32)[0]
+    assert host(out["amax"]).view(np.uint32)[0] == a_ref.view(np.uint32)[0]
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (256, 384)])
+def test_stochastic_given_scale_all_layouts(hq, shape):
+    rng = np.random.default_rng(shape[0] * 3 + shape[1])
+    x, xd = _input(rng, shape, Q.BF16)
+    s = np.float32(np.abs(Q.widen(x, Q.BF16)).max() / fp8.fmax(fp8.E5M2) / 3.0)
+    out = hq.hq_quantize_fp8_layouts_stochastic(xd, 2 ** 63 + 11, scale_in=dev_f32(np.array([s])), **ALL)
+    torch.cuda.synchronize()
+    q_ref, s_ref = S.quantize_with_scale_stochastic(x, Q.BF16, s, 2 ** 63 + 11)
+    _check_layouts(out, q_ref)
+    assert host(out["scale"]).view(np.uint32)[0] == s_ref.view(np.uint32)[0]
+
+
+def test_stochastic_ring_sequence(hq):
+    """Delayed (ring) steps, one with a NaN: codes in every layout, the scale
+    used and the ring state match the oracle after each step."""
+    rng = np.random.default_rng(77)
+    ring = hq.Ring(4, margin=1)
+    st, flag = Q.ring_new(4), 0
+    for t in range(5):
+        x = (rng.standard_normal((128, 256)) * np.exp(rng.standard_normal())).astype(np.float32)
+        if t == 2:
+            x[3, 9] = np.nan
+        out = hq.hq_quantize_fp8_layouts_stochastic(dev_f32(x), 1234 + t, ring=ring, ring_idx=t % 4, **ALL)
+        torch.cuda.synchronize()
+        q_ref, s_ref, a_ref, st, flag = S.quantize_delayed_stochastic(x, Q.F32, st, t % 4, 1, 1234 + t, flag)
+        _check_layouts(out, q_ref)
+        assert host(out["scale"]).view(np.uint32)[0] == s_ref.view(np.uint32)[0]
+        assert np.array_equal(host(ring.state).view(np.uint32), st.view(np.uint32)), t
+        assert int(host(ring.flag)[0]) == flag

@@ -103,3 +103,31 @@ def test_scales_equal_deterministic_quantization(gran):
     mags = np.unique(t[(t >= 0) & np.isfinite(t)])
     step = np.abs(np.searchsorted(mags, np.abs(t[q])) - np.searchsorted(mags, np.abs(t[q_d])))
     assert step.max() <= 1 and (step == 1).any()
+
+
+def test_given_scale_stochastic_with_the_dynamic_scale_is_the_dynamic_stochastic():
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal((12, 64)) * 3).astype(np.float32)
+    q_dyn, s_dyn, _ = S.quantize_stochastic(x, Q.F32, Q.PER_TENSOR, seed=99)
+    q_giv, s_giv = S.quantize_with_scale_stochastic(x, Q.F32, s_dyn, seed=99)
+    assert np.array_equal(q_giv, q_dyn) and s_giv[0] == s_dyn[0]
+
+
+def test_given_scale_stochastic_codes_neighbour_the_deterministic_ones():
+    """With a scale that saturates part of the tensor: saturated values keep
+    the saturated code, the rest lie at most one E5M2 step from round-to-nearest,
+    on the side of the exact value."""
+    rng = np.random.default_rng(62)
+    x = (rng.standard_normal((16, 128)) * 10).astype(np.float32)
+    s = np.float32(np.abs(x).max() / fp8.fmax(fp8.E5M2) / 4)
+    q_sr, _ = S.quantize_with_scale_stochastic(x, Q.F32, s, seed=7)
+    q_rn, _, _ = Q.quantize_with_scale(x, Q.F32, fp8.E5M2, s)
+    t = fp8.decode_table(fp8.E5M2)
+    y = (x * np.float32(np.float32(1) / s)).astype(np.float32).astype(np.float64)
+    d_sr, d_rn = t[q_sr], t[q_rn]
+    sat = np.abs(y) >= fp8.fmax(fp8.E5M2)
+    assert np.array_equal(q_sr[sat], q_rn[sat])
+    lo = np.minimum(d_sr, d_rn)[~sat]
+    hi = np.maximum(d_sr, d_rn)[~sat]
+    # both codes bracket y: the stochastic one is a neighbour of y, never farther
+    assert np.all((d_sr[~sat] == d_rn[~sat]) | ((lo <= y[~sat]) & (y[~sat] <= hi)))
