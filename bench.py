@@ -456,7 +456,22 @@ def training_linear_timings(torch, hq, lib, copies=12):
     out["quant_g_delayed_stochastic"] = {"shape": f"[{rows},{cols}] bf16 -> E5M2 (stochastic)",
                                          "us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
                                          "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del srcs, qs, rings
+    # the same, written row-major (dgrad) and transposed (wgrad) in one pass
+    # (hq_quantize_fp8_layouts_stochastic); algorithmic bytes: input + two codes
+    qts = [torch.empty((cols, rows), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+
+    def sllaunch(i, h):
+        st = lib.hq_quantize_fp8_layouts_stochastic(P(srcs[i % copies].data_ptr()), BF16, rows, cols, 1234 + i, None,
+                                                    ctypes.byref(ring_structs[i % copies]),
+                                                    P(qs[i % copies].data_ptr()), P(qts[i % copies].data_ptr()),
+                                                    None, None, P(so.data_ptr()), None, P(wsp.data_ptr()), wsb, h)
+        assert st == 0, hq.hq_last_error()
+    ms = time_graph(torch, sllaunch, 2 * copies)
+    alg = rows * cols * 4
+    out["layouts_g_e5m2_ring_q_and_qt_stochastic"] = {"shape": f"[{rows},{cols}] bf16", "us": round(ms * 1e3, 3),
+                                                      "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+                                                      "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del srcs, qs, qts, rings
 
     # GEMM operands (made once, untimed): E4M3 X, W for the forward; E5M2 G, W^T, G^T, X^T for the backward
     def quant(t, fmt):
