@@ -21,7 +21,7 @@ __all__ = [
     "hq_quantize_fp8_blockwise",
     "hq_gemm_a8w8_blockscaled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
-    "hq_grouped_gemm_a8w8", "hq_last_error",
+    "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_last_error",
 ]
 
 _XT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16}
@@ -354,4 +354,34 @@ def hq_grouped_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: in
                                       _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
                                       int(num_experts), t, n, k, _ptr(out),
                                       _stream(xq.device, stream)))
+    return out
+
+
+def hq_grouped_gemm_a8w8_epilogue(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
+                                  x_scale: torch.Tensor, w_scale: torch.Tensor, group_offsets: torch.Tensor,
+                                  num_experts: int, n: int, *, bias: torch.Tensor | None = None,
+                                  bias_type: int = HQ_BIAS_BF16, bias_scale: torch.Tensor | None = None,
+                                  out_scale: torch.Tensor | None = None, out_fmt: int = HQ_E4M3, out=None,
+                                  stream=None) -> torch.Tensor:
+    """hq_grouped_gemm_a8w8 with a per-expert bias [E, n] (bf16, or uint8 FP8
+    codes with bias_scale [E]) and bf16 output or, with out_scale, FP8 codes.
+    Returns out (bf16 or uint8 [T, n])."""
+    xq = xq.contiguous()
+    t, k = xq.shape
+    x_scale = x_scale.contiguous()
+    w_scale = w_scale.contiguous()
+    group_offsets = group_offsets.contiguous()
+    if bias is not None:
+        bias = bias.contiguous()
+    if bias_scale is not None:
+        bias_scale = bias_scale.contiguous()
+    if out is None:
+        out = torch.empty((t, n), dtype=torch.uint8 if out_scale is not None else torch.bfloat16, device=xq.device)
+    ep = hq_epilogue(0 if bias is None else bias.data_ptr(), int(bias_type),
+                     0 if bias_scale is None else bias_scale.data_ptr(),
+                     0 if out_scale is None else out_scale.data_ptr(), int(out_fmt))
+    check(load().hq_grouped_gemm_a8w8_epilogue(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                                               _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
+                                               int(num_experts), t, n, k, ctypes.byref(ep), _ptr(out),
+                                               _stream(xq.device, stream)))
     return out

@@ -433,7 +433,14 @@ __global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, cons
   const int row_end = min(s_sel[2], m0 + BM);
   const int tn = t % tiles_n;
   const float* ws = a.w_scale + (size_t)e * (a.w_scale_per_col ? a.n : 1);
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL>(a, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
+  // the epilogue's bias is per expert: [experts, n] values, and an FP8 bias has
+  // one bias scale per expert; the output scale is shared
+  GemmArgs ae = a;
+  if (a.bias) {
+    ae.bias = static_cast<const uint8_t*>(a.bias) + (size_t)e * a.n * (a.bias_kind == kBiasBF16 ? 2 : 1);
+    if (a.bias_scale) ae.bias_scale = a.bias_scale + e;
+  }
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL>(ae, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
 }
 
 // ---------------------------------------------------------------------------

@@ -387,6 +387,34 @@ hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k, uint8_t*
   return launched(hq::launch_preshuffle(wq, (int)n, (int)k, wq_pre, stream), "hq_preshuffle_weight");
 }
 
+// Epilogue arguments shared by the plain and grouped forms: bias kind, pointers
+// and the validation of their combination. Returns HQ_OK and fills the outputs.
+static hq_status epilogue_args(const hq_epilogue* ep, const void** bias, int* bias_kind, const float** bias_scale,
+                               const float** out_scale, int* out_fmt) {
+  *bias = ep ? ep->bias : nullptr;
+  *bias_scale = ep ? ep->bias_scale : nullptr;
+  *out_scale = ep ? ep->out_scale : nullptr;
+  *bias_kind = hq::kBiasNone;
+  *out_fmt = 0;
+  if (*bias) {
+    switch (ep->bias_type) {
+      case HQ_BIAS_BF16: *bias_kind = hq::kBiasBF16; break;
+      case HQ_BIAS_E4M3: *bias_kind = hq::kBiasE4M3; break;
+      case HQ_BIAS_E5M2: *bias_kind = hq::kBiasE5M2; break;
+      default: return fail(HQ_ERR_INVALID_ARGUMENT, "unknown bias_type %d", ep->bias_type);
+    }
+    if ((*bias_kind == hq::kBiasBF16) != (*bias_scale == nullptr))
+      return fail(HQ_ERR_INVALID_ARGUMENT, "an FP8 bias requires bias_scale and a bf16 bias takes none");
+  } else if (*bias_scale) {
+    return fail(HQ_ERR_INVALID_ARGUMENT, "bias_scale given without a bias");
+  }
+  if (*out_scale) {
+    if (!valid_fmt(ep->out_fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "out_fmt must be HQ_E4M3 or HQ_E5M2, got %d", ep->out_fmt);
+    *out_fmt = ep->out_fmt;
+  }
+  return HQ_OK;
+}
+
 static hq_status check_gemm_common(int xf, int wf, int64_t m, int64_t n, int64_t k) {
   if (!valid_fmt(xf) || !valid_fmt(wf)) return fail(HQ_ERR_INVALID_ARGUMENT, "xf and wf must be HQ_E4M3 or HQ_E5M2");
   if (m < 0 || m > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "m must be in [0, 2^31), got %lld", (long long)m);
@@ -425,24 +453,11 @@ hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre
     return fail(HQ_ERR_INVALID_ARGUMENT, "x_scale_count must be 1 or m (%lld), got %lld", (long long)m, (long long)x_scale_count);
   if (w_scale_count != 1 && w_scale_count != n)
     return fail(HQ_ERR_INVALID_ARGUMENT, "w_scale_count must be 1 or n (%lld), got %lld", (long long)n, (long long)w_scale_count);
-  const void* bias = ep ? ep->bias : nullptr;
-  const float* bias_scale = ep ? ep->bias_scale : nullptr;
-  const float* out_scale = ep ? ep->out_scale : nullptr;
-  int bias_kind = hq::kBiasNone;
-  if (bias) {
-    switch (ep->bias_type) {
-      case HQ_BIAS_BF16: bias_kind = hq::kBiasBF16; break;
-      case HQ_BIAS_E4M3: bias_kind = hq::kBiasE4M3; break;
-      case HQ_BIAS_E5M2: bias_kind = hq::kBiasE5M2; break;
-      default: return fail(HQ_ERR_INVALID_ARGUMENT, "unknown bias_type %d", ep->bias_type);
-    }
-    if ((bias_kind == hq::kBiasBF16) != (bias_scale == nullptr))
-      return fail(HQ_ERR_INVALID_ARGUMENT, "an FP8 bias requires bias_scale and a bf16 bias takes none");
-  } else if (bias_scale) {
-    return fail(HQ_ERR_INVALID_ARGUMENT, "bias_scale given without a bias");
-  }
-  if (out_scale && !valid_fmt(ep->out_fmt))
-    return fail(HQ_ERR_INVALID_ARGUMENT, "out_fmt must be HQ_E4M3 or HQ_E5M2, got %d", ep->out_fmt);
+  const void* bias;
+  int bias_kind, out_fmt;
+  const float *bias_scale, *out_scale;
+  st = epilogue_args(ep, &bias, &bias_kind, &bias_scale, &out_scale, &out_fmt);
+  if (st != HQ_OK) return st;
   if (m == 0 || n == 0) return ok();
   if (!xq || !wq_pre || !x_scale || !w_scale || !out)
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scale, w_scale and out must be non-NULL");
@@ -470,7 +485,7 @@ hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre
   st = check_device();
   if (st != HQ_OK) return st;
   hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1,
-                 bias, bias_kind, bias_scale, out_scale, out_scale ? ep->out_fmt : 0};
+                 bias, bias_kind, bias_scale, out_scale, out_fmt};
   (void)hipGetLastError();
   return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), "hq_gemm_a8w8");
 }
@@ -479,6 +494,15 @@ hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
                                int64_t x_scale_count, const float* w_scale, int64_t w_scale_count,
                                const int32_t* group_offsets, int32_t num_experts, int64_t total_rows, int64_t n,
                                int64_t k, uint16_t* out, hipStream_t stream) {
+  return hq_grouped_gemm_a8w8_epilogue(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count,
+                                       group_offsets, num_experts, total_rows, n, k, nullptr, out, stream);
+}
+
+hq_status hq_grouped_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                                        const float* x_scale, int64_t x_scale_count, const float* w_scale,
+                                        int64_t w_scale_count, const int32_t* group_offsets, int32_t num_experts,
+                                        int64_t total_rows, int64_t n, int64_t k, const hq_epilogue* ep, void* out,
+                                        hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, total_rows, n, k);
   if (st != HQ_OK) return st;
   if (num_experts < 1 || num_experts > 1024)
@@ -491,30 +515,42 @@ hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
                 (long long)w_scale_count);
   if ((double)((total_rows + 127) / 128 + num_experts) * (double)((n + 127) / 128) > 1.0e9)
     return fail(HQ_ERR_INVALID_ARGUMENT, "output too large for one launch");
+  const void* bias;
+  int bias_kind, out_fmt;
+  const float *bias_scale, *out_scale;
+  st = epilogue_args(ep, &bias, &bias_kind, &bias_scale, &out_scale, &out_fmt);
+  if (st != HQ_OK) return st;
   if (total_rows == 0 || n == 0) return ok();
   if (!xq || !wq_pre || !x_scale || !w_scale || !group_offsets || !out)
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scale, w_scale, group_offsets and out must be non-NULL");
   if (!aligned(xq, 16) || !aligned(wq_pre, 16) || !aligned(out, 16))
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre and out must be 16-byte aligned");
-  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(group_offsets, 4))
-    return fail(HQ_ERR_INVALID_ARGUMENT, "scales and group_offsets must be 4-byte aligned");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(group_offsets, 4) ||
+      (bias_scale && !aligned(bias_scale, 4)) || (out_scale && !aligned(out_scale, 4)) ||
+      (bias_kind == hq::kBiasBF16 && !aligned(bias, 2)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scales and group_offsets must be 4-byte aligned and a bf16 bias 2-byte aligned");
+  const size_t bias_bytes = bias ? (size_t)num_experts * (size_t)n * (bias_kind == hq::kBiasBF16 ? 2 : 1) : 0;
   const Range rg[] = {
-      {out, (size_t)total_rows * (size_t)n * 2, "out"},
+      {out, (size_t)total_rows * (size_t)n * (out_scale ? 1 : 2), "out"},
       {xq, (size_t)total_rows * (size_t)k, "xq"},
       {wq_pre, (size_t)padded_bytes(n, k) * (size_t)num_experts, "wq_pre"},
       {x_scale, (size_t)x_scale_count * 4, "x_scale"},
       {w_scale, (size_t)w_scale_count * 4, "w_scale"},
       {group_offsets, ((size_t)num_experts + 1) * 4, "group_offsets"},
+      {bias, bias_bytes, "bias"},
+      {bias_scale, bias_scale ? (size_t)num_experts * 4 : 0, "bias_scale"},
+      {out_scale, out_scale ? 4u : 0u, "out_scale"},
   };
   const char* other = nullptr;
-  const char* a = find_overlap(rg, 6, &other);
+  const char* a = find_overlap(rg, 9, &other);
   if (a && strcmp(a, "out") == 0) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
   st = check_device();
   if (st != HQ_OK) return st;
   hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)total_rows, (int)n, (int)k, x_scale_count != 1,
-                 w_scale_count != num_experts};
+                 w_scale_count != num_experts, bias, bias_kind, bias_scale, out_scale, out_fmt};
   (void)hipGetLastError();
-  return launched(hq::launch_grouped_gemm(g, group_offsets, num_experts, xf, wf, stream), "hq_grouped_gemm_a8w8");
+  return launched(hq::launch_grouped_gemm(g, group_offsets, num_experts, xf, wf, stream),
+                  ep ? "hq_grouped_gemm_a8w8_epilogue" : "hq_grouped_gemm_a8w8");
 }
 
 hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq, int wf, const float* x_scales,

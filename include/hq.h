@@ -369,6 +369,23 @@ hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
                                int64_t total_rows, int64_t n, int64_t k,
                                uint16_t* out, hipStream_t stream);
 
+/* hq_grouped_gemm_a8w8 with an epilogue (the hq_gemm_a8w8_epilogue arithmetic
+ * per row range; AstrAI ops.cu, linear_forward_fp8 for the bias and output
+ * options). Each expert has its own bias row:
+ *   ep->bias        device [num_experts, n]: expert e's rows add bias[e, :]
+ *                   (bf16 bits, or FP8 codes with a bias_scale)
+ *   ep->bias_scale  device float32 [num_experts], one per expert (FP8 bias)
+ *   ep->out_scale   device float32 [1], shared by every expert; the output is
+ *                   then uint8 codes [total_rows, n] in ep->out_fmt
+ * `ep` is a host pointer; NULL is exactly hq_grouped_gemm_a8w8. All other
+ * arguments and requirements are those of hq_grouped_gemm_a8w8. */
+hq_status hq_grouped_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre,
+                                        int wf, const float* x_scale, int64_t x_scale_count,
+                                        const float* w_scale, int64_t w_scale_count,
+                                        const int32_t* group_offsets, int32_t num_experts,
+                                        int64_t total_rows, int64_t n, int64_t k,
+                                        const hq_epilogue* ep, void* out, hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* hq_last_error(void);
 

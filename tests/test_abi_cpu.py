@@ -329,6 +329,44 @@ def test_grouped_valid_call_reaches_device_gate(hq):
     assert _grouped(hq, wsc=8) == hq.HQ_ERR_UNSUPPORTED_DEVICE
 
 
+def _grouped_ep(hq, ep, e=8, t=512, n=128, k=256, out=fake(4)):
+    return hq.load().hq_grouped_gemm_a8w8_epilogue(fake(0), 0, fake(1), 0, fake(2), t, fake(3), e * n, fake(5), e,
+                                                   t, n, k, ctypes.byref(ep) if ep is not None else None, out, None)
+
+
+def test_grouped_epilogue_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    bias, bsc, osc = BASE + 6 * (1 << 32), BASE + 7 * (1 << 32), BASE + 8 * (1 << 32)
+    assert _grouped_ep(hq, hq.hq_epilogue(bias, 7, None, None, 0)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_E5M2, None, None, 0)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_BF16, bsc, None, 0)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(None, 0, bsc, None, 0)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(None, 0, None, osc, 9)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(None, 0, None, osc + 1, 0)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_E4M3, bsc + 2, None, 0)) == E   # misaligned bias_scale
+    # FP8 output is t*n bytes; a per-expert FP8 bias [E, n] one byte before its end overlaps it
+    assert _grouped_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) + 512 * 128 - 1, hq.HQ_BIAS_E4M3, bsc, osc, 0)) == E
+    assert "overlaps" in hq.hq_last_error()
+    # bf16 output is 2*t*n bytes: the same bias now overlaps it
+    assert _grouped_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) + 512 * 128, hq.HQ_BIAS_E4M3, bsc, None, 0)) == E
+    # the bias region is [E, n]: a bf16 bias ending one byte into out overlaps it
+    assert _grouped_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) - 8 * 128 * 2 + 2, hq.HQ_BIAS_BF16, None, None,
+                                          0)) == E
+    assert _grouped_ep(hq, hq.hq_epilogue(None, 0, None, None, 0), e=0) == E
+    assert _grouped_ep(hq, None, t=0) == hq.HQ_OK
+
+
+@no_gpu
+def test_grouped_epilogue_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    bias, bsc, osc = BASE + 6 * (1 << 32), BASE + 7 * (1 << 32), BASE + 8 * (1 << 32)
+    assert _grouped_ep(hq, None) == U
+    assert _grouped_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_BF16, None, osc, hq.HQ_E5M2)) == U
+    assert _grouped_ep(hq, hq.hq_epilogue(bias, hq.HQ_BIAS_E4M3, bsc, None, 0)) == U
+    assert _grouped_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) - 8 * 128 * 2, hq.HQ_BIAS_BF16, None, None, 0)) == U
+    assert _grouped_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) + 512 * 128, hq.HQ_BIAS_E4M3, bsc, osc, 0)) == U
+
+
 def test_preshuffle_and_ring_validation(hq):
     lib = hq.load()
     E = hq.HQ_ERR_INVALID_ARGUMENT

@@ -1,4 +1,4 @@
-"""GPU parity of hq_gemm_a8w8_epilogue: the bias (bf16, or FP8 codes times a
+"""GPU parity of hq_gemm_a8w8_epilogue and hq_grouped_gemm_a8w8_epilogue: the bias (bf16, or FP8 codes times a
 bias scale) and the FP8 output (codes of v * 1/out_scale) of the GEMM epilogue.
 
 With operands whose products are multiples of 2^-6 in [1, 4) (narrow codes)
@@ -162,5 +162,90 @@ def test_plain_epilogue_equals_hq_gemm_a8w8(hq):
     pre = hq.hq_preshuffle_weight(dev_u8(wq))
     a = hq.hq_gemm_a8w8(dev_u8(xq), fp8.E4M3, pre, fp8.E4M3, xs, ws, n)
     b = hq.hq_gemm_a8w8_epilogue(dev_u8(xq), fp8.E4M3, pre, fp8.E4M3, xs, ws, n)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---- grouped ---------------------------------------------------------------------
+
+def _grouped_bias(rng, e_count, n, kind):
+    """(device bias [E, n], device bias_scale [E] or None, float64 values [E, n])."""
+    if kind == "bf16":
+        b = (rng.standard_normal((e_count, n)) * 8).astype(np.float32)
+        bits = torch.from_numpy(b).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return (torch.from_numpy(bits.view(np.int16)).cuda(), None,
+                np.stack([G.bias_values(bits[i], G.BIAS_BF16) for i in range(e_count)]))
+    table = fp8.decode_table(FMT[kind])
+    finite = np.array([c for c in range(256) if np.isfinite(table[c])], dtype=np.uint8)
+    codes = rng.choice(finite, (e_count, n))
+    bsc = rng.uniform(0.01, 0.1, e_count).astype(np.float32)
+    vals = np.stack([G.bias_values(codes[i], KIND[kind], bsc[i]) for i in range(e_count)])
+    return dev_u8(codes), dev_f32(bsc), vals
+
+
+@pytest.mark.parametrize("bias_kind", BIASES)
+@pytest.mark.parametrize("out_kind", OUTS)
+def test_grouped_epilogue_bit_exact_on_exact_accumulators(hq, bias_kind, out_kind):
+    """Per-expert bias rows and a shared output scale over ragged groups (two
+    empty experts, rows past the last offset left untouched): on exact
+    accumulators every covered element equals epilogue_f32 bit for bit."""
+    rng = np.random.default_rng(zlib.crc32(repr(("grouped", bias_kind, out_kind)).encode()))
+    counts = [5, 0, 130, 1, 0, 257, 64]
+    e_count = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    t, n, k = int(offsets[-1]) + 7, 144, 400
+    xq = narrow_codes(rng, (t, k), fp8.E4M3)
+    wq = narrow_codes(rng, (e_count, n, k), fp8.E5M2)
+    xs = rng.uniform(1e-3, 2.0, t).astype(np.float32)
+    ws = rng.uniform(1e-3, 2.0, (e_count, n)).astype(np.float32)
+    out_scale = np.float32(rng.uniform(0.5, 4.0))
+    kw = {}
+    bvals = None
+    if bias_kind != "none":
+        bd, bs, bvals = _grouped_bias(rng, e_count, n, bias_kind)
+        kw.update(bias=bd, bias_type=KIND[bias_kind], bias_scale=bs)
+    if out_kind != "bf16":
+        kw.update(out_scale=dev_f32(np.array([out_scale])), out_fmt=FMT[out_kind])
+        sentinel = 0x55
+        out = torch.full((t, n), sentinel, dtype=torch.uint8, device="cuda")
+    else:
+        sentinel = 0x7FC1
+        out = torch.full((t, n), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    pre = torch.cat([hq.hq_preshuffle_weight(dev_u8(wq[i])) for i in range(e_count)])
+    off = torch.from_numpy(offsets).cuda()
+    hq.hq_grouped_gemm_a8w8_epilogue(dev_u8(xq), fp8.E4M3, pre, fp8.E5M2, dev_f32(xs), dev_f32(ws.reshape(-1)), off,
+                                     e_count, n, out=out, **kw)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.all(got[offsets[-1]:] == sentinel)
+    dx, dw = fp8.decode(xq, fp8.E4M3), fp8.decode(wq, fp8.E5M2)
+    for e in range(e_count):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        acc = dx[lo:hi] @ dw[e].T
+        acc32 = acc.astype(np.float32)
+        assert np.array_equal(acc32.astype(np.float64), acc)
+        b = None if bvals is None else np.broadcast_to(bvals[e], acc.shape).astype(np.float32)
+        want = G.epilogue_f32(acc32, xs[lo:hi, None], ws[e][None, :], b,
+                              None if out_kind == "bf16" else out_scale, FMT.get(out_kind))
+        bad = np.argwhere(got[lo:hi] != want)
+        assert bad.size == 0, (f"expert {e}: {len(bad)} differ; first at row {lo + bad[0][0]}, col {bad[0][1]}: "
+                               f"got {got[lo + bad[0][0], bad[0][1]]:#x} want {want[bad[0][0], bad[0][1]]:#x}")
+
+
+def test_grouped_plain_epilogue_equals_hq_grouped_gemm_a8w8(hq):
+    """No bias, bf16 output: the same bits as hq_grouped_gemm_a8w8 (full-range codes)."""
+    rng = np.random.default_rng(9)
+    counts = [300, 0, 77, 513]
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    t, n, k = sum(counts), 520, 1040
+    xq = dev_u8(rng.integers(0, 0x7E, (t, k), dtype=np.uint8))
+    wq = rng.integers(0, 0x7E, (len(counts), n, k), dtype=np.uint8)
+    pre = torch.cat([hq.hq_preshuffle_weight(dev_u8(wq[i])) for i in range(len(counts))])
+    xs = dev_f32(rng.uniform(0.1, 1.0, t).astype(np.float32))
+    ws = dev_f32(rng.uniform(0.1, 1.0, len(counts) * n).astype(np.float32))
+    a = hq.hq_grouped_gemm_a8w8(xq, fp8.E4M3, pre, fp8.E4M3, xs, ws, offsets, len(counts), n)
+    b = hq.hq_grouped_gemm_a8w8_epilogue(xq, fp8.E4M3, pre, fp8.E4M3, xs, ws, offsets, len(counts), n)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
