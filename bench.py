@@ -3,8 +3,10 @@
 Workload (the PTPC square configuration): X bf16 [4096, 4096] N(0,1) with 0.1%
 of entries x50, W bf16 [4096, 4096] N(0, 0.02^2). One step is one pass of the
 whole path: per-token E4M3 quantization of X, per-output-channel E4M3
-quantization of W (row reduction on [N, K]), pre-shuffle of WQ, and the a8w8
-GEMM M = N = K = 4096 into bf16. Inputs are resident in HBM before timing;
+quantization of W (row reduction on [N, K]) written straight into the GEMM's
+pre-shuffled weight layout (the quantize and pre-shuffle in one pass), and the
+a8w8 GEMM M = N = K = 4096 into bf16. The two-launch form of the weight side
+(row-major codes, then the pre-shuffle) is timed beside it. Inputs are resident in HBM before timing;
 ``--rotate`` input/output sets (default 8, ~1.2 GB) cycle so that neither a step
 nor a single kernel's timing loop finds its data in the 256 MB Infinity Cache.
 
@@ -94,12 +96,21 @@ def make_ops(hq, lib, stream):
         st = lib.hq_preshuffle_weight(b.p["wq"], N, K, b.p["wpre"], h or stream)
         assert st == 0, hq.hq_last_error()
 
+    def quant_w_pre(b, h=None):
+        st = lib.hq_quantize_fp8_preshuffled(b.p["w"], BF16, N, K, E4M3, None, b.p["wpre"], b.p["ws"], b.p["wa"],
+                                             h or stream)
+        assert st == 0, hq.hq_last_error()
+
     def gemm(b, h=None):
         st = lib.hq_gemm_a8w8(b.p["xq"], E4M3, b.p["wpre"], E4M3, b.p["xs"], M, b.p["ws"], N, M, N, K, b.p["out"],
                               None, 0, h or stream)
         assert st == 0, hq.hq_last_error()
 
-    return {"quant_x": quant_x, "quant_w": quant_w, "preshuffle": preshuffle, "gemm": gemm}
+    step = {"quant_x": quant_x, "quant_w_pre": quant_w_pre, "gemm": gemm}
+    # the two-launch form of quant_w_pre (row-major codes, then the pre-shuffle),
+    # timed for comparison only
+    two_launch = {"quant_w": quant_w, "preshuffle": preshuffle}
+    return step, two_launch
 
 
 def time_kernel(torch, fn, sets, reps):
@@ -653,7 +664,7 @@ def main():
     x_bits, w_bits = workloads.ptpc_square(1)
     pre_bytes = hq.hq_preshuffled_bytes(N, K)
     sets = [Buffers(torch, x_bits, w_bits, pre_bytes) for _ in range(args.rotate)]
-    ops = make_ops(hq, lib, stream)
+    ops, two_launch = make_ops(hq, lib, stream)
 
     def step(i):
         b = sets[i % len(sets)]
@@ -677,7 +688,7 @@ def main():
     # sets inside a HIP graph on a side stream, bracketed by HIP events on that
     # stream (no host launch overhead, no event between launches).
     kms = {}
-    for name, fn in ops.items():
+    for name, fn in {**ops, **two_launch}.items():
         def launch(i, h, fn=fn):
             fn(sets[i % len(sets)], h)
         kms[name] = time_graph(torch, launch, 2 * len(sets))
@@ -685,6 +696,7 @@ def main():
         log(f"  {name}: {ms * 1e3:.2f} us")
     quant_bytes = M * K * 2 + M * K + M * 4 * 2      # bf16 in, codes out, scale + amax out
     pre_alg_bytes = N * K + pre_bytes
+    qwp_bytes = N * K * 2 + pre_bytes + N * 4 * 2   # bf16 in, pre-shuffled codes out, scale + amax out
     gemm_tflops = flops / (kms["gemm"] * 1e-3) / 1e12
     quant_gbs = quant_bytes / (kms["quant_x"] * 1e-3) / 1e9
 
@@ -716,7 +728,9 @@ def main():
         "config": {
             "workload": "PTPC square: X bf16 [4096,4096] N(0,1) with 0.1% of entries x50, W bf16 [4096,4096] "
                         "N(0,0.02^2); per-token X, per-output-channel W, E4M3; GEMM M=N=K=4096 -> bf16",
-            "step": "quantize X + quantize W + pre-shuffle W + GEMM",
+            "step": "quantize X per token + quantize W per output channel straight into the pre-shuffled "
+                    "layout (hq_quantize_fp8_preshuffled: the codes and layout of per-token quantize + "
+                    "pre-shuffle in one pass) + GEMM",
             "m": M, "n": N, "k": K, "rotating_sets": args.rotate,
         },
         "roofline": {
@@ -742,6 +756,16 @@ def main():
             "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": quant_bytes,
             "traffic": traffic_from_profile("quant_rows_ptpc4096"),
+        },
+        "quant_w_pre": {
+            "kernel": "per-output-channel quantize of W into the pre-shuffled layout (hq_quantize_fp8_preshuffled)",
+            "bound": "hbm",
+            "achieved": round(qwp_bytes / (kms["quant_w_pre"] * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(qwp_bytes / (kms["quant_w_pre"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": qwp_bytes,
+            "two_launch_us": round((kms["quant_w"] + kms["preshuffle"]) * 1e3, 3),
         },
         "preshuffle_gbs": round(pre_alg_bytes / (kms["preshuffle"] * 1e-3) / 1e9, 1),
         "copy_probe_gbs": round(copy_gbs, 1),

@@ -9,7 +9,7 @@ from ._lib import (HQ_BF16, HQ_BIAS_BF16, HQ_BIAS_E4M3, HQ_BIAS_E5M2, HQ_E4M3, H
                    HQUnsupportedDevice, LIB_PATH, SIGNATURES, hq_epilogue, hq_ring, load)
 from .api import (Ring, gemm_workspace, hq_gemm_a8w8, hq_gemm_a8w8_blockscaled, hq_gemm_a8w8_epilogue,
                   hq_gemm_workspace_bytes, hq_quantize_fp8_blockwise, hq_grouped_gemm_a8w8,
-                  hq_grouped_gemm_a8w8_epilogue,
+                  hq_grouped_gemm_a8w8_epilogue, hq_quantize_fp8_preshuffled,
                   hq_last_error, hq_preshuffle_weight, hq_preshuffled_bytes, hq_quantize_fp8,
                   hq_quantize_fp8_layouts, hq_quantize_fp8_layouts_stochastic, hq_quantize_fp8_stochastic,
                   hq_quantize_workspace_bytes, hq_scale_count,
@@ -23,5 +23,5 @@ __all__ = [
     "hq_quantize_workspace_bytes", "hq_preshuffled_bytes", "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_layouts_stochastic", "hq_quantize_fp8_stochastic", "hq_quantize_fp8_blockwise", "hq_gemm_a8w8_blockscaled",
     "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_workspace_bytes", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue", "hq_epilogue", "HQ_BIAS_BF16", "HQ_BIAS_E4M3", "HQ_BIAS_E5M2",
-    "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_last_error", "gemm_workspace",
+    "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error", "gemm_workspace",
 ]

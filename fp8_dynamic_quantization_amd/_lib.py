@@ -84,6 +84,7 @@ SIGNATURES = {
     "hq_scale_ring_update": (_I, [ctypes.POINTER(hq_ring), _P, _I, _P]),
     "hq_preshuffled_bytes": (_I64, [_I64, _I64]),
     "hq_preshuffle_weight": (_I, [_P, _I64, _I64, _P, _P]),
+    "hq_quantize_fp8_preshuffled": (_I, [_P, _I, _I64, _I64, _I, _P, _P, _P, _P, _P]),
     "hq_gemm_workspace_bytes": (_I64, [_I64, _I64, _I64]),
     "hq_gemm_a8w8": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "hq_gemm_a8w8_epilogue": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, ctypes.POINTER(hq_epilogue),

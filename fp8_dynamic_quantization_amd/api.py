@@ -21,7 +21,7 @@ __all__ = [
     "hq_quantize_fp8_blockwise",
     "hq_gemm_a8w8_blockscaled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
-    "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_last_error",
+    "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error",
 ]
 
 _XT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16}
@@ -263,6 +263,33 @@ def hq_preshuffle_weight(wq: torch.Tensor, out=None, stream=None) -> torch.Tenso
         out = torch.empty(max(nbytes, 0), dtype=torch.uint8, device=wq.device)
     check(lib.hq_preshuffle_weight(_ptr(wq), n, k, _ptr(out), _stream(wq.device, stream)))
     return out
+
+
+def hq_quantize_fp8_preshuffled(x: torch.Tensor, fmt: int = HQ_E4M3, *, row_major: bool = False, q=None,
+                                q_pre=None, scale_out=None, amax_out=None, stream=None):
+    """Per-row quantization of a weight [n, k] straight into the pre-shuffled
+    layout; returns (q_pre uint8 flat, scale_out fp32 [n], amax_out fp32 [n],
+    q uint8 [n, k] or None). Row-major codes are written too when `q` is given
+    or `row_major` is set."""
+    if x.dtype not in _XT:
+        raise ValueError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    x = x.contiguous()
+    rows, cols = x.shape
+    lib = load()
+    dev = x.device
+    if q is None and row_major:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if q_pre is None:
+        q_pre = torch.empty(max(int(lib.hq_preshuffled_bytes(rows, cols)), 0), dtype=torch.uint8, device=dev)
+    if scale_out is None:
+        scale_out = torch.empty(rows, dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty(rows, dtype=torch.float32, device=dev)
+    check(lib.hq_quantize_fp8_preshuffled(_ptr(x), _XT[x.dtype], rows, cols, fmt, _ptr(q), _ptr(q_pre),
+                                          _ptr(scale_out), _ptr(amax_out), _stream(dev, stream)))
+    return q_pre, scale_out, amax_out, q
 
 
 _GEMM_WORKSPACE = {}

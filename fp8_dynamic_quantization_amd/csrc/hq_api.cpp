@@ -370,6 +370,38 @@ hq_status hq_scale_ring_update(const hq_ring* ring, const float* amax, int fmt, 
                   "hq_scale_ring_update");
 }
 
+hq_status hq_quantize_fp8_preshuffled(const void* x, int xt, int64_t rows, int64_t cols, int fmt, uint8_t* q,
+                                      uint8_t* q_pre, float* scale_out, float* amax_out, hipStream_t stream) {
+  if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
+  if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
+  if (rows < 0 || rows > kI32Max - 31)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 32), got %lld", (long long)rows);
+  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
+  if (rows == 0) return ok();
+  if (!x || !q_pre || !scale_out) return fail(HQ_ERR_INVALID_ARGUMENT, "x, q_pre and scale_out must be non-NULL");
+  if (!aligned(x, 16) || !aligned(q_pre, 16) || (q && !aligned(q, 16)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "x, q and q_pre must be 16-byte aligned");
+  if (!aligned(scale_out, 4) || (amax_out && !aligned(amax_out, 4)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "scale_out and amax_out must be 4-byte aligned");
+  const size_t numel = (size_t)rows * (size_t)cols;
+  const Range rg[] = {
+      {x, numel * (xt == HQ_BF16 ? 2 : 4), "x"},
+      {q, q ? numel : 0, "q"},
+      {q_pre, (size_t)padded_bytes(rows, cols), "q_pre"},
+      {scale_out, (size_t)rows * 4, "scale_out"},
+      {amax_out, amax_out ? (size_t)rows * 4 : 0, "amax_out"},
+  };
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 5, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  return launched(hq::launch_quant_rows_pre(x, xt, (int)rows, (int)cols, fmt, q, q_pre, scale_out, amax_out, stream),
+                  "hq_quantize_fp8_preshuffled");
+}
+
 hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k, uint8_t* wq_pre, hipStream_t stream) {
   if (n < 0 || n > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31), got %lld", (long long)n);
   if (k < 16 || k > kI32Max || k % 16 != 0)

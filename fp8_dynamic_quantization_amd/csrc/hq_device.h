@@ -211,6 +211,7 @@ __device__ __forceinline__ void cast_vec(const uint4& v, float r, uint32_t raw, 
 // ---- code stores -----------------------------------------------------------------
 
 typedef unsigned int hq_u2v __attribute__((ext_vector_type(2)));
+typedef unsigned int hq_u4v __attribute__((ext_vector_type(4)));
 
 // E codes (E/4 words in w) to p. The codes are written once and read by a later
 // kernel, so they go out as non-temporal stores: streamed to memory without
@@ -223,6 +224,17 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t* w) {
     __builtin_nontemporal_store(v, reinterpret_cast<hq_u2v*>(p));
   } else {
     __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+  }
+}
+
+// The same with ordinary stores, for outputs whose 128-byte lines are filled by
+// several wavefronts of a workgroup and should meet in L2 before write-back.
+template <int E>
+__device__ __forceinline__ void store_codes_temporal(uint8_t* p, const uint32_t* w) {
+  if constexpr (E == 8) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = w[0];
   }
 }
 

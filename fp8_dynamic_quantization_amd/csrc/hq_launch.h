@@ -32,6 +32,10 @@ int col_chunks(int rows);                 // partial rows of the per-column pass
 // `sr`: stochastic rounding to E5M2 (fmt must be E5M2) with hash key `seed`.
 hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,
                              float* amax, bool sr, uint64_t seed, hipStream_t st);
+// Per-row dynamic quantization of a weight [rows, cols] straight into the
+// pre-shuffled layout qp (and row-major codes into q when non-null).
+hipError_t launch_quant_rows_pre(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, uint8_t* qp,
+                                 float* scale, float* amax, hipStream_t st);
 hipError_t launch_quant_tensor(const void* x, int xt, size_t numel, int fmt, uint8_t* q, float* scale,
                                float* amax, void* ws, bool sr, uint64_t seed, hipStream_t st);
 hipError_t launch_quant_cols(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, float* scale,

@@ -938,6 +938,128 @@ __global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// per row, straight into the pre-shuffled weight layout
+// ---------------------------------------------------------------------------
+// Row n of a weight [N, K] is the GEMM's output channel n, so per-row scaling
+// is the per-output-channel weight scale, and the codes can go to the
+// pre-shuffled layout at once instead of through a row-major copy. A workgroup
+// of 16 wavefronts owns 16 consecutive rows, one row per wavefront, held in
+// registers between the amax and the cast as in quant_rows_wave_kernel. Rows
+// 32G .. 32G+15 are slots 0..7 of fragments 2G and 2G+1 (and rows 32G+16 ..
+// +31 slots 8..15), so a workgroup fills whole 128-byte lines of both
+// fragments and each line is complete in one XCD's L2 before it is written
+// back; one workgroup per 16 rows, so 4096 rows give 256 workgroups of 16
+// wavefronts, the per-token kernel's occupancy. Columns past K up to the
+// 128-padded K, and rows past N up to the 32-padded N, are written as zero
+// codes. NV == 0: rows too long for registers are read twice (amax pass, then
+// cast pass).
+constexpr int kPreRows = 16;
+
+template <int XT, int FMT, int NV>
+__global__ __launch_bounds__(64 * kPreRows) void quant_rows_pre_kernel(
+    const uint4* __restrict__ x, uint8_t* __restrict__ q, uint8_t* __restrict__ qp, float* __restrict__ scale,
+    float* __restrict__ amax_out, int rows, int vpr, int kblocks) {
+  constexpr int E = VecTraits<XT>::kElems;
+  constexpr int NR = NV > 0 ? NV : 1;
+  // NV > 0: the 16 rows' codes are staged in LDS in output order, then written
+  // as whole 128-byte lines (8 lanes per line). Line L of the workgroup is
+  // (fragment 2G+p, K block kb, h, q) with L = ((p * kblocks + kb) * 2 + h) * 4
+  // + q, and holds this workgroup's 8 slots of it; slot s8 sits at position
+  // (s8 + L) % 8 of the staged line, which spreads a wavefront's LDS writes
+  // over the banks.
+  constexpr int kStage = NV > 0 ? kPreRows * 64 * NV * E : 16;
+  __shared__ __align__(16) uint8_t stage[kStage];
+  const int lane = threadIdx.x & 63;
+  const int lr = threadIdx.x >> 6;
+  const int row = blockIdx.x * kPreRows + lr;
+  const bool valid = row < rows;  // rows past N up to a multiple of 32 are zero codes
+  const int vpp = kblocks * (128 / E);  // vectors per padded row
+  const SrSeed sd{0u, 0u};
+  const uint32_t zero[4] = {0u, 0u, 0u, 0u};
+  const uint4* xr = x + (size_t)(valid ? row : 0) * vpr;
+  const int s8 = 4 * (lr >> 3) + (lr & 3), pf = (lr >> 2) & 1;
+  // lanes past the row end reload the row's last vector (a real element, so it
+  // cannot change the max) and write zero codes instead
+  uint4 cur[NR];
+  uint32_t raw[NR];
+  uint32_t mx = 0;
+  if (valid) {
+    if (NV > 0) {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) cur[j] = xr[min(lane + 64 * j, vpr - 1)];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        raw[j] = vec_absmax_raw<XT>(cur[j]);
+        mx = max(mx, raw[j]);
+      }
+    } else {
+      for (int i = lane; i < vpr; i += 64) mx = max(mx, vec_absmax_raw<XT>(xr[i]));
+    }
+    mx = wave_max_u32(mx);
+    if (mx >= kInfBits) {  // the row holds an Inf/NaN: recompute over finite elements
+      uint32_t f = 0;
+      if (NV > 0) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) f = max(f, vec_absmax_finite<XT>(cur[j]));
+      } else {
+        for (int i = lane; i < vpr; i += 64) f = max(f, vec_absmax_finite<XT>(xr[i]));
+      }
+      mx = wave_max_u32(f);
+    }
+  }
+  const float amax = __uint_as_float(mx);
+  const float s = scale_from_amax<FMT>(amax);
+  const float r = 1.0f / s;
+  if (valid && lane == 0) {
+    scale[row] = s;
+    if (amax_out) amax_out[row] = amax;
+  }
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int i = lane + 64 * j;
+      if (i < vpp) {
+        uint32_t w[E / 4];
+        if (valid && i < vpr) {
+          cast_vec<XT, FMT, false>(cur[j], r, raw[j], w, sd, 0);
+          if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
+        } else {
+#pragma unroll
+          for (int d = 0; d < E / 4; ++d) w[d] = 0u;
+        }
+        const int c0 = i * E, kin = c0 & 127;
+        const int L = ((pf * kblocks + (c0 >> 7)) * 2 + ((kin >> 4) & 1)) * 4 + (kin >> 5);
+        store_codes_temporal<E>(stage + L * 128 + (((s8 + L) & 7) << 4) + (kin & 15), w);
+      }
+    }
+    __syncthreads();
+    const int G = blockIdx.x >> 1, half = blockIdx.x & 1;
+    const int pieces = 128 * kblocks;  // 16 rows x padded K / 16 bytes
+    for (int t = threadIdx.x; t < pieces; t += 64 * kPreRows) {
+      const int L = t >> 3, pos = t & 7;
+      const hq_u4v v = *reinterpret_cast<const hq_u4v*>(stage + t * 16);
+      const int slot = 8 * half + ((pos - L) & 7);
+      const int kbp = L >> 3, pp = kbp >= kblocks ? 1 : 0, kb = kbp - pp * kblocks;
+      const size_t off = ((size_t)(2 * G + pp) * kblocks + kb) * 2048 + ((L >> 2) & 1) * 1024 + ((L & 3) * 16 + slot) * 16;
+      __builtin_nontemporal_store(v, reinterpret_cast<hq_u4v*>(qp + off));
+    }
+  } else {
+    // rows too long for registers: read twice, codes stored one vector at a time
+    for (int i = lane; i < vpp; i += 64) {
+      uint32_t w[E / 4];
+      if (valid && i < vpr) {
+        const uint4 v = xr[i];
+        cast_vec<XT, FMT, false>(v, r, vec_absmax_raw<XT>(v), w, sd, 0);
+        if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
+        store_codes_temporal<E>(qp + preshuffled_offset(row, i * E, kblocks), w);
+      } else {
+        store_codes_temporal<E>(qp + preshuffled_offset(row, i * E, kblocks), zero);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -979,6 +1101,39 @@ hipError_t launch_quant_rows(const void* x, int xt, int rows, int cols, int fmt,
 #define CALL(A, B, S) return launch_rows_t<A, B, S>(x, rows, vpr, q, scale, amax, sd, st)
   HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
+}
+
+template <int XT, int FMT>
+static hipError_t launch_rows_pre_t(const void* x, int rows, int cols, uint8_t* q, uint8_t* qp, float* scale,
+                                    float* amax, hipStream_t st) {
+  constexpr int E = VecTraits<XT>::kElems;
+  const uint4* xv = static_cast<const uint4*>(x);
+  const int vpr = cols / E;
+  const int kblocks = (cols + 127) / 128;
+  const int vpp = kblocks * (128 / E);
+  const dim3 grid((rows + 31) / 32 * 32 / kPreRows), block(64 * kPreRows);
+  if (vpp <= 64) {
+    hipLaunchKernelGGL((quant_rows_pre_kernel<XT, FMT, 1>), grid, block, 0, st, xv, q, qp, scale, amax, rows, vpr, kblocks);
+  } else if (vpp <= 128) {
+    hipLaunchKernelGGL((quant_rows_pre_kernel<XT, FMT, 2>), grid, block, 0, st, xv, q, qp, scale, amax, rows, vpr, kblocks);
+  } else if (vpp <= 256) {
+    hipLaunchKernelGGL((quant_rows_pre_kernel<XT, FMT, 4>), grid, block, 0, st, xv, q, qp, scale, amax, rows, vpr, kblocks);
+  } else if (vpp <= 512) {
+    hipLaunchKernelGGL((quant_rows_pre_kernel<XT, FMT, 8>), grid, block, 0, st, xv, q, qp, scale, amax, rows, vpr, kblocks);
+  } else {
+    hipLaunchKernelGGL((quant_rows_pre_kernel<XT, FMT, 0>), grid, block, 0, st, xv, q, qp, scale, amax, rows, vpr, kblocks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_pre(const void* x, int xt, int rows, int cols, int fmt, uint8_t* q, uint8_t* qp,
+                                 float* scale, float* amax, hipStream_t st) {
+  if (xt == kBF16) {
+    return fmt == kE4M3 ? launch_rows_pre_t<kBF16, kE4M3>(x, rows, cols, q, qp, scale, amax, st)
+                        : launch_rows_pre_t<kBF16, kE5M2>(x, rows, cols, q, qp, scale, amax, st);
+  }
+  return fmt == kE4M3 ? launch_rows_pre_t<kF32, kE4M3>(x, rows, cols, q, qp, scale, amax, st)
+                      : launch_rows_pre_t<kF32, kE5M2>(x, rows, cols, q, qp, scale, amax, st);
 }
 
 // Blocks of the single-pass kernel that one device holds at once, for this

@@ -271,6 +271,22 @@ int64_t hq_preshuffled_bytes(int64_t n, int64_t k);
 hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
                                uint8_t* wq_pre, hipStream_t stream);
 
+/* Per-row dynamic quantization of a weight x [rows, cols] (rows = the GEMM's
+ * output channels N, cols = K) written straight into the pre-shuffled layout:
+ * the codes, scales and amax are exactly those of hq_quantize_fp8 with
+ * HQ_PER_TOKEN (per output channel of the weight, the PTPC weight side of the
+ * aiter PR), and q_pre is byte for byte hq_preshuffle_weight of those codes,
+ * padding included (zero codes), without the row-major copy in between.
+ *   x          device, fp32 / bf16 [rows, cols] row-major, 16-byte aligned
+ *   q          device uint8 [rows, cols] row-major codes, or NULL for none
+ *   q_pre      device, hq_preshuffled_bytes(rows, cols) bytes, 16-byte aligned
+ *   scale_out  device float32 [rows]; amax_out device float32 [rows] or NULL
+ * Requires cols % 16 == 0, rows < 2^31 - 32; no output may overlap another
+ * buffer. rows == 0 returns HQ_OK without a launch. */
+hq_status hq_quantize_fp8_preshuffled(const void* x, int xt, int64_t rows, int64_t cols, int fmt,
+                                      uint8_t* q, uint8_t* q_pre, float* scale_out, float* amax_out,
+                                      hipStream_t stream);
+
 /* Bytes of GEMM workspace worth passing to hq_gemm_a8w8 for an m x n x k
  * product: nonzero only for the decode shapes (1 <= m <= 64) whose weight
  * stream is split over several workgroups per column group. Returns -1 for

@@ -367,6 +367,40 @@ def test_grouped_epilogue_valid_calls_reach_device_gate(hq):
     assert _grouped_ep(hq, hq.hq_epilogue(BASE + 4 * (1 << 32) + 512 * 128, hq.HQ_BIAS_E4M3, bsc, osc, 0)) == U
 
 
+def _qpre(hq, x=fake(0), xt=1, rows=64, cols=128, fmt=0, q=None, qp=fake(1), s=fake(2), a=None):
+    return hq.load().hq_quantize_fp8_preshuffled(x, xt, rows, cols, fmt, q, qp, s, a, None)
+
+
+def test_quantize_preshuffled_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    assert _qpre(hq, xt=5) == E
+    assert _qpre(hq, fmt=3) == E
+    assert _qpre(hq, cols=24) == E
+    assert _qpre(hq, cols=0) == E
+    assert _qpre(hq, rows=-1) == E
+    assert _qpre(hq, rows=(1 << 31) - 31) == E
+    assert _qpre(hq, qp=ctypes.c_void_p(0)) == E
+    assert _qpre(hq, s=ctypes.c_void_p(0)) == E
+    assert _qpre(hq, qp=fake(1, 8)) == E                      # misaligned q_pre
+    assert _qpre(hq, q=fake(3, 4)) == E                       # misaligned q
+    assert _qpre(hq, a=fake(3, 2)) == E                       # misaligned amax
+    # q_pre is padded: 64 x 128 codes = 8192 bytes; x (bf16) is 16384 bytes
+    assert _qpre(hq, qp=fake(0, 16384 - 16)) == E             # q_pre overlaps x
+    assert _qpre(hq, q=fake(1, 8192 - 16)) == E               # q overlaps q_pre
+    assert _qpre(hq, rows=40, cols=16, s=fake(1, 64 * 128 - 4)) == E   # scale_out inside the padded rows
+    assert "overlaps" in hq.hq_last_error()
+    assert _qpre(hq, rows=0) == hq.HQ_OK
+
+
+@no_gpu
+def test_quantize_preshuffled_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    assert _qpre(hq) == U
+    assert _qpre(hq, q=fake(3), a=fake(4), xt=0, fmt=1) == U
+    assert _qpre(hq, qp=fake(0, 16384)) == U                  # right after x
+    assert _qpre(hq, rows=40, cols=16, s=fake(1, 64 * 128)) == U      # right after the 64 x 128 padded q_pre
+
+
 def test_preshuffle_and_ring_validation(hq):
     lib = hq.load()
     E = hq.HQ_ERR_INVALID_ARGUMENT
