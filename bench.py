@@ -766,6 +766,7 @@ def main():
             "frac": round(qwp_bytes / (kms["quant_w_pre"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": qwp_bytes,
             "two_launch_us": round((kms["quant_w"] + kms["preshuffle"]) * 1e3, 3),
+            "traffic": traffic_from_profile("quant_rows_pre_ptpc4096"),
         },
         "preshuffle_gbs": round(pre_alg_bytes / (kms["preshuffle"] * 1e-3) / 1e9, 1),
         "copy_probe_gbs": round(copy_gbs, 1),
