@@ -669,6 +669,10 @@ def main():
     sets = [Buffers(torch, x_bits, w_bits, pre_bytes) for _ in range(args.rotate)]
     ops, two_launch = make_ops(hq, lib, stream)
 
+    def same_traffic(b, h):  # h unused: inside the graph capture torch's current stream is h
+        halves = b.x.view(torch.uint8).view(2, M * K)
+        torch.bitwise_xor(halves[0], halves[1], out=b.xq.view(-1))
+
     def step(i):
         b = sets[i % len(sets)]
         for fn in ops.values():
@@ -710,6 +714,13 @@ def main():
     copy_gbs = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
     log(f"  copy probe: {copy_gbs:.0f} GB/s")
     del src, dst
+    # the quantize's own traffic without its arithmetic: the 2 bytes of each
+    # element read, one byte written (torch's vectorised elementwise xor of the
+    # two halves of X's bytes into the code buffer), over the same rotating
+    # sets; a practical ceiling for a pass of this size
+    same_ms = time_graph(torch, lambda i, h: same_traffic(sets[i % len(sets)], h), 2 * len(sets))
+    same_gbs = (M * K * 3) / (same_ms * 1e-3) / 1e9
+    log(f"  same-traffic probe: {same_ms * 1e3:.2f} us = {same_gbs:.0f} GB/s")
     other = None if args.no_other else other_workloads(torch, hq, lib, args.kernel_reps)
     if other:
         log(json.dumps(other))
@@ -759,6 +770,10 @@ def main():
             "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": quant_bytes,
             "traffic": traffic_from_profile("quant_rows_ptpc4096"),
+            "same_traffic_probe": {"us": round(same_ms * 1e3, 3), "gbs": round(same_gbs, 1),
+                                   "what": "the 32 MiB of X read, 16 MiB written (torch elementwise xor of the "
+                                           "two halves of X's bytes), same rotating sets",
+                                   "quantize_frac_of_probe": round(same_ms / kms["quant_x"], 4)},
         },
         "quant_w_pre": {
             "kernel": "per-output-channel quantize of W into the pre-shuffled layout (hq_quantize_fp8_preshuffled)",
