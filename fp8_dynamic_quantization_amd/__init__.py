@@ -8,6 +8,7 @@ from ._lib import (HQ_BF16, HQ_BIAS_BF16, HQ_BIAS_E4M3, HQ_BIAS_E5M2, HQ_E4M3, H
                    HQ_PER_TOKEN, HQError, HQInvalidArgument, HQLaunchError,
                    HQUnsupportedDevice, LIB_PATH, SIGNATURES, hq_epilogue, hq_ring, load)
 from .api import (Ring, gemm_workspace, hq_gemm_a8w8, hq_gemm_a8w8_blockscaled, hq_gemm_a8w8_epilogue,
+                  hq_gemm_a8w8_blockscaled_preshuffled,
                   hq_gemm_workspace_bytes, hq_quantize_fp8_blockwise, hq_grouped_gemm_a8w8,
                   hq_grouped_gemm_a8w8_epilogue, hq_quantize_fp8_preshuffled,
                   hq_last_error, hq_preshuffle_weight, hq_preshuffled_bytes, hq_quantize_fp8,
@@ -20,7 +21,7 @@ __all__ = [
     "HQ_E4M3", "HQ_E5M2", "HQ_F32", "HQ_BF16", "HQ_PER_TENSOR", "HQ_PER_TOKEN",
     "HQ_PER_CHANNEL", "HQError", "HQInvalidArgument", "HQUnsupportedDevice", "HQLaunchError",
     "LIB_PATH", "SIGNATURES", "hq_ring", "load", "Ring", "hq_scale_count",
-    "hq_quantize_workspace_bytes", "hq_preshuffled_bytes", "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_layouts_stochastic", "hq_quantize_fp8_stochastic", "hq_quantize_fp8_blockwise", "hq_gemm_a8w8_blockscaled",
+    "hq_quantize_workspace_bytes", "hq_preshuffled_bytes", "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_layouts_stochastic", "hq_quantize_fp8_stochastic", "hq_quantize_fp8_blockwise", "hq_gemm_a8w8_blockscaled", "hq_gemm_a8w8_blockscaled_preshuffled",
     "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_workspace_bytes", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue", "hq_epilogue", "HQ_BIAS_BF16", "HQ_BIAS_E4M3", "HQ_BIAS_E5M2",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error", "gemm_workspace",

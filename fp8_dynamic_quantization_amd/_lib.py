@@ -77,6 +77,7 @@ SIGNATURES = {
                                         ctypes.POINTER(hq_ring), _P, _SZ, _P]),
     "hq_quantize_fp8_blockwise": (_I, [_P, _I, _I64, _I64, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P]),
     "hq_gemm_a8w8_blockscaled": (_I, [_P, _I, _P, _I, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P]),
+    "hq_gemm_a8w8_blockscaled_preshuffled": (_I, [_P, _I, _P, _I, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P]),
     "hq_quantize_fp8_layouts": (_I, [_P, _I, _I64, _I64, _I, _P, ctypes.POINTER(hq_ring), _P, _P, _P, _P, _P, _P,
                                      _P, _SZ, _P]),
     "hq_quantize_fp8_layouts_stochastic": (_I, [_P, _I, _I64, _I64, ctypes.c_uint64, _P, ctypes.POINTER(hq_ring), _P,

@@ -19,7 +19,7 @@ __all__ = [
     "Ring", "hq_scale_count", "hq_quantize_workspace_bytes", "hq_preshuffled_bytes",
     "hq_quantize_fp8", "hq_quantize_fp8_layouts", "hq_quantize_fp8_layouts_stochastic", "hq_quantize_fp8_stochastic",
     "hq_quantize_fp8_blockwise",
-    "hq_gemm_a8w8_blockscaled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
+    "hq_gemm_a8w8_blockscaled", "hq_gemm_a8w8_blockscaled_preshuffled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error",
 ]
@@ -179,6 +179,27 @@ def hq_gemm_a8w8_blockscaled(xq: torch.Tensor, xf: int, wq: torch.Tensor, wf: in
         out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
     check(load().hq_gemm_a8w8_blockscaled(_ptr(xq), xf, _ptr(wq), wf, _ptr(x_scales), _ptr(w_scales), int(block_size),
                                           m, n, k, _ptr(bias), _ptr(out), _stream(xq.device, stream)))
+    return out
+
+
+def hq_gemm_a8w8_blockscaled_preshuffled(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
+                                         x_scales: torch.Tensor, w_scales: torch.Tensor, n: int, block_size: int = 128,
+                                         bias=None, out=None, stream=None) -> torch.Tensor:
+    """Block-scaled GEMM (blocks of 128) of row-major codes xq [m, k] and the
+    pre-shuffled weight wq_pre (hq_preshuffle_weight of [n, k]) with block
+    scales [m, nb], [n, nb] and an optional bf16 bias [n]; returns bf16 [m, n]."""
+    xq = xq.contiguous()
+    x_scales, w_scales = x_scales.contiguous(), w_scales.contiguous()
+    m, k = xq.shape
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.numel() != n:
+            raise ValueError("bias must be bf16 with n elements")
+        bias = bias.contiguous()
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    check(load().hq_gemm_a8w8_blockscaled_preshuffled(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scales), _ptr(w_scales),
+                                                      int(block_size), m, n, k, _ptr(bias), _ptr(out),
+                                                      _stream(xq.device, stream)))
     return out
 
 

@@ -134,16 +134,23 @@ struct BsCfg {
   static constexpr int kRowStep = kThreads / 8;    // rows between a thread's A pieces
   static constexpr int kABytes = BM * kBK;         // one LDS stage
   static constexpr int kLdsBytes = 2 * kABytes + (BM + 2 * kBN) * 4;  // two A stages + epilogue scales and bias
+  static constexpr int kBsfBytes = 2 * (BM + kBN) * 4;                // block-scaled form: two stages of block scales
   static_assert(BM % 32 == 0 && TN % 32 == 0 && kWR % 16 == 0, "tile");
 };
 
 // KTAIL: K is not a multiple of 128, so the A chunks past K are zeroed on their
 // way to LDS; without it the K loop has no masking at all.
-template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
+// BSF: the block-scaled form with blocks of 128 along K (one K step): x_scale is
+// [m, nblk] and w_scale [n, nblk] row-major; each step's MFMAs start from zero
+// and their sums are folded as acc = fma(t, fl32(xs[m, kb] * ws[n, kb]), acc),
+// the step's scales staged in LDS one step ahead; the epilogue then applies no
+// scale (only the bias).
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, bool BSF>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m0, int row_end, int n0,
                                           const uint8_t* __restrict__ wq, const float* __restrict__ ws) {
   using C = BsCfg<BM, TN, WM>;
   static_assert(C::kAVec <= C::kIM && C::kIN <= C::kIM, "slot schedule: at most one A piece and two B halves per slot");
+  static_assert(!BSF || BM + C::kBN <= C::kThreads, "block scales: one per thread per step");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront column
@@ -180,19 +187,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // w_scale of its 4*TN columns (clamped at the edges; masked on store).
   float* s_xs = reinterpret_cast<float*>(lds + 2 * C::kABytes);
   float* s_ws = s_xs + BM;
-  for (int t = tid; t < BM; t += C::kThreads) {
-    const int row = min(m0 + t, row_end - 1);
-    s_xs[t] = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
-  }
-  for (int t = tid; t < C::kBN; t += C::kThreads) {
-    const int col = min(n0 + t, a.n - 1);
-    s_ws[t] = a.w_scale_per_col ? ws[col] : ws[0];
+  if constexpr (!BSF) {
+    for (int t = tid; t < BM; t += C::kThreads) {
+      const int row = min(m0 + t, row_end - 1);
+      s_xs[t] = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
+    }
+    for (int t = tid; t < C::kBN; t += C::kThreads) {
+      const int col = min(n0 + t, a.n - 1);
+      s_ws[t] = a.w_scale_per_col ? ws[col] : ws[0];
+    }
   }
   float* s_bias = s_ws + C::kBN;
   if (a.bias_kind != kBiasNone) {
     const float bsc = a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0];
     for (int t = tid; t < C::kBN; t += C::kThreads) s_bias[t] = bias_at(a, min(n0 + t, a.n - 1), bsc);
   }
+
+  // Block scales (BSF): thread t < BM holds xs of tile row t, thread BM + c
+  // holds ws of tile column c, for one K block; a step's values sit in LDS stage
+  // (step % 2) after the tile's epilogue data.
+  float* s_bsf = reinterpret_cast<float*>(lds + C::kLdsBytes);
+  auto bsf_load = [&](int kbq) -> float {
+    if (tid < BM) return a.x_scale[(size_t)min(m0 + tid, row_end - 1) * a.nblk + kbq];
+    if (tid < BM + C::kBN) return ws[(size_t)min(n0 + tid - BM, a.n - 1) * a.nblk + kbq];
+    return 0.0f;
+  };
+  auto bsf_store = [&](int stage, float v) {
+    if (tid < BM + C::kBN) s_bsf[stage * (BM + C::kBN) + tid] = v;
+  };
+  // the lane's rows (16 i + l % 16 of its wavefront row) and its 8 columns,
+  // one base each so every read of a step is a constant offset from it
+  const float* xs_lane = s_bsf + wrow * C::kWR + (lane & 15);
+  const float* ws_lane = s_bsf + BM + wave * TN + 8 * (lane >> 4);
 
   // MFMA-order reads: fragment i is rows i*16 .. i*16+15; lane l reads row
   // i*16 + l%16, chunks 2*(l/16) and 2*(l/16)+1; the swizzle again only depends
@@ -232,6 +258,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   } while (0)
 #define HQ_V8(LO, HI) v8i{(int)LO.x, (int)LO.y, (int)LO.z, (int)LO.w, (int)HI.x, (int)HI.y, (int)HI.z, (int)HI.w}
 
+  // BSF fold of slot I's zero-start sums, issued in the next slot after that
+  // slot's MFMAs: acc = fma(t, fl32(xs * ws), acc), blocks in K order.
+#define HQ_FOLD(I, XS)                                                                                 \
+  _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                                   \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r)                                                      \
+      acc[(I)][j][r] = fmaf(tp_[(I) & 1][j][r], (XS) * wsl_[j][r], acc[(I)][j][r])
+
   // One K step, as kIM slots. Slot i: read an upcoming A fragment from LDS, then memory
   // operations, then the kIN MFMAs of A fragment i. Slots 0 .. kIN-1 load the B
   // halves of step KB+1 (two each), as early as possible, since step KB+1 needs
@@ -247,6 +280,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
     const uint8_t* cur_ = lds + (BUF) * C::kABytes;                                                    \
     uint4 lo0_, hi0_, lo1_, hi1_, lo2_, hi2_;                                                          \
     bool st_valid_ = ra_valid;                                                                         \
+    const float bs_nx_ = BSF ? bsf_load(nb1_) : 0.0f;                                                  \
+    float wsl_[BSF ? C::kIN : 1][4];                                                                   \
+    v4f tp_[2][C::kIN];                                                                                \
+    float xs_prev_ = 0.0f;                                                                             \
+    if constexpr (BSF) {                                                                               \
+      _Pragma("unroll") for (int j = 0; j < C::kIN; ++j) {                                             \
+        const v4f w_ = *reinterpret_cast<const v4f*>(ws_lane + (BUF) * (BM + C::kBN) + 32 * (j >> 1) + 4 * (j & 1)); \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) wsl_[j][r] = w_[r];                              \
+      }                                                                                                \
+    }                                                                                                  \
     HQ_READ_A(cur_, 0, lo0_, hi0_);                                                                    \
     if (kFaDepth == 3) HQ_READ_A(cur_, 1, lo1_, hi1_);                                                 \
     _Pragma("unroll") for (int i = 0; i < C::kIM; ++i) {                                               \
@@ -271,15 +314,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
       }                                                                                                \
       const v8i fa_ = kFaDepth == 2 ? ((i & 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo0_, hi0_))                \
                     : (i % 3 == 0) ? HQ_V8(lo0_, hi0_) : (i % 3 == 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo2_, hi2_); \
-      _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                               \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, \
-                                                                     acc[i][j], WF, XF, 0, 0, 0, 0);   \
+      if constexpr (BSF) {                                                                             \
+        _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                             \
+          tp_[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                            \
+              HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, v4f{0.f, 0.f, 0.f, 0.f}, WF, XF, 0, 0, 0, 0);    \
+        if (i > 0) {                                                                                   \
+          HQ_FOLD(i - 1, xs_prev_);                                                                    \
+          /* the empty asm keeps the folds in this slot, so two slots' sums are live at most */        \
+          _Pragma("unroll") for (int j = 0; j < C::kIN; ++j) asm volatile("" : "+v"(acc[i - 1][j]));   \
+        }                                                                                              \
+        xs_prev_ = xs_lane[(BUF) * (BM + C::kBN) + 16 * i];                                            \
+      } else {                                                                                         \
+        _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                             \
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, \
+                                                                       acc[i][j], WF, XF, 0, 0, 0, 0); \
+      }                                                                                                \
       __builtin_amdgcn_sched_barrier(0);                                                               \
+    }                                                                                                  \
+    if constexpr (BSF) {                                                                               \
+      HQ_FOLD(C::kIM - 1, xs_prev_);                                                                   \
+      bsf_store((BUF) ^ 1, bs_nx_);                                                                    \
     }                                                                                                  \
     __syncthreads();                                                                                   \
   } while (0)
 
   // prologue: A(0) to LDS buffer 0, B(0) to registers, A(1) in flight
+  if constexpr (BSF) bsf_store(0, bsf_load(0));
 #pragma unroll
   for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(0, v);
   ra_valid = a_c * 16 < K;
@@ -309,6 +369,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #undef HQ_READ_A
 #undef HQ_V8
 #undef HQ_STEP
+#undef HQ_FOLD
 
   // Epilogue: fragment pair (2*jp, 2*jp+1) gives lane l the 8 consecutive output
   // columns n0 + wave*TN + 32*jp + 8*(l/16) .. +7 of row m0 + 16*i + l%16.
@@ -322,20 +383,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #pragma unroll
   for (int jp = 0; jp < C::kIN / 2; ++jp)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wsc[jp][e] = s_ws[wave * TN + 32 * jp + ccol + e];
+    for (int e = 0; e < 8; ++e) wsc[jp][e] = BSF ? 1.0f : s_ws[wave * TN + 32 * jp + ccol + e];
 #pragma unroll
   for (int i = 0; i < C::kIM; ++i) {
     const int row = m0 + wrow * C::kWR + i * 16 + (lane & 15);
     if (row >= row_end) continue;
-    const float xsc = s_xs[wrow * C::kWR + i * 16 + (lane & 15)];
+    const float xsc = BSF ? 1.0f : s_xs[wrow * C::kWR + i * 16 + (lane & 15)];
 #pragma unroll
     for (int jp = 0; jp < C::kIN / 2; ++jp) {
       const int col0 = n0 + wave * TN + 32 * jp + ccol;
       if (col0 >= a.n) continue;
       const v4f p0 = acc[i][2 * jp], p1 = acc[i][2 * jp + 1];
       float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      if constexpr (!BSF) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * wsc[jp][e];
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * wsc[jp][e];
+      }
       if (a.bias_kind != kBiasNone) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += s_bias[wave * TN + 32 * jp + ccol + e];
@@ -395,7 +458,18 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(GemmArgs a, int tiles_m,
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM;
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, false>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
+}
+
+// Block-scaled form (blocks of 128 along K) on the same data path.
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
+__global__ __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bsf_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  using C = BsCfg<BM, TN, WM>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes + C::kBsfBytes];
+  int tm, tn;
+  tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM;
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, true>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
 }
 
 // Grouped: a linear tile id enumerates, per expert in order, its row tiles x the
@@ -440,7 +514,7 @@ __global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, cons
     ae.bias = static_cast<const uint8_t*>(a.bias) + (size_t)e * a.n * (a.bias_kind == kBiasBF16 ? 2 : 1);
     if (a.bias_scale) ae.bias_scale = a.bias_scale + e;
   }
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL>(ae, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, false>(ae, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -767,6 +841,44 @@ static hipError_t launch_grouped_cfg(const GemmArgs& a, const int32_t* offsets, 
   return hipGetLastError();
 }
 
+// Block-scaled form: 256 x 128, 128 x 128 or 64 x 128 tiles (64 accumulators
+// per wavefront, room for the fold's sums and scales), chosen by the cost rule
+// of pick_tile with their measured relative throughputs (0.83, 0.81, 0.67 of the
+// plain 256 x 256 tile).
+template <int XF, int WF, int BM, int TN, int WM>
+static hipError_t launch_bsf_cfg(const GemmArgs& a, hipStream_t st) {
+  using C = BsCfg<BM, TN, WM>;
+  const int tiles_m = (a.m + BM - 1) / BM, tiles_n = (a.n + C::kBN - 1) / C::kBN;
+  if (a.k % kBK == 0)
+    hipLaunchKernelGGL((gemm_bsf_kernel<XF, WF, BM, TN, WM, false>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, st,
+                       a, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_bsf_kernel<XF, WF, BM, TN, WM, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, st,
+                       a, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int XF, int WF>
+static hipError_t launch_bsf_t(const GemmArgs& a, hipStream_t st) {
+  const struct {
+    int bm;
+    double eff;
+  } cands[] = {{256, 0.83}, {128, 0.81}, {64, 0.67}};
+  int best = 0;
+  double best_cost = 0.0;
+  for (int c = 0; c < 3; ++c) {
+    const long tiles = (long)((a.m + cands[c].bm - 1) / cands[c].bm) * ((a.n + 127) / 128);
+    const double cost = (double)((tiles + kNumCUs - 1) / kNumCUs) * cands[c].bm * 128 / cands[c].eff;
+    if (c == 0 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  if (best == 0) return launch_bsf_cfg<XF, WF, 256, 32, 2>(a, st);
+  if (best == 1) return launch_bsf_cfg<XF, WF, 128, 32, 1>(a, st);
+  return launch_bsf_cfg<XF, WF, 64, 32, 1>(a, st);
+}
+
 // Up to this many rows the weight-streaming kernel runs the GEMM.
 constexpr int kSkinnyMaxM = 64;
 
@@ -801,6 +913,12 @@ size_t gemm_workspace_bytes(int m, int n, int k) {
 
 hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_t workspace_bytes, hipStream_t st) {
 #define CALL(X, W) return launch_gemm_t<X, W>(a, workspace, workspace_bytes, st)
+  HQ_DISPATCH_FMT_PAIR(xf, wf, CALL);
+#undef CALL
+}
+
+hipError_t launch_gemm_bsf(const GemmArgs& a, int xf, int wf, hipStream_t st) {
+#define CALL(X, W) return launch_bsf_t<X, W>(a, st)
   HQ_DISPATCH_FMT_PAIR(xf, wf, CALL);
 #undef CALL
 }

@@ -617,4 +617,39 @@ hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq,
   return launched(hq::launch_gemm_blockscaled(g, xf, wf, block_size, stream), "hq_gemm_a8w8_blockscaled");
 }
 
+hq_status hq_gemm_a8w8_blockscaled_preshuffled(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                                               const float* x_scales, const float* w_scales, int block_size,
+                                               int64_t m, int64_t n, int64_t k, const uint16_t* bias, uint16_t* out,
+                                               hipStream_t stream) {
+  hq_status st = check_gemm_common(xf, wf, m, n, k);
+  if (st != HQ_OK) return st;
+  if (block_size != 128)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "the pre-shuffled block-scaled GEMM takes blocks of 128, got %d", block_size);
+  if (m == 0 || n == 0) return ok();
+  if (!xq || !wq_pre || !x_scales || !w_scales || !out)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scales, w_scales and out must be non-NULL");
+  if (!aligned(xq, 16) || !aligned(wq_pre, 16) || !aligned(out, 16))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre and out must be 16-byte aligned");
+  if (!aligned(x_scales, 4) || !aligned(w_scales, 4) || (bias && !aligned(bias, 2)))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "the scales must be 4-byte and bias 2-byte aligned");
+  const int64_t nb = (k + 127) / 128;
+  const Range rg[] = {
+      {out, (size_t)m * (size_t)n * 2, "out"},
+      {xq, (size_t)m * (size_t)k, "xq"},
+      {wq_pre, (size_t)padded_bytes(n, k), "wq_pre"},
+      {x_scales, (size_t)m * (size_t)nb * 4, "x_scales"},
+      {w_scales, (size_t)n * (size_t)nb * 4, "w_scales"},
+      {bias, bias ? (size_t)n * 2 : 0, "bias"},
+  };
+  const char* other = nullptr;
+  const char* a = find_overlap(rg, 6, &other);
+  if (a && strcmp(a, "out") == 0) return fail(HQ_ERR_INVALID_ARGUMENT, "out overlaps %s", other);
+  st = check_device();
+  if (st != HQ_OK) return st;
+  hq::GemmArgs g{xq, wq_pre, x_scales, w_scales, out, (int)m, (int)n, (int)k, 1, 1,
+                 bias, bias ? hq::kBiasBF16 : hq::kBiasNone, nullptr, nullptr, 0, (int)nb};
+  (void)hipGetLastError();
+  return launched(hq::launch_gemm_bsf(g, xf, wf, stream), "hq_gemm_a8w8_blockscaled_preshuffled");
+}
+
 }  // extern "C"

@@ -401,6 +401,32 @@ def test_quantize_preshuffled_valid_calls_reach_device_gate(hq):
     assert _qpre(hq, rows=40, cols=16, s=fake(1, 64 * 128)) == U      # right after the 64 x 128 padded q_pre
 
 
+def _bs_pre(hq, bs=128, m=64, n=128, k=256, out=fake(4), bias=None, xs=fake(2), wp=fake(1)):
+    return hq.load().hq_gemm_a8w8_blockscaled_preshuffled(fake(0), 0, wp, 0, xs, fake(3), bs, m, n, k, bias, out, None)
+
+
+def test_blockscaled_preshuffled_validation(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    assert _bs_pre(hq, bs=64) == E and "blocks of 128" in hq.hq_last_error()
+    assert _bs_pre(hq, k=24) == E
+    assert _bs_pre(hq, out=fake(4, 2)) == E            # out must be 16-byte aligned
+    assert _bs_pre(hq, wp=fake(1, 8)) == E
+    assert _bs_pre(hq, xs=fake(2, 2)) == E
+    assert _bs_pre(hq, bias=fake(5, 1)) == E
+    assert _bs_pre(hq, wp=ctypes.c_void_p(0)) == E
+    # the pre-shuffled weight is hq_preshuffled_bytes(128, 256) = 32768 bytes: out inside it overlaps
+    assert _bs_pre(hq, out=fake(1, 32768 - 16)) == E and "overlaps" in hq.hq_last_error()
+    assert _bs_pre(hq, m=0) == hq.HQ_OK
+
+
+@no_gpu
+def test_blockscaled_preshuffled_valid_calls_reach_device_gate(hq):
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    assert _bs_pre(hq) == U
+    assert _bs_pre(hq, bias=fake(5), k=272) == U
+    assert _bs_pre(hq, out=fake(1, 32768)) == U
+
+
 def test_preshuffle_and_ring_validation(hq):
     lib = hq.load()
     E = hq.HQ_ERR_INVALID_ARGUMENT

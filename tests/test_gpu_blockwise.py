@@ -307,3 +307,102 @@ def test_blockscaled_gemm_bias_exact(hq):
     assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
     want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(host(out), want)
+
+
+# ---------------------------------------------------------------------------
+# block-scaled GEMM over the pre-shuffled weight (blocks of 128)
+# ---------------------------------------------------------------------------
+def _bs_pre(hq, xq, xf, wq, wf, xs, ws, bias=None):
+    n = wq.shape[0]
+    pre = hq.hq_preshuffle_weight(dev_u8(wq))
+    return hq.hq_gemm_a8w8_blockscaled_preshuffled(dev_u8(xq), xf, pre, wf, dev_f32(xs), dev_f32(ws), n,
+                                                   bias=None if bias is None else dev_bf16(bias))
+
+
+# (m, n, k): one tile; ragged M, N and K (a partial last block); a single row
+# (the 64 x 128 tile); the 128 x 128 and 256 x 128 tiles over several K blocks
+PSHAPES = [(128, 128, 128), (300, 520, 1040), (1, 96, 256), (130, 260, 272), (520, 384, 2048), (1100, 700, 640)]
+
+
+@pytest.mark.parametrize("shape", PSHAPES)
+@pytest.mark.parametrize("formats", PAIRS)
+def test_blockscaled_preshuffled_narrow_strict(hq, shape, formats):
+    m, n, k = shape
+    xf, wf = formats
+    rng = np.random.default_rng(_seed(shape, formats, "pre-narrow"))
+    xq, wq = narrow_codes(rng, (m, k), xf), narrow_codes(rng, (n, k), wf)
+    nb = B.block_count(k, 128)
+    xs, ws = _block_scales(rng, m, nb), _block_scales(rng, n, nb)
+    out = _bs_pre(hq, xq, xf, wq, wf, xs, ws)
+    torch.cuda.synchronize()
+    _check_bs_gemm(host(out), xq, xf, wq, wf, xs, ws, 128, strict_only=True)
+
+
+@pytest.mark.parametrize("shape", [(300, 520, 1040), (64, 4000, 512), (1030, 1030, 1152)])
+def test_blockscaled_preshuffled_full_range(hq, shape):
+    m, n, k = shape
+    rng = np.random.default_rng(_seed(shape, "pre-full"))
+    finite = np.array([c for c in range(256) if np.isfinite(fp8.decode_table(fp8.E4M3)[c])], np.uint8)
+    xq, wq = rng.choice(finite, (m, k)), rng.choice(finite, (n, k))
+    nb = B.block_count(k, 128)
+    xs = (_block_scales(rng, m, nb) * 1e-3).astype(np.float32)
+    ws = (_block_scales(rng, n, nb) * 1e-3).astype(np.float32)
+    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
+    torch.cuda.synchronize()
+    pairs = np.stack([rng.integers(0, m, 6000), rng.integers(0, n, 6000)], axis=1)
+    _check_bs_gemm(host(out), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, 128, pairs=pairs)
+
+
+def test_blockscaled_preshuffled_exact_with_bias(hq):
+    """Exact block partials, power-of-two scales and integer biases: every sum
+    is exact in float32, so the output is the bf16 rounding of the oracle's
+    value, bit for bit."""
+    rng = np.random.default_rng(43)
+    m, n, k = 200, 136, 384
+    xq, wq = narrow_codes(rng, (m, k), fp8.E4M3), narrow_codes(rng, (n, k), fp8.E5M2)
+    xs = np.ldexp(1.0, rng.integers(-2, 2, (m, 3))).astype(np.float32)
+    ws = np.ldexp(1.0, rng.integers(-2, 2, (n, 3))).astype(np.float32)
+    bias = workloads.to_bf16_bits(rng.integers(-64, 65, n).astype(np.float32))
+    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, bias=bias)
+    torch.cuda.synchronize()
+    ref = B.gemm_blockscaled(xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, 128, bias=bias)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(host(out), want)
+
+
+def test_blockscaled_preshuffled_bench_size(hq):
+    """The benchmark's 4096^3 block-scaled pass (blocks of 128, the PTPC
+    operands) through the pre-shuffled weight: 4096 sampled outputs against the
+    oracle; and, as the same arithmetic in the same order, the same bits as the
+    row-major entry point."""
+    xb, wb = workloads.ptpc_square()
+    xq, xs, _ = hq.hq_quantize_fp8_blockwise(dev_bf16(xb), fp8.E4M3, 128)
+    wq, ws, _ = hq.hq_quantize_fp8_blockwise(dev_bf16(wb), fp8.E4M3, 128)
+    pre = hq.hq_preshuffle_weight(wq)
+    out = hq.hq_gemm_a8w8_blockscaled_preshuffled(xq, fp8.E4M3, pre, fp8.E4M3, xs, ws, 4096)
+    row_major = hq.hq_gemm_a8w8_blockscaled(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, 128)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(14)
+    pairs = np.stack([rng.integers(0, 4096, 4096), rng.integers(0, 4096, 4096)], axis=1)
+    pairs[:4] = [[0, 0], [4095, 4095], [0, 4095], [4095, 0]]
+    _check_bs_gemm(host(out), host(xq), fp8.E4M3, host(wq), fp8.E4M3, host(xs), host(ws), 128, pairs=pairs)
+    assert torch.equal(out.view(torch.int16), row_major.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [(4096, 1024, 384), (2560, 2560, 272)])
+def test_blockscaled_preshuffled_large_tiles_sampled(hq, shape):
+    """Shapes whose launch takes the 128 x 128 tile (4096 x 1024) and the
+    256 x 128 tile (2560 x 2560, with a partial last block): narrow codes, 8192
+    sampled outputs within the strict bound, tile edges included."""
+    m, n, k = shape
+    rng = np.random.default_rng(_seed(shape, "pre-large"))
+    xq, wq = narrow_codes(rng, (m, k), fp8.E4M3), narrow_codes(rng, (n, k), fp8.E4M3)
+    nb = B.block_count(k, 128)
+    xs, ws = _block_scales(rng, m, nb), _block_scales(rng, n, nb)
+    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
+    torch.cuda.synchronize()
+    pairs = np.stack([rng.integers(0, m, 8192), rng.integers(0, n, 8192)], axis=1)
+    edges = np.array([[r, c] for r in (0, 127, 128, 255, 256, m - 1) for c in (0, 127, 128, n - 1)])
+    pairs[:len(edges)] = edges
+    _check_bs_gemm(host(out), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, 128, pairs=pairs, strict_only=True)
