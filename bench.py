@@ -321,8 +321,8 @@ def blockwise_timings(torch, hq, lib):
     """Block-wise path on the PTPC operands: X bf16 [4096, 4096] quantized in
     blocks of 32 and 128 along K (codes + one float32 scale and amax per block),
     and the block-scaled GEMM 4096^3 at blocks of 32, 64 and 128 on the codes
-    of X and W quantized at that block size (blocks of 128 also through the
-    pre-shuffled weight). Rotating sets as elsewhere."""
+    of X and W quantized at that block size, over the row-major and over the
+    pre-shuffled weight. Rotating sets as elsewhere."""
     import workloads
     P = ctypes.c_void_p
     E4M3, BF16 = hq.HQ_E4M3, hq.HQ_BF16
@@ -365,22 +365,21 @@ def blockwise_timings(torch, hq, lib):
         valu_floor_us = 2.0 * M * N * (K // bs) / (16 * 4 * 256 * 2.4e9) * 1e6
         gemm[f"bs{bs}"] = {"us": round(ms * 1e3, 3), "tflops": round(tf, 1), "frac_mfma": round(tf / FP8_PEAK_TFLOPS, 4),
                            "fold_valu_floor_us": round(valu_floor_us, 1)}
-        if bs == 128:
-            # the same product through the pre-shuffled weight (the plain GEMM's data path)
-            psets = [(a_, hq.hq_preshuffle_weight(b_), c_, d_, o_) for a_, b_, c_, d_, o_ in sets]
+        # the same product through the pre-shuffled weight (the plain GEMM's data path)
+        psets = [(a_, hq.hq_preshuffle_weight(b_), c_, d_, o_) for a_, b_, c_, d_, o_ in sets]
 
-            def plaunch(i, h, psets=psets):
-                a_, p_, c_, d_, o_ = psets[i % 4]
-                st = lib.hq_gemm_a8w8_blockscaled_preshuffled(P(a_.data_ptr()), E4M3, P(p_.data_ptr()), E4M3,
-                                                              P(c_.data_ptr()), P(d_.data_ptr()), 128, M, N, K, None,
-                                                              P(o_.data_ptr()), h)
-                assert st == 0, hq.hq_last_error()
-            ms = time_graph(torch, plaunch, 8)
-            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-            gemm["bs128_preshuffled"] = {"us": round(ms * 1e3, 3), "tflops": round(tf, 1),
-                                         "frac_mfma": round(tf / FP8_PEAK_TFLOPS, 4),
-                                         "fold_valu_floor_us": round(valu_floor_us, 1)}
-            del psets
+        def plaunch(i, h, bs=bs, psets=psets):
+            a_, p_, c_, d_, o_ = psets[i % 4]
+            st = lib.hq_gemm_a8w8_blockscaled_preshuffled(P(a_.data_ptr()), E4M3, P(p_.data_ptr()), E4M3,
+                                                          P(c_.data_ptr()), P(d_.data_ptr()), bs, M, N, K, None,
+                                                          P(o_.data_ptr()), h)
+            assert st == 0, hq.hq_last_error()
+        ms = time_graph(torch, plaunch, 8)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        gemm[f"bs{bs}_preshuffled"] = {"us": round(ms * 1e3, 3), "tflops": round(tf, 1),
+                                       "frac_mfma": round(tf / FP8_PEAK_TFLOPS, 4),
+                                       "fold_valu_floor_us": round(valu_floor_us, 1)}
+        del psets
         del sets
     return {"shape": "X, W bf16 [4096, 4096] (PTPC operands), E4M3, blocks along K", "quantize_x": quant,
             "gemm_4096": gemm}

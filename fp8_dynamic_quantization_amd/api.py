@@ -185,7 +185,7 @@ def hq_gemm_a8w8_blockscaled(xq: torch.Tensor, xf: int, wq: torch.Tensor, wf: in
 def hq_gemm_a8w8_blockscaled_preshuffled(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
                                          x_scales: torch.Tensor, w_scales: torch.Tensor, n: int, block_size: int = 128,
                                          bias=None, out=None, stream=None) -> torch.Tensor:
-    """Block-scaled GEMM (blocks of 128) of row-major codes xq [m, k] and the
+    """Block-scaled GEMM (blocks of 32, 64 or 128) of row-major codes xq [m, k] and the
     pre-shuffled weight wq_pre (hq_preshuffle_weight of [n, k]) with block
     scales [m, nb], [n, nb] and an optional bf16 bias [n]; returns bf16 [m, n]."""
     xq = xq.contiguous()

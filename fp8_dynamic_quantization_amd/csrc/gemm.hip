@@ -140,17 +140,23 @@ struct BsCfg {
 
 // KTAIL: K is not a multiple of 128, so the A chunks past K are zeroed on their
 // way to LDS; without it the K loop has no masking at all.
-// BSF: the block-scaled form with blocks of 128 along K (one K step): x_scale is
-// [m, nblk] and w_scale [n, nblk] row-major; each step's MFMAs start from zero
-// and their sums are folded as acc = fma(t, fl32(xs[m, kb] * ws[n, kb]), acc),
-// the step's scales staged in LDS one step ahead; the epilogue then applies no
-// scale (only the bias).
-template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, bool BSF>
+// BSZ > 0: the block-scaled form with blocks of BSZ (32, 64 or 128) along K:
+// x_scale is [m, nblk] and w_scale [n, nblk] row-major; each block's MFMA sums
+// start from zero and are folded as acc = fma(t, fl32(xs[m, b] * ws[n, b]), acc)
+// in block order, the step's scales staged in LDS one step ahead; the epilogue
+// then applies no scale (only the bias). Blocks narrower than the 128-deep MFMA
+// take one MFMA per block, whose per-lane E8M0 operand scales are 2^0 for the
+// block's 32-element chunks and 2^-127 for the others: their products are then
+// scaled by 2^-254 and vanish below float32's range.
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, int BSZ>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m0, int row_end, int n0,
                                           const uint8_t* __restrict__ wq, const float* __restrict__ ws) {
   using C = BsCfg<BM, TN, WM>;
+  constexpr bool BSF = BSZ > 0;
+  constexpr int NB = BSF ? kBK / BSZ : 1;  // scale blocks per K step
+  static_assert(!BSF || BSZ == 32 || BSZ == 64 || BSZ == 128, "block size");
   static_assert(C::kAVec <= C::kIM && C::kIN <= C::kIM, "slot schedule: at most one A piece and two B halves per slot");
-  static_assert(!BSF || BM + C::kBN <= C::kThreads, "block scales: one per thread per step");
+  static_assert(!BSF || BM + C::kBN <= C::kThreads, "block scales: one row or column per thread per step");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront column
@@ -180,7 +186,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(wq + (size_t)nbw_c * nkb * kFragBytes), (short)0, min(C::kIN, nfrag - nbw_c) * nkb * kFragBytes,
       kRsrcFlags);
-  const int b_vo = lane * 16;
+  // Blocks narrower than 128 (NB > 1) need each operand byte at the K
+  // position the MFMA's block scales assume: within a lane's 32 bytes, lane
+  // group g = l / 16 holds K 16g .. 16g+15 in bytes 0-15 and K 64+16g .. +15 in
+  // bytes 16-31 (scale block b = K 32b .. 32b+31 takes its scale from lane group
+  // b). So the weight halves come from pieces (g % 2, g / 2) and (g % 2, 2 + g / 2)
+  // of the pre-shuffled fragment, and the activation from chunks g and g + 4 of
+  // the row; otherwise (the plain order) half h and chunks 2g, 2g + 1.
+  const int kg = lane >> 4, slot16 = (lane & 15) * 16;
+  const int b_vo0 = NB > 1 ? (kg & 1) * 1024 + (kg >> 1) * 256 + slot16 : lane * 16;
+  const int b_vo1 = NB > 1 ? (kg & 1) * 1024 + (2 + (kg >> 1)) * 256 + slot16 : lane * 16 + 1024;
 
   // The epilogue's scales go to LDS (after the two A stages) at the start, so
   // their load latency hides behind the K loop: x_scale of the tile's BM rows,
@@ -203,29 +218,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
     for (int t = tid; t < C::kBN; t += C::kThreads) s_bias[t] = bias_at(a, min(n0 + t, a.n - 1), bsc);
   }
 
-  // Block scales (BSF): thread t < BM holds xs of tile row t, thread BM + c
-  // holds ws of tile column c, for one K block; a step's values sit in LDS stage
-  // (step % 2) after the tile's epilogue data.
+  // Block scales (BSZ > 0): thread t < BM holds the NB scales of tile row t,
+  // thread BM + c those of tile column c, for one K step; a step's values sit in
+  // LDS stage (step % 2), [row or column][NB], after the tile's epilogue data.
+  // Blocks past the last one (the K tail) get scale 0: their codes are zero.
+  typedef float bsv_t __attribute__((ext_vector_type(NB)));
   float* s_bsf = reinterpret_cast<float*>(lds + C::kLdsBytes);
-  auto bsf_load = [&](int kbq) -> float {
-    if (tid < BM) return a.x_scale[(size_t)min(m0 + tid, row_end - 1) * a.nblk + kbq];
-    if (tid < BM + C::kBN) return ws[(size_t)min(n0 + tid - BM, a.n - 1) * a.nblk + kbq];
-    return 0.0f;
+  auto bsf_load = [&](int kbq) -> bsv_t {
+    bsv_t v;
+    const float* src = tid < BM ? a.x_scale + (size_t)min(m0 + tid, row_end - 1) * a.nblk
+                                : ws + (size_t)min(n0 + tid - BM, a.n - 1) * a.nblk;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) v[b] = (tid < BM + C::kBN && kbq * NB + b < a.nblk) ? src[kbq * NB + b] : 0.0f;
+    return v;
   };
-  auto bsf_store = [&](int stage, float v) {
-    if (tid < BM + C::kBN) s_bsf[stage * (BM + C::kBN) + tid] = v;
+  auto bsf_store = [&](int stage, bsv_t v) {
+    if (tid < BM + C::kBN) *reinterpret_cast<bsv_t*>(s_bsf + (stage * (BM + C::kBN) + tid) * NB) = v;
   };
   // the lane's rows (16 i + l % 16 of its wavefront row) and its 8 columns,
   // one base each so every read of a step is a constant offset from it
-  const float* xs_lane = s_bsf + wrow * C::kWR + (lane & 15);
-  const float* ws_lane = s_bsf + BM + wave * TN + 8 * (lane >> 4);
+  const float* xs_lane = s_bsf + (wrow * C::kWR + (lane & 15)) * NB;
+  const float* ws_lane = s_bsf + (BM + wave * TN + 8 * (lane >> 4)) * NB;
+  // E8M0 operand scale of block b for this lane's 32-element K chunk (l / 16)
+  auto blk_sel = [&](int b) -> int { return ((lane >> 4) / (4 / NB)) == b ? 127 : 0; };
 
   // MFMA-order reads: fragment i is rows i*16 .. i*16+15; lane l reads row
   // i*16 + l%16, chunks 2*(l/16) and 2*(l/16)+1; the swizzle again only depends
   // on the lane, fragment i adds i*2048.
-  const int rl = lane & 15, cg = 2 * (lane >> 4);
-  const int a_rd0 = wrow * C::kWR * kBK + rl * kBK + ((cg ^ (rl & 7)) << 4);
-  const int a_rd1 = wrow * C::kWR * kBK + rl * kBK + (((cg + 1) ^ (rl & 7)) << 4);
+  const int rl = lane & 15, cg0 = NB > 1 ? kg : 2 * kg, cg1 = NB > 1 ? kg + 4 : 2 * kg + 1;
+  const int a_rd0 = wrow * C::kWR * kBK + rl * kBK + ((cg0 ^ (rl & 7)) << 4);
+  const int a_rd1 = wrow * C::kWR * kBK + rl * kBK + ((cg1 ^ (rl & 7)) << 4);
 
   v4f acc[C::kIM][C::kIN];
 #pragma unroll
@@ -249,7 +271,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
       (!KTAIL || (VALID)) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
 #define HQ_LOAD_B_HALF(KB, FB, H)                                                                 \
-  FB[H] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_vo + ((H) & 1) * 1024,               \
+  FB[H] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, ((H) & 1) ? b_vo1 : b_vo0,             \
                                                          ((H) >> 1) * nkb * kFragBytes + (KB) * kFragBytes, 0))
 #define HQ_READ_A(BASE, I, LO, HI)                                         \
   do {                                                                     \
@@ -258,12 +280,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   } while (0)
 #define HQ_V8(LO, HI) v8i{(int)LO.x, (int)LO.y, (int)LO.z, (int)LO.w, (int)HI.x, (int)HI.y, (int)HI.z, (int)HI.w}
 
-  // BSF fold of slot I's zero-start sums, issued in the next slot after that
-  // slot's MFMAs: acc = fma(t, fl32(xs * ws), acc), blocks in K order.
+  // Block-scaled fold of slot I's zero-start sums (block by block, in K order):
+  // acc = fma(t, fl32(xs * ws), acc). Issued in the next slot after that slot's
+  // MFMAs when at most two blocks share a step; with four (blocks of 32) in the
+  // slot itself, which halves the sums held live.
+  constexpr bool kFoldLate = NB <= 2;
 #define HQ_FOLD(I, XS)                                                                                 \
-  _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                                   \
-    _Pragma("unroll") for (int r = 0; r < 4; ++r)                                                      \
-      acc[(I)][j][r] = fmaf(tp_[(I) & 1][j][r], (XS) * wsl_[j][r], acc[(I)][j][r])
+  _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                       \
+    _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                                 \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r)                                                    \
+        acc[(I)][j][r] = fmaf(tp_[(I) & 1][b][j][r], (XS)[b] * wsl_[b][j][r], acc[(I)][j][r])
 
   // One K step, as kIM slots. Slot i: read an upcoming A fragment from LDS, then memory
   // operations, then the kIN MFMAs of A fragment i. Slots 0 .. kIN-1 load the B
@@ -280,15 +306,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
     const uint8_t* cur_ = lds + (BUF) * C::kABytes;                                                    \
     uint4 lo0_, hi0_, lo1_, hi1_, lo2_, hi2_;                                                          \
     bool st_valid_ = ra_valid;                                                                         \
-    const float bs_nx_ = BSF ? bsf_load(nb1_) : 0.0f;                                                  \
-    float wsl_[BSF ? C::kIN : 1][4];                                                                   \
-    v4f tp_[2][C::kIN];                                                                                \
-    float xs_prev_ = 0.0f;                                                                             \
+    bsv_t bs_nx_{};                                                                                    \
+    if constexpr (BSF) bs_nx_ = bsf_load(nb1_);                                                        \
+    float wsl_[NB][BSF ? C::kIN : 1][4];                                                               \
+    v4f tp_[2][NB][C::kIN];                                                                            \
+    bsv_t xs_prev_{};                                                                                  \
     if constexpr (BSF) {                                                                               \
-      _Pragma("unroll") for (int j = 0; j < C::kIN; ++j) {                                             \
-        const v4f w_ = *reinterpret_cast<const v4f*>(ws_lane + (BUF) * (BM + C::kBN) + 32 * (j >> 1) + 4 * (j & 1)); \
-        _Pragma("unroll") for (int r = 0; r < 4; ++r) wsl_[j][r] = w_[r];                              \
-      }                                                                                                \
+      _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                               \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                                \
+          const bsv_t w_ = *reinterpret_cast<const bsv_t*>(                                            \
+              ws_lane + ((BUF) * (BM + C::kBN) + 32 * (j >> 1) + 4 * (j & 1) + r) * NB);               \
+          _Pragma("unroll") for (int b = 0; b < NB; ++b) wsl_[b][j][r] = w_[b];                        \
+        }                                                                                              \
     }                                                                                                  \
     HQ_READ_A(cur_, 0, lo0_, hi0_);                                                                    \
     if (kFaDepth == 3) HQ_READ_A(cur_, 1, lo1_, hi1_);                                                 \
@@ -315,15 +344,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
       const v8i fa_ = kFaDepth == 2 ? ((i & 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo0_, hi0_))                \
                     : (i % 3 == 0) ? HQ_V8(lo0_, hi0_) : (i % 3 == 1) ? HQ_V8(lo1_, hi1_) : HQ_V8(lo2_, hi2_); \
       if constexpr (BSF) {                                                                             \
-        _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                             \
-          tp_[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                            \
-              HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, v4f{0.f, 0.f, 0.f, 0.f}, WF, XF, 0, 0, 0, 0);    \
-        if (i > 0) {                                                                                   \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                 \
+          _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                           \
+            tp_[i & 1][b][j] = NB == 1                                                                 \
+                ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, \
+                                                                   v4f{0.f, 0.f, 0.f, 0.f}, WF, XF, 0, 0, 0, 0) \
+                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, \
+                                                                   v4f{0.f, 0.f, 0.f, 0.f}, WF, XF, 0, blk_sel(b), \
+                                                                   0, blk_sel(b));                     \
+        if (kFoldLate && i > 0) {                                                                      \
           HQ_FOLD(i - 1, xs_prev_);                                                                    \
           /* the empty asm keeps the folds in this slot, so two slots' sums are live at most */        \
           _Pragma("unroll") for (int j = 0; j < C::kIN; ++j) asm volatile("" : "+v"(acc[i - 1][j]));   \
         }                                                                                              \
-        xs_prev_ = xs_lane[(BUF) * (BM + C::kBN) + 16 * i];                                            \
+        xs_prev_ = *reinterpret_cast<const bsv_t*>(xs_lane + ((BUF) * (BM + C::kBN) + 16 * i) * NB);   \
+        if (!kFoldLate) {                                                                              \
+          HQ_FOLD(i, xs_prev_);                                                                        \
+          _Pragma("unroll") for (int j = 0; j < C::kIN; ++j) asm volatile("" : "+v"(acc[i][j]));       \
+        }                                                                                              \
       } else {                                                                                         \
         _Pragma("unroll") for (int j = 0; j < C::kIN; ++j)                                             \
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HQ_V8(FBC[2 * j], FBC[2 * j + 1]), fa_, \
@@ -332,7 +370,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
       __builtin_amdgcn_sched_barrier(0);                                                               \
     }                                                                                                  \
     if constexpr (BSF) {                                                                               \
-      HQ_FOLD(C::kIM - 1, xs_prev_);                                                                   \
+      if (kFoldLate) HQ_FOLD(C::kIM - 1, xs_prev_);                                                    \
       bsf_store((BUF) ^ 1, bs_nx_);                                                                    \
     }                                                                                                  \
     __syncthreads();                                                                                   \
@@ -458,18 +496,18 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(GemmArgs a, int tiles_m,
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM;
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL, false>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, 0>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
 }
 
 // Block-scaled form (blocks of 128 along K) on the same data path.
-template <int XF, int WF, int BM, int TN, int WM, bool KTAIL>
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, int BSZ>
 __global__ __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bsf_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   using C = BsCfg<BM, TN, WM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes + C::kBsfBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes + C::kBsfBytes * (128 / BSZ)];
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM;
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL, true>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, BSZ>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
 }
 
 // Grouped: a linear tile id enumerates, per expert in order, its row tiles x the
@@ -514,7 +552,7 @@ __global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, cons
     ae.bias = static_cast<const uint8_t*>(a.bias) + (size_t)e * a.n * (a.bias_kind == kBiasBF16 ? 2 : 1);
     if (a.bias_scale) ae.bias_scale = a.bias_scale + e;
   }
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL, false>(ae, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, 0>(ae, lds, m0, row_end, tn * C::kBN, a.wq_pre + e * expert_bytes, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -845,20 +883,20 @@ static hipError_t launch_grouped_cfg(const GemmArgs& a, const int32_t* offsets, 
 // per wavefront, room for the fold's sums and scales), chosen by the cost rule
 // of pick_tile with their measured relative throughputs (0.83, 0.81, 0.67 of the
 // plain 256 x 256 tile).
-template <int XF, int WF, int BM, int TN, int WM>
+template <int XF, int WF, int BM, int TN, int WM, int BSZ>
 static hipError_t launch_bsf_cfg(const GemmArgs& a, hipStream_t st) {
   using C = BsCfg<BM, TN, WM>;
   const int tiles_m = (a.m + BM - 1) / BM, tiles_n = (a.n + C::kBN - 1) / C::kBN;
   if (a.k % kBK == 0)
-    hipLaunchKernelGGL((gemm_bsf_kernel<XF, WF, BM, TN, WM, false>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, st,
-                       a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_bsf_kernel<XF, WF, BM, TN, WM, false, BSZ>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       st, a, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_bsf_kernel<XF, WF, BM, TN, WM, true>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0, st,
-                       a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_bsf_kernel<XF, WF, BM, TN, WM, true, BSZ>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
+                       st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int XF, int WF>
+template <int XF, int WF, int BSZ>
 static hipError_t launch_bsf_t(const GemmArgs& a, hipStream_t st) {
   const struct {
     int bm;
@@ -874,9 +912,9 @@ static hipError_t launch_bsf_t(const GemmArgs& a, hipStream_t st) {
       best_cost = cost;
     }
   }
-  if (best == 0) return launch_bsf_cfg<XF, WF, 256, 32, 2>(a, st);
-  if (best == 1) return launch_bsf_cfg<XF, WF, 128, 32, 1>(a, st);
-  return launch_bsf_cfg<XF, WF, 64, 32, 1>(a, st);
+  if (best == 0) return launch_bsf_cfg<XF, WF, 256, 32, 2, BSZ>(a, st);
+  if (best == 1) return launch_bsf_cfg<XF, WF, 128, 32, 1, BSZ>(a, st);
+  return launch_bsf_cfg<XF, WF, 64, 32, 1, BSZ>(a, st);
 }
 
 // Up to this many rows the weight-streaming kernel runs the GEMM.
@@ -917,8 +955,10 @@ hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_
 #undef CALL
 }
 
-hipError_t launch_gemm_bsf(const GemmArgs& a, int xf, int wf, hipStream_t st) {
-#define CALL(X, W) return launch_bsf_t<X, W>(a, st)
+hipError_t launch_gemm_bsf(const GemmArgs& a, int xf, int wf, int bs, hipStream_t st) {
+#define CALL(X, W)                                            \
+  return bs == 32 ? launch_bsf_t<X, W, 32>(a, st)             \
+         : bs == 64 ? launch_bsf_t<X, W, 64>(a, st) : launch_bsf_t<X, W, 128>(a, st)
   HQ_DISPATCH_FMT_PAIR(xf, wf, CALL);
 #undef CALL
 }

@@ -623,8 +623,8 @@ hq_status hq_gemm_a8w8_blockscaled_preshuffled(const uint8_t* xq, int xf, const 
                                                hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, m, n, k);
   if (st != HQ_OK) return st;
-  if (block_size != 128)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "the pre-shuffled block-scaled GEMM takes blocks of 128, got %d", block_size);
+  if (block_size != 32 && block_size != 64 && block_size != 128)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "block_size must be 32, 64 or 128, got %d", block_size);
   if (m == 0 || n == 0) return ok();
   if (!xq || !wq_pre || !x_scales || !w_scales || !out)
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre, x_scales, w_scales and out must be non-NULL");
@@ -632,7 +632,7 @@ hq_status hq_gemm_a8w8_blockscaled_preshuffled(const uint8_t* xq, int xf, const 
     return fail(HQ_ERR_INVALID_ARGUMENT, "xq, wq_pre and out must be 16-byte aligned");
   if (!aligned(x_scales, 4) || !aligned(w_scales, 4) || (bias && !aligned(bias, 2)))
     return fail(HQ_ERR_INVALID_ARGUMENT, "the scales must be 4-byte and bias 2-byte aligned");
-  const int64_t nb = (k + 127) / 128;
+  const int64_t nb = (k + block_size - 1) / block_size;
   const Range rg[] = {
       {out, (size_t)m * (size_t)n * 2, "out"},
       {xq, (size_t)m * (size_t)k, "xq"},
@@ -649,7 +649,7 @@ hq_status hq_gemm_a8w8_blockscaled_preshuffled(const uint8_t* xq, int xf, const 
   hq::GemmArgs g{xq, wq_pre, x_scales, w_scales, out, (int)m, (int)n, (int)k, 1, 1,
                  bias, bias ? hq::kBiasBF16 : hq::kBiasNone, nullptr, nullptr, 0, (int)nb};
   (void)hipGetLastError();
-  return launched(hq::launch_gemm_bsf(g, xf, wf, stream), "hq_gemm_a8w8_blockscaled_preshuffled");
+  return launched(hq::launch_gemm_bsf(g, xf, wf, block_size, stream), "hq_gemm_a8w8_blockscaled_preshuffled");
 }
 
 }  // extern "C"

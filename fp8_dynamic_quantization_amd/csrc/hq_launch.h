@@ -85,8 +85,8 @@ struct GemmArgs {
   const float* bias_scale; // [1]: dequant scale of an FP8 bias
   const float* out_scale;  // [1] or null
   int out_fmt;             // kE4M3 / kE5M2 (with out_scale)
-  // Block-scaled form only (launch_gemm_bsf): K blocks of 128; x_scale is then
-  // [m, nblk] and w_scale [n, nblk], row-major.
+  // Block-scaled form only (launch_gemm_bsf): the number of K blocks; x_scale
+  // is then [m, nblk] and w_scale [n, nblk], row-major.
   int nblk;
 };
 
@@ -121,9 +121,10 @@ struct BlockGemmArgs {
   int m, n, k, nb;
 };
 hipError_t launch_gemm_blockscaled(const BlockGemmArgs& a, int xf, int wf, int bs, hipStream_t st);
-// Block-scaled GEMM with blocks of 128 along K over the pre-shuffled weight
-// (the plain GEMM's data path, each block's sums folded with its two scales).
-hipError_t launch_gemm_bsf(const GemmArgs& a, int xf, int wf, hipStream_t st);
+// Block-scaled GEMM with blocks of bs (32, 64, 128) along K over the
+// pre-shuffled weight (the plain GEMM's data path, each block's sums folded
+// with its two scales).
+hipError_t launch_gemm_bsf(const GemmArgs& a, int xf, int wf, int bs, hipStream_t st);
 
 // Grouped form: rows [offsets[e], offsets[e+1]) use expert e's weight at
 // wq_pre + e * preshuffled_bytes(n, k) and scales w_scale + e * (per_col ? n : 1).

@@ -248,13 +248,16 @@ hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq,
                                    int64_t m, int64_t n, int64_t k, const uint16_t* bias,
                                    uint16_t* out, hipStream_t stream);
 
-/* hq_gemm_a8w8_blockscaled for blocks of 128 along K with the weight
- * pre-shuffled (hq_preshuffle_weight of WQ [n, k]; as in hq_gemm_a8w8): the
- * same operation and the same per-block fold in K order,
+/* hq_gemm_a8w8_blockscaled with the weight pre-shuffled (hq_preshuffle_weight
+ * of WQ [n, k]; as in hq_gemm_a8w8): the same operation and the same per-block
+ * fold in K order,
  *   out[m, n] = bf16( fl32-fold over b of fma(S_b[m,n], fl32(xs[m,b] * ws[n,b]), . ) + bias[n] )
  * with S_b the float32 MFMA sum over block b, on the plain GEMM's data path.
+ * Blocks of 128 give the same bits as hq_gemm_a8w8_blockscaled; blocks of 32
+ * and 64 sum each block on the 128-deep MFMA (the other chunks scaled out),
+ * within the same error bound.
  *   wq_pre      device, hq_preshuffled_bytes(n, k) bytes, 16-byte aligned
- *   block_size  must be 128; x_scales [m, ceil(k/128)], w_scales [n, ceil(k/128)]
+ *   block_size  32, 64 or 128; x_scales [m, ceil(k/bs)], w_scales [n, ceil(k/bs)]
  *   out         device bf16 [m, n], 16-byte aligned
  * All other arguments and requirements are those of hq_gemm_a8w8_blockscaled. */
 hq_status hq_gemm_a8w8_blockscaled_preshuffled(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,

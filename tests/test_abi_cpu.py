@@ -407,7 +407,7 @@ def _bs_pre(hq, bs=128, m=64, n=128, k=256, out=fake(4), bias=None, xs=fake(2), 
 
 def test_blockscaled_preshuffled_validation(hq):
     E = hq.HQ_ERR_INVALID_ARGUMENT
-    assert _bs_pre(hq, bs=64) == E and "blocks of 128" in hq.hq_last_error()
+    assert _bs_pre(hq, bs=16) == E and "block_size" in hq.hq_last_error()
     assert _bs_pre(hq, k=24) == E
     assert _bs_pre(hq, out=fake(4, 2)) == E            # out must be 16-byte aligned
     assert _bs_pre(hq, wp=fake(1, 8)) == E
@@ -424,6 +424,7 @@ def test_blockscaled_preshuffled_valid_calls_reach_device_gate(hq):
     U = hq.HQ_ERR_UNSUPPORTED_DEVICE
     assert _bs_pre(hq) == U
     assert _bs_pre(hq, bias=fake(5), k=272) == U
+    assert _bs_pre(hq, bs=32) == U and _bs_pre(hq, bs=64, k=272) == U
     assert _bs_pre(hq, out=fake(1, 32768)) == U
 
 

@@ -312,10 +312,10 @@ def test_blockscaled_gemm_bias_exact(hq):
 # ---------------------------------------------------------------------------
 # block-scaled GEMM over the pre-shuffled weight (blocks of 128)
 # ---------------------------------------------------------------------------
-def _bs_pre(hq, xq, xf, wq, wf, xs, ws, bias=None):
+def _bs_pre(hq, xq, xf, wq, wf, xs, ws, bs=128, bias=None):
     n = wq.shape[0]
     pre = hq.hq_preshuffle_weight(dev_u8(wq))
-    return hq.hq_gemm_a8w8_blockscaled_preshuffled(dev_u8(xq), xf, pre, wf, dev_f32(xs), dev_f32(ws), n,
+    return hq.hq_gemm_a8w8_blockscaled_preshuffled(dev_u8(xq), xf, pre, wf, dev_f32(xs), dev_f32(ws), n, bs,
                                                    bias=None if bias is None else dev_bf16(bias))
 
 
@@ -325,47 +325,52 @@ PSHAPES = [(128, 128, 128), (300, 520, 1040), (1, 96, 256), (130, 260, 272), (52
 
 
 @pytest.mark.parametrize("shape", PSHAPES)
+@pytest.mark.parametrize("bs", [32, 64, 128])
 @pytest.mark.parametrize("formats", PAIRS)
-def test_blockscaled_preshuffled_narrow_strict(hq, shape, formats):
+def test_blockscaled_preshuffled_narrow_strict(hq, shape, bs, formats):
     m, n, k = shape
     xf, wf = formats
-    rng = np.random.default_rng(_seed(shape, formats, "pre-narrow"))
+    rng = np.random.default_rng(_seed(shape, bs, formats, "pre-narrow"))
     xq, wq = narrow_codes(rng, (m, k), xf), narrow_codes(rng, (n, k), wf)
-    nb = B.block_count(k, 128)
+    nb = B.block_count(k, bs)
     xs, ws = _block_scales(rng, m, nb), _block_scales(rng, n, nb)
-    out = _bs_pre(hq, xq, xf, wq, wf, xs, ws)
+    out = _bs_pre(hq, xq, xf, wq, wf, xs, ws, bs)
     torch.cuda.synchronize()
-    _check_bs_gemm(host(out), xq, xf, wq, wf, xs, ws, 128, strict_only=True)
+    _check_bs_gemm(host(out), xq, xf, wq, wf, xs, ws, bs, strict_only=True)
 
 
 @pytest.mark.parametrize("shape", [(300, 520, 1040), (64, 4000, 512), (1030, 1030, 1152)])
-def test_blockscaled_preshuffled_full_range(hq, shape):
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_blockscaled_preshuffled_full_range(hq, shape, bs):
     m, n, k = shape
-    rng = np.random.default_rng(_seed(shape, "pre-full"))
+    rng = np.random.default_rng(_seed(shape, bs, "pre-full"))
     finite = np.array([c for c in range(256) if np.isfinite(fp8.decode_table(fp8.E4M3)[c])], np.uint8)
     xq, wq = rng.choice(finite, (m, k)), rng.choice(finite, (n, k))
-    nb = B.block_count(k, 128)
+    nb = B.block_count(k, bs)
     xs = (_block_scales(rng, m, nb) * 1e-3).astype(np.float32)
     ws = (_block_scales(rng, n, nb) * 1e-3).astype(np.float32)
-    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
+    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs)
     torch.cuda.synchronize()
     pairs = np.stack([rng.integers(0, m, 6000), rng.integers(0, n, 6000)], axis=1)
-    _check_bs_gemm(host(out), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, 128, pairs=pairs)
+    _check_bs_gemm(host(out), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs, pairs=pairs)
 
 
-def test_blockscaled_preshuffled_exact_with_bias(hq):
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_blockscaled_preshuffled_exact_with_bias(hq, bs):
     """Exact block partials, power-of-two scales and integer biases: every sum
     is exact in float32, so the output is the bf16 rounding of the oracle's
-    value, bit for bit."""
-    rng = np.random.default_rng(43)
-    m, n, k = 200, 136, 384
+    value, bit for bit (for blocks of 32 and 64 this also shows that the chunks
+    scaled out of each block's MFMA contribute exactly nothing)."""
+    rng = np.random.default_rng(43 + bs)
+    m, n, k = 200, 136, 400
     xq, wq = narrow_codes(rng, (m, k), fp8.E4M3), narrow_codes(rng, (n, k), fp8.E5M2)
-    xs = np.ldexp(1.0, rng.integers(-2, 2, (m, 3))).astype(np.float32)
-    ws = np.ldexp(1.0, rng.integers(-2, 2, (n, 3))).astype(np.float32)
+    nb = B.block_count(k, bs)
+    xs = np.ldexp(1.0, rng.integers(-2, 2, (m, nb))).astype(np.float32)
+    ws = np.ldexp(1.0, rng.integers(-2, 2, (n, nb))).astype(np.float32)
     bias = workloads.to_bf16_bits(rng.integers(-64, 65, n).astype(np.float32))
-    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, bias=bias)
+    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, bs, bias=bias)
     torch.cuda.synchronize()
-    ref = B.gemm_blockscaled(xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, 128, bias=bias)
+    ref = B.gemm_blockscaled(xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, bs, bias=bias)
     assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
     want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(host(out), want)
@@ -391,18 +396,19 @@ def test_blockscaled_preshuffled_bench_size(hq):
 
 
 @pytest.mark.parametrize("shape", [(4096, 1024, 384), (2560, 2560, 272)])
-def test_blockscaled_preshuffled_large_tiles_sampled(hq, shape):
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_blockscaled_preshuffled_large_tiles_sampled(hq, shape, bs):
     """Shapes whose launch takes the 128 x 128 tile (4096 x 1024) and the
     256 x 128 tile (2560 x 2560, with a partial last block): narrow codes, 8192
     sampled outputs within the strict bound, tile edges included."""
     m, n, k = shape
-    rng = np.random.default_rng(_seed(shape, "pre-large"))
+    rng = np.random.default_rng(_seed(shape, bs, "pre-large"))
     xq, wq = narrow_codes(rng, (m, k), fp8.E4M3), narrow_codes(rng, (n, k), fp8.E4M3)
-    nb = B.block_count(k, 128)
+    nb = B.block_count(k, bs)
     xs, ws = _block_scales(rng, m, nb), _block_scales(rng, n, nb)
-    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
+    out = _bs_pre(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs)
     torch.cuda.synchronize()
     pairs = np.stack([rng.integers(0, m, 8192), rng.integers(0, n, 8192)], axis=1)
     edges = np.array([[r, c] for r in (0, 127, 128, 255, 256, m - 1) for c in (0, 127, 128, n - 1)])
     pairs[:len(edges)] = edges
-    _check_bs_gemm(host(out), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, 128, pairs=pairs, strict_only=True)
+    _check_bs_gemm(host(out), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bs, pairs=pairs, strict_only=True)
