@@ -336,7 +336,11 @@ def test_blockscaled_preshuffled_narrow_strict(hq, shape, bs, formats):
     xs, ws = _block_scales(rng, m, nb), _block_scales(rng, n, nb)
     out = _bs_pre(hq, xq, xf, wq, wf, xs, ws, bs)
     torch.cuda.synchronize()
-    _check_bs_gemm(host(out), xq, xf, wq, wf, xs, ws, bs, strict_only=True)
+    pairs = None
+    if m * n > 300 * 600:  # sampled, tile edges included
+        pairs = np.stack([rng.integers(0, m, 8192), rng.integers(0, n, 8192)], axis=1)
+        pairs[:16] = [[r, c] for r in (0, 63, 64, m - 1) for c in (0, 127, 128, n - 1)]
+    _check_bs_gemm(host(out), xq, xf, wq, wf, xs, ws, bs, pairs=pairs, strict_only=True)
 
 
 @pytest.mark.parametrize("shape", [(300, 520, 1040), (64, 4000, 512), (1030, 1030, 1152)])
