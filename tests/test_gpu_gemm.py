@@ -158,6 +158,24 @@ def _sample_pairs(rng, m, n, count):
     return np.concatenate([pairs, corners])
 
 
+def test_output_past_2_31_elements(hq):
+    """M = 65540, N = 32768, K = 128: the bf16 output holds 2^31 + 131072
+    elements (4.3 GB), so its row offsets must be carried in 64 bits; sampled
+    outputs on both sides of element 2^31 (rows 65535 .. 65539 included)
+    against the oracle."""
+    m, n, k = 65540, 32768, 128
+    rng = np.random.default_rng(2031)
+    xq = _finite_codes(rng, (m, k), fp8.E4M3)
+    wq = _finite_codes(rng, (n, k), fp8.E5M2)
+    xs = rng.uniform(1e-3, 1e-1, m).astype(np.float32)
+    ws = rng.uniform(1e-3, 1e-1, n).astype(np.float32)
+    out = _gemm(hq, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws)
+    edge = np.array([[r, c] for r in (0, 65535, 65536, 65537, m - 1) for c in (0, 255, 256, n - 1)])
+    pairs = np.concatenate([_sample_pairs(rng, m, n, 6000), edge])
+    check_gemm(out, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, pairs=pairs)
+    del out
+
+
 def test_ptpc_square_full_size(hq):
     """4096^3 with per-token X and per-output-channel W, in the launch
     configuration the benchmark times; sampled outputs against the oracle."""

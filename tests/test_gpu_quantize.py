@@ -127,6 +127,57 @@ def test_grouped_moe_full(hq):
     _assert_same(hq, w.reshape(-1, w.shape[-1]), Q.BF16, fp8.E4M3, Q.PER_TOKEN, "moe W")
 
 
+def test_more_than_2_31_elements(hq):
+    """A bf16 [65540, 32768] tensor: 2^31 + 131072 elements (4.3 GB), so every
+    index past element 2^31 must be carried in 64 bits. Checked against the
+    oracle on sampled rows on both sides of element 2^31 (per token: a row's
+    codes, scale and amax depend on that row alone), on sampled columns (per
+    channel, likewise), and per tensor with the maximum planted in the last
+    element (every other value is clamped to |x| <= 8 except one planted in the
+    next-to-last row), so the reduction has to reach it."""
+    rows, cols = 65540, 32768
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20240531)
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 8192):  # slabs: one fp32 draw of the whole tensor would take 8.6 GB
+        r1 = min(rows, r0 + 8192)
+        x[r0:r1] = torch.randn((r1 - r0, cols), generator=gen, device="cuda").clamp_(-8.0, 8.0)
+    x[rows - 1, cols - 1] = 100.0
+    x[rows - 2, 7] = -96.0
+    rng = np.random.default_rng(5)
+    srows = np.unique(np.concatenate([[0, 1, 65535, 65536, 65537, rows - 2, rows - 1], rng.integers(0, rows, 25)]))
+    scols = np.unique(np.concatenate([[0, 7, cols - 1], rng.integers(0, cols, 13)]))
+    ir, ic = torch.from_numpy(srows).cuda(), torch.from_numpy(scols).cuda()
+    xr = host(x.index_select(0, ir).contiguous())
+    xc = host(x.index_select(1, ic).contiguous())
+    planted = (np.array([[100.0]], dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    def same_f32(gpu, ref):
+        return np.array_equal(np.asarray(gpu, np.float32).view(np.uint32), np.asarray(ref, np.float32).view(np.uint32))
+
+    for fmt in FMTS:
+        q, s, a = hq.hq_quantize_fp8(x, fmt, Q.PER_TOKEN)
+        q_ref, s_ref, a_ref = Q.quantize_dynamic(xr, Q.BF16, fmt, Q.PER_TOKEN)
+        assert np.array_equal(host(q.index_select(0, ir)), q_ref), f"per-token codes, fmt {fmt}"
+        assert same_f32(host(s)[srows], s_ref) and same_f32(host(a)[srows], a_ref), f"per-token scales, fmt {fmt}"
+        del q, s, a
+
+        q, s, a = hq.hq_quantize_fp8(x, fmt, Q.PER_CHANNEL)
+        q_ref, s_ref, a_ref = Q.quantize_dynamic(xc, Q.BF16, fmt, Q.PER_CHANNEL)
+        assert np.array_equal(host(q.index_select(1, ic).contiguous()), q_ref), f"per-channel codes, fmt {fmt}"
+        assert same_f32(host(s)[scols], s_ref) and same_f32(host(a)[scols], a_ref), f"per-channel scales, fmt {fmt}"
+        del q, s, a
+
+        q, s, a = hq.hq_quantize_fp8(x, fmt, Q.PER_TENSOR)
+        _, s_ref, a_ref = Q.quantize_dynamic(planted, Q.BF16, fmt, Q.PER_TENSOR)
+        assert same_f32(host(a), a_ref) and same_f32(host(s), s_ref), f"per-tensor amax / scale, fmt {fmt}"
+        q_ref, _, _ = Q.quantize_with_scale(xr, Q.BF16, fmt, s_ref)
+        assert np.array_equal(host(q.index_select(0, ir)), q_ref), f"per-tensor codes, fmt {fmt}"
+        del q, s, a
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_repeated_calls_with_shared_workspace(hq):
     """Per-tensor and per-channel reuse one workspace (zero-filled once) across
     calls of different sizes, single-pass and two-pass per-tensor grids
