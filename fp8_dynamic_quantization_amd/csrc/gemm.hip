@@ -177,10 +177,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // step. A load reads zero for every dword at or past the extent (the per-lane
   // and uniform offsets both count), which covers all tails without clamping:
   // A rows past row_end and B fragments past the padded N read zero, and their
-  // outputs are masked on store. K < 2^24 keeps every offset below 2^32.
+  // outputs are masked on store. The hardware takes extents and offsets as
+  // unsigned 32-bit values; K < 2^24 keeps them below 2^32 for tiles of up to
+  // 256 rows, so they are formed in uint32_t (a 256-row extent at K >= 2^23
+  // passes 2^31) and handed over as the same bits.
+  const uint32_t uK = (uint32_t)K;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.xq + (size_t)m0 * K), (short)0, (row_end - m0) * K, kRsrcFlags);
-  const int a_vo = a_r * K + a_c * 16;
+      (void*)(a.xq + (size_t)m0 * K), (short)0, (int)((uint32_t)(row_end - m0) * uK), kRsrcFlags);
+  const int a_vo = (int)((uint32_t)a_r * uK + (uint32_t)(a_c * 16));
   const int nbw = __builtin_amdgcn_readfirstlane((n0 + wave * TN) / 16);
   const int nbw_c = min(nbw, nfrag);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -263,7 +267,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   constexpr int kFaDepth = WM == 1 ? 3 : 2;
 
 #define HQ_LOAD_A_PIECE(KB, V) \
-  ra[V] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_vo, (V) * C::kRowStep * K + (KB) * kBK, 0))
+  ra[V] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_vo, (int)((uint32_t)((V) * C::kRowStep) * uK + (uint32_t)((KB) * kBK)), 0))
 #define HQ_STORE_A_PIECE(BUF, V)                                          \
   *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
       (!KTAIL || ra_valid) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
