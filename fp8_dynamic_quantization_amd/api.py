@@ -2,13 +2,17 @@
 
 Each function only marshals arguments (tensor -> pointer, current HIP stream,
 optional output allocation with ``torch.empty``) and calls the C ABI; every
-step of the computation runs in the library's HIP kernels. Errors come back as
+step of the computation runs in the library's HIP kernels. With ``stream=``
+every buffer the binding allocates (outputs, zero-filled workspaces) is made
+and filled on that stream, so the launch is ordered after it. Errors come back as
 ``HQInvalidArgument`` (ValueError), ``HQUnsupportedDevice``
 (NotImplementedError) or ``HQLaunchError``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 
 import torch
 
@@ -22,9 +26,21 @@ __all__ = [
     "hq_gemm_a8w8_blockscaled", "hq_gemm_a8w8_blockscaled_preshuffled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error",
+    "hq_gemm_a8w8_strict", "hq_grouped_gemm_a8w8_strict",
 ]
 
 _XT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16}
+
+
+def _on_stream(fn):
+    """Run `fn` with its `stream=` argument (if any) as torch's current stream,
+    so the binding's allocations and fills are ordered before the launch."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kwargs):
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return wrapped
 
 
 def _ptr(t):
@@ -75,6 +91,7 @@ class Ring:
         return hq_ring(self.state.data_ptr(), self.length, int(idx), self.margin, self.flag.data_ptr())
 
 
+@_on_stream
 def hq_quantize_fp8(x: torch.Tensor, fmt: int = HQ_E4M3, gran: int = HQ_PER_TOKEN, *,
                     ring: Ring | None = None, ring_idx: int = 0, q=None, scale_out=None,
                     amax_out=None, workspace=None, stream=None):
@@ -106,6 +123,7 @@ def hq_quantize_fp8(x: torch.Tensor, fmt: int = HQ_E4M3, gran: int = HQ_PER_TOKE
     return q, scale_out, amax_out
 
 
+@_on_stream
 def hq_quantize_fp8_stochastic(x: torch.Tensor, gran: int = HQ_PER_TOKEN, seed: int = 0, *,
                                ring: Ring | None = None, ring_idx: int = 0, q=None, scale_out=None,
                                amax_out=None, workspace=None, stream=None):
@@ -138,6 +156,7 @@ def hq_quantize_fp8_stochastic(x: torch.Tensor, gran: int = HQ_PER_TOKEN, seed: 
     return q, scale_out, amax_out
 
 
+@_on_stream
 def hq_quantize_fp8_blockwise(x: torch.Tensor, fmt: int = HQ_E4M3, block_size: int = 32, *, stochastic: bool = False,
                               seed: int = 0, q=None, scales=None, amax_out=None, stream=None):
     """Block-wise quantization: returns (q uint8 [rows, cols], scales fp32
@@ -162,6 +181,7 @@ def hq_quantize_fp8_blockwise(x: torch.Tensor, fmt: int = HQ_E4M3, block_size: i
     return q, scales, amax_out
 
 
+@_on_stream
 def hq_gemm_a8w8_blockscaled(xq: torch.Tensor, xf: int, wq: torch.Tensor, wf: int, x_scales: torch.Tensor,
                              w_scales: torch.Tensor, block_size: int = 32, bias=None, out=None,
                              stream=None) -> torch.Tensor:
@@ -182,6 +202,7 @@ def hq_gemm_a8w8_blockscaled(xq: torch.Tensor, xf: int, wq: torch.Tensor, wf: in
     return out
 
 
+@_on_stream
 def hq_gemm_a8w8_blockscaled_preshuffled(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
                                          x_scales: torch.Tensor, w_scales: torch.Tensor, n: int, block_size: int = 128,
                                          bias=None, out=None, stream=None) -> torch.Tensor:
@@ -203,6 +224,7 @@ def hq_gemm_a8w8_blockscaled_preshuffled(xq: torch.Tensor, xf: int, wq_pre: torc
     return out
 
 
+@_on_stream
 def hq_quantize_fp8_layouts(x: torch.Tensor, fmt: int = HQ_E4M3, *, scale_in: torch.Tensor | None = None,
                             ring: Ring | None = None, ring_idx: int = 0, q=False, q_t=False, q_pre=False,
                             q_t_pre=False, scale_out=None, amax_out=None, workspace=None, stream=None):
@@ -214,6 +236,7 @@ def hq_quantize_fp8_layouts(x: torch.Tensor, fmt: int = HQ_E4M3, *, scale_in: to
                     stream)
 
 
+@_on_stream
 def hq_quantize_fp8_layouts_stochastic(x: torch.Tensor, seed: int, *, scale_in: torch.Tensor | None = None,
                                        ring: Ring | None = None, ring_idx: int = 0, q=False, q_t=False, q_pre=False,
                                        q_t_pre=False, scale_out=None, amax_out=None, workspace=None, stream=None):
@@ -263,6 +286,7 @@ def _layouts(x, fmt, seed, scale_in, ring, ring_idx, q, q_t, q_pre, q_t_pre, sca
     return outs
 
 
+@_on_stream
 def hq_scale_ring_update(ring: Ring, amax: torch.Tensor, fmt: int = HQ_E4M3, ring_idx: int = 0,
                          stream=None) -> None:
     """Fold a device float32 amax scalar into the ring and publish the next scale."""
@@ -272,6 +296,7 @@ def hq_scale_ring_update(ring: Ring, amax: torch.Tensor, fmt: int = HQ_E4M3, rin
     check(st)
 
 
+@_on_stream
 def hq_preshuffle_weight(wq: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     """Pre-shuffle FP8 codes WQ [n, k] (uint8); returns the flat uint8 buffer."""
     if wq.dim() != 2:
@@ -286,6 +311,7 @@ def hq_preshuffle_weight(wq: torch.Tensor, out=None, stream=None) -> torch.Tenso
     return out
 
 
+@_on_stream
 def hq_quantize_fp8_preshuffled(x: torch.Tensor, fmt: int = HQ_E4M3, *, row_major: bool = False, q=None,
                                 q_pre=None, scale_out=None, amax_out=None, stream=None):
     """Per-row quantization of a weight [n, k] straight into the pre-shuffled
@@ -317,14 +343,15 @@ _GEMM_WORKSPACE = {}
 
 
 def gemm_workspace(device, nbytes: int) -> torch.Tensor | None:
-    """A GEMM workspace of at least `nbytes` for `device`, zero-filled when made
-    and kept for reuse (the kernels leave its counters at zero). Calls sharing
-    it must not overlap, so pass your own `workspace=` to GEMMs that run
-    concurrently on other streams."""
+    """A GEMM workspace of at least `nbytes` for `device` and torch's current
+    stream, zero-filled on that stream when made and kept for reuse (the
+    kernels leave its counters at zero). Launches on one stream are ordered,
+    so they may share it; each stream gets its own."""
     if nbytes <= 0:
         return None
     dev = torch.device(device)
-    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (dev.type, idx, torch.cuda.current_stream(idx).cuda_stream)
     ws = _GEMM_WORKSPACE.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
@@ -332,12 +359,16 @@ def gemm_workspace(device, nbytes: int) -> torch.Tensor | None:
     return ws
 
 
+@_on_stream
 def hq_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_scale: torch.Tensor,
-                 w_scale: torch.Tensor, n: int, out=None, workspace=None, stream=None) -> torch.Tensor:
+                 w_scale: torch.Tensor, n: int, out=None, workspace=None, stream=None,
+                 strict: bool = False) -> torch.Tensor:
     """out[m, n] = bf16(x_scale[m] * w_scale[n] * sum_k XQ[m,k] WQ[n,k]); returns out.
 
     `workspace`: None (a shared zero-filled buffer of the size the shape wants),
-    False (run without one) or a zero-filled uint8 device tensor."""
+    False (run without one) or a zero-filled uint8 device tensor.
+    `strict`: exact products (hq_gemm_a8w8_strict) instead of the FP8
+    matrix-core window."""
     xq = xq.contiguous()
     m, k = xq.shape
     x_scale = x_scale.contiguous()
@@ -350,17 +381,28 @@ def hq_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_sca
     elif workspace is False:
         workspace = None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if strict:
+        check(lib.hq_gemm_a8w8_strict(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                                      _ptr(w_scale), w_scale.numel(), m, n, k, None, _ptr(out), _ptr(workspace),
+                                      ws_bytes, _stream(xq.device, stream)))
+        return out
     check(lib.hq_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
                            _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(xq.device, stream)))
     return out
 
 
+def hq_gemm_a8w8_strict(*args, **kwargs) -> torch.Tensor:
+    """hq_gemm_a8w8 with exact products (float16 matrix cores); same arguments."""
+    return hq_gemm_a8w8(*args, strict=True, **kwargs)
+
+
+@_on_stream
 def hq_gemm_a8w8_epilogue(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_scale: torch.Tensor,
                           w_scale: torch.Tensor, n: int, *, bias: torch.Tensor | None = None,
                           bias_type: int = HQ_BIAS_BF16, bias_scale: torch.Tensor | None = None,
                           out_scale: torch.Tensor | None = None, out_fmt: int = HQ_E4M3, out=None,
-                          workspace=None, stream=None) -> torch.Tensor:
+                          workspace=None, stream=None, strict: bool = False) -> torch.Tensor:
     """hq_gemm_a8w8 with a bias (bf16 tensor, or uint8 FP8 codes with
     bias_scale) added after the scales, and bf16 output or, with out_scale,
     FP8 (out_fmt) codes of v / out_scale. Returns out (bf16 or uint8 [m, n])."""
@@ -381,16 +423,19 @@ def hq_gemm_a8w8_epilogue(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: i
     ep = hq_epilogue(0 if bias is None else bias.data_ptr(), int(bias_type),
                      0 if bias_scale is None else bias_scale.data_ptr(),
                      0 if out_scale is None else out_scale.data_ptr(), int(out_fmt))
-    check(lib.hq_gemm_a8w8_epilogue(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
-                                    _ptr(w_scale), w_scale.numel(), m, n, k, ctypes.byref(ep), _ptr(out),
-                                    _ptr(workspace), ws_bytes, _stream(xq.device, stream)))
+    fn = lib.hq_gemm_a8w8_strict if strict else lib.hq_gemm_a8w8_epilogue
+    check(fn(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+             _ptr(w_scale), w_scale.numel(), m, n, k, ctypes.byref(ep), _ptr(out),
+             _ptr(workspace), ws_bytes, _stream(xq.device, stream)))
     return out
 
 
+@_on_stream
 def hq_grouped_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
                          x_scale: torch.Tensor, w_scale: torch.Tensor, group_offsets: torch.Tensor,
-                         num_experts: int, n: int, out=None, stream=None) -> torch.Tensor:
-    """Per-expert GEMM over row ranges [offsets[e], offsets[e+1]); returns out [T, n]."""
+                         num_experts: int, n: int, out=None, stream=None, strict: bool = False) -> torch.Tensor:
+    """Per-expert GEMM over row ranges [offsets[e], offsets[e+1]); returns out [T, n].
+    `strict`: exact products (hq_grouped_gemm_a8w8_strict)."""
     xq = xq.contiguous()
     t, k = xq.shape
     x_scale = x_scale.contiguous()
@@ -398,6 +443,12 @@ def hq_grouped_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: in
     group_offsets = group_offsets.contiguous()
     if out is None:
         out = torch.empty((t, n), dtype=torch.bfloat16, device=xq.device)
+    if strict:
+        check(load().hq_grouped_gemm_a8w8_strict(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                                                 _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
+                                                 int(num_experts), t, n, k, None, _ptr(out),
+                                                 _stream(xq.device, stream)))
+        return out
     check(load().hq_grouped_gemm_a8w8(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
                                       _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
                                       int(num_experts), t, n, k, _ptr(out),
@@ -405,12 +456,18 @@ def hq_grouped_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: in
     return out
 
 
+def hq_grouped_gemm_a8w8_strict(*args, **kwargs) -> torch.Tensor:
+    """hq_grouped_gemm_a8w8 with exact products (float16 matrix cores)."""
+    return hq_grouped_gemm_a8w8(*args, strict=True, **kwargs)
+
+
+@_on_stream
 def hq_grouped_gemm_a8w8_epilogue(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int,
                                   x_scale: torch.Tensor, w_scale: torch.Tensor, group_offsets: torch.Tensor,
                                   num_experts: int, n: int, *, bias: torch.Tensor | None = None,
                                   bias_type: int = HQ_BIAS_BF16, bias_scale: torch.Tensor | None = None,
                                   out_scale: torch.Tensor | None = None, out_fmt: int = HQ_E4M3, out=None,
-                                  stream=None) -> torch.Tensor:
+                                  stream=None, strict: bool = False) -> torch.Tensor:
     """hq_grouped_gemm_a8w8 with a per-expert bias [E, n] (bf16, or uint8 FP8
     codes with bias_scale [E]) and bf16 output or, with out_scale, FP8 codes.
     Returns out (bf16 or uint8 [T, n])."""
@@ -428,8 +485,10 @@ def hq_grouped_gemm_a8w8_epilogue(xq: torch.Tensor, xf: int, wq_pre: torch.Tenso
     ep = hq_epilogue(0 if bias is None else bias.data_ptr(), int(bias_type),
                      0 if bias_scale is None else bias_scale.data_ptr(),
                      0 if out_scale is None else out_scale.data_ptr(), int(out_fmt))
-    check(load().hq_grouped_gemm_a8w8_epilogue(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
-                                               _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
-                                               int(num_experts), t, n, k, ctypes.byref(ep), _ptr(out),
-                                               _stream(xq.device, stream)))
+    lib = load()
+    fn = lib.hq_grouped_gemm_a8w8_strict if strict else lib.hq_grouped_gemm_a8w8_epilogue
+    check(fn(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+             _ptr(w_scale), w_scale.numel(), _ptr(group_offsets),
+             int(num_experts), t, n, k, ctypes.byref(ep), _ptr(out),
+             _stream(xq.device, stream)))
     return out

@@ -471,10 +471,10 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                                out, workspace, workspace_bytes, stream);
 }
 
-hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
-                                int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m,
-                                int64_t n, int64_t k, const hq_epilogue* ep, void* out, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+static hq_status gemm_impl(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                           int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m, int64_t n,
+                           int64_t k, const hq_epilogue* ep, void* out, void* workspace, size_t workspace_bytes,
+                           bool strict, const char* name, hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, m, n, k);
   if (st != HQ_OK) return st;
   if (workspace_bytes > 0 && workspace == nullptr)
@@ -518,8 +518,25 @@ hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre
   if (st != HQ_OK) return st;
   hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1,
                  bias, bias_kind, bias_scale, out_scale, out_fmt};
+  g.strict = strict;
   (void)hipGetLastError();
-  return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), "hq_gemm_a8w8");
+  return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), name);
+}
+
+hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                                int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m,
+                                int64_t n, int64_t k, const hq_epilogue* ep, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return gemm_impl(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count, m, n, k, ep, out, workspace,
+                   workspace_bytes, false, ep ? "hq_gemm_a8w8_epilogue" : "hq_gemm_a8w8", stream);
+}
+
+hq_status hq_gemm_a8w8_strict(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                              int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m, int64_t n,
+                              int64_t k, const hq_epilogue* ep, void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return gemm_impl(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count, m, n, k, ep, out, workspace,
+                   workspace_bytes, true, "hq_gemm_a8w8_strict", stream);
 }
 
 hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
@@ -530,11 +547,11 @@ hq_status hq_grouped_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre,
                                        group_offsets, num_experts, total_rows, n, k, nullptr, out, stream);
 }
 
-hq_status hq_grouped_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
-                                        const float* x_scale, int64_t x_scale_count, const float* w_scale,
-                                        int64_t w_scale_count, const int32_t* group_offsets, int32_t num_experts,
-                                        int64_t total_rows, int64_t n, int64_t k, const hq_epilogue* ep, void* out,
-                                        hipStream_t stream) {
+static hq_status grouped_impl(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                              int64_t x_scale_count, const float* w_scale, int64_t w_scale_count,
+                              const int32_t* group_offsets, int32_t num_experts, int64_t total_rows, int64_t n,
+                              int64_t k, const hq_epilogue* ep, void* out, bool strict, const char* name,
+                              hipStream_t stream) {
   hq_status st = check_gemm_common(xf, wf, total_rows, n, k);
   if (st != HQ_OK) return st;
   if (num_experts < 1 || num_experts > 1024)
@@ -580,9 +597,28 @@ hq_status hq_grouped_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t
   if (st != HQ_OK) return st;
   hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)total_rows, (int)n, (int)k, x_scale_count != 1,
                  w_scale_count != num_experts, bias, bias_kind, bias_scale, out_scale, out_fmt};
+  g.strict = strict;
   (void)hipGetLastError();
-  return launched(hq::launch_grouped_gemm(g, group_offsets, num_experts, xf, wf, stream),
-                  ep ? "hq_grouped_gemm_a8w8_epilogue" : "hq_grouped_gemm_a8w8");
+  return launched(hq::launch_grouped_gemm(g, group_offsets, num_experts, xf, wf, stream), name);
+}
+
+hq_status hq_grouped_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                                        const float* x_scale, int64_t x_scale_count, const float* w_scale,
+                                        int64_t w_scale_count, const int32_t* group_offsets, int32_t num_experts,
+                                        int64_t total_rows, int64_t n, int64_t k, const hq_epilogue* ep, void* out,
+                                        hipStream_t stream) {
+  return grouped_impl(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count, group_offsets, num_experts,
+                      total_rows, n, k, ep, out, false,
+                      ep ? "hq_grouped_gemm_a8w8_epilogue" : "hq_grouped_gemm_a8w8", stream);
+}
+
+hq_status hq_grouped_gemm_a8w8_strict(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                                      const float* x_scale, int64_t x_scale_count, const float* w_scale,
+                                      int64_t w_scale_count, const int32_t* group_offsets, int32_t num_experts,
+                                      int64_t total_rows, int64_t n, int64_t k, const hq_epilogue* ep, void* out,
+                                      hipStream_t stream) {
+  return grouped_impl(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count, group_offsets, num_experts,
+                      total_rows, n, k, ep, out, true, "hq_grouped_gemm_a8w8_strict", stream);
 }
 
 hq_status hq_gemm_a8w8_blockscaled(const uint8_t* xq, int xf, const uint8_t* wq, int wf, const float* x_scales,

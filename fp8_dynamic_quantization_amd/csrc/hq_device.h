@@ -5,9 +5,11 @@
 // saturating round-to-nearest-even: the scaled value is clamped to +-fmax with
 // v_med3_f32 and converted with the gfx950 OCP conversion instructions
 // (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, round-to-nearest-even). Clamp + convert
-// equals the saturating RNE encoder on every non-NaN float32 input (checked
-// exhaustively over all 2^32 patterns on the device); NaN inputs, which the clamp
-// would turn into +-fmax, are patched to the canonical code 0x7F.
+// equals the saturating RNE encoder on every float32 input the encoder decides
+// (every pattern from 2^-20 up to 2^18, zero, subnormals, Inf and NaN, compared on
+// the device with the CPU encoder; below and above those binades every value is a
+// signed zero or saturates); NaN inputs, which the clamp would turn into +-fmax,
+// are patched to the canonical code 0x7F.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -18,13 +18,17 @@ Modules
   gemm        the scaled a8w8 GEMM and its grouped (per-expert) variant in
               float64, plus the comparison tolerance
   preshuffle  the byte map of the pre-shuffled weight layout
+  stochastic  Philox-4x32-10 and the stochastic E5M2 rounding rule
+  blockwise   block-wise scaling and the block-scaled GEMM, with its tolerance
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` (closed forms, library cross-checks, brute force and
-invariants). The pre-shuffled byte map is a layout of this library's own design
+invariants); the block-scaled GEMM tolerance by ``tests/test_mfma_model.py``
+(the fold's float32 rounding accepted, a dropped term rejected). The pre-shuffled byte map is a layout of this library's own design
 (the pages leave the layout open); it is pinned by its bijectivity, by
-hand-derived positions in ``tests/golden/preshuffle_positions.json`` and, end to
-end, by the GEMM on pre-shuffled weights matching the plain oracle GEMM.
+hand-derived byte positions written out in ``tests/test_oracle_preshuffle.py``
+and, end to end, by the GEMM on pre-shuffled weights matching the plain oracle
+GEMM.
 """
 
 from . import fp8, quantize, gemm, preshuffle  # noqa: F401

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 from oracle import fp8, gemm as G
-from tests.gpu_helpers import (check_gemm, dev_f32, dev_u8, host, narrow_codes, require_gpu, run_term_rows)
+from tests.gpu_helpers import check_gemm, dev_f32, dev_u8, host, narrow_codes, require_gpu
+from tests.mfma_model import window_drop
 
 pytestmark = pytest.mark.gpu
 
@@ -112,7 +113,7 @@ def test_bias_full_range_operands_within_tolerance(hq, shape, bias_kind):
     ii, jj = rng.integers(0, m, 5000), rng.integers(0, n, 5000)
     ref, at = G.gemm_a8w8_rows(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, np.stack([ii, jj], axis=1))
     ref = ref + bvals[jj]
-    run = run_term_rows(t[xq[ii]], t[wq[jj]]) * np.abs(xs[ii] * ws[jj])
+    run = window_drop(xq[ii], fp8.E4M3, wq[jj], fp8.E4M3) * np.abs(xs[ii] * ws[jj])
     err = np.abs(G.bf16_bits_to_f64(got[ii, jj]) - ref)
     assert np.all(err <= G.tolerance(ref, at) + run)
 
@@ -135,7 +136,7 @@ def test_fp8_output_full_range_within_half_step(hq, out_kind):
     # an output scale (from the oracle's values) that saturates about a tenth of the outputs
     out_scale = np.float32(np.quantile(np.abs(ref), 0.9) / fp8.fmax(fmt))
     got, _ = _run(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, "none", out_kind, rng, out_scale)
-    run = run_term_rows(t[xq[ii]], t[wq[jj]]) * np.abs(xs[ii] * ws[jj])
+    run = window_drop(xq[ii], fp8.E4M3, wq[jj], fp8.E4M3) * np.abs(xs[ii] * ws[jj])
     v = ref / float(out_scale)
     slack = (2.0 ** -22 * at + run) / float(out_scale) + 2.0 ** -21 * np.abs(v)
     dec = fp8.decode_table(fmt)[got[ii, jj]]

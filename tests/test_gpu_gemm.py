@@ -1,5 +1,10 @@
-"""GPU parity of hq_preshuffle_weight, hq_gemm_a8w8 and hq_grouped_gemm_a8w8 with
-the oracle (pre-shuffle bit-exact; GEMM within the tolerance of gpu_helpers)."""
+"""GPU parity of hq_preshuffle_weight, hq_gemm_a8w8 and hq_grouped_gemm_a8w8 (and
+their strict forms) with the oracle: pre-shuffle bit-exact; strict GEMMs within
+the method's bound on every element; FP8-path GEMMs within that bound plus the
+matrix cores' window drop on every element, with the share of elements outside
+the method's bound alone at most the share measured for the test
+(gpu_helpers.MEASURED_SHARE).
+"""
 import zlib
 
 import numpy as np
@@ -8,7 +13,7 @@ import torch
 
 import workloads
 from oracle import fp8, gemm as G, preshuffle as P, quantize as Q
-from tests.gpu_helpers import (check_gemm, dev_bf16, dev_f32, dev_u8, host, narrow_codes,
+from tests.gpu_helpers import (allowed_share, check_gemm, dev_bf16, dev_f32, dev_u8, host, narrow_codes,
                                require_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -27,10 +32,11 @@ def _finite_codes(rng, shape, fmt):
     return rng.choice(finite, size=shape)
 
 
-def _gemm(hq, xq, xf, wq, wf, xs, ws):
+def _gemm(hq, xq, xf, wq, wf, xs, ws, strict=False):
     n = wq.shape[0]
     pre = hq.hq_preshuffle_weight(dev_u8(wq))
-    out = hq.hq_gemm_a8w8(dev_u8(xq), xf, pre, wf, dev_f32(np.atleast_1d(xs)), dev_f32(np.atleast_1d(ws)), n)
+    out = hq.hq_gemm_a8w8(dev_u8(xq), xf, pre, wf, dev_f32(np.atleast_1d(xs)), dev_f32(np.atleast_1d(ws)), n,
+                          strict=strict)
     torch.cuda.synchronize()
     return host(out)
 
@@ -73,6 +79,8 @@ def test_gemm_narrow_operands_strict(hq, shape, pair, scales):
         xs, ws = np.float32(0.37), np.float32(1.9)
     out = _gemm(hq, xq, xf, wq, wf, xs, ws)
     check_gemm(out, xq, xf, wq, wf, xs, ws, strict_only=True)
+    strict = _gemm(hq, xq, xf, wq, wf, xs, ws, strict=True)
+    assert np.array_equal(strict, out)  # exact partial sums: the same bits either way
 
 
 def _edge_pairs(rng, m, n, count):
@@ -102,13 +110,17 @@ def test_gemm_tile_configs_narrow_strict(hq, shape, pair):
     xs = rng.uniform(1e-3, 2.0, m).astype(np.float32)
     ws = rng.uniform(1e-3, 2.0, n).astype(np.float32)
     out = _gemm(hq, xq, xf, wq, wf, xs, ws)
-    check_gemm(out, xq, xf, wq, wf, xs, ws, pairs=_edge_pairs(rng, m, n, 3000), strict_only=True)
+    pairs = _edge_pairs(rng, m, n, 3000)
+    check_gemm(out, xq, xf, wq, wf, xs, ws, pairs=pairs, strict_only=True)
+    strict = _gemm(hq, xq, xf, wq, wf, xs, ws, strict=True)
+    check_gemm(strict, xq, xf, wq, wf, xs, ws, pairs=pairs, strict_only=True)
 
 
 @pytest.mark.parametrize("shape", [(16, 64, 128), (130, 200, 400), (64, 96, 1024)])
 @pytest.mark.parametrize("pair", PAIRS)
 def test_gemm_full_range_codes(hq, shape, pair):
-    """Every finite code, both formats: within strict + MFMA-run bound."""
+    """Every finite code, both formats: the FP8 path within the bound plus the
+    window drop, the strict path within the bound, on every element."""
     m, n, k = shape
     xf, wf = pair
     rng = np.random.default_rng(hash((shape, pair, 7)) % 2**32)
@@ -117,7 +129,10 @@ def test_gemm_full_range_codes(hq, shape, pair):
     xs = rng.uniform(1e-4, 1e-2, m).astype(np.float32)
     ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
     out = _gemm(hq, xq, xf, wq, wf, xs, ws)
-    check_gemm(out, xq, xf, wq, wf, xs, ws, max_strict_frac=0.05)
+    key = f"full_range {shape} {pair}"
+    check_gemm(out, xq, xf, wq, wf, xs, ws, max_strict_frac=allowed_share(key, m * n), label=key)
+    strict = _gemm(hq, xq, xf, wq, wf, xs, ws, strict=True)
+    check_gemm(strict, xq, xf, wq, wf, xs, ws, strict_only=True, label=key + " strict")
 
 
 def test_one_hot_reproduces_scales(hq):
@@ -147,9 +162,11 @@ def test_tiny_per_tensor_workload(hq):
     gw, gws, _ = hq.hq_quantize_fp8(dev_f32(w), fp8.E4M3, Q.PER_TENSOR)
     pre = hq.hq_preshuffle_weight(gw)
     out = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, 64))
+    strict = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, 64, strict=True))
     assert np.array_equal(host(gx), xq) and np.array_equal(host(gw), wq)
-    st = check_gemm(out, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
-    print("tiny per-tensor:", st)
+    check_gemm(out, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, max_strict_frac=allowed_share("tiny", 16 * 64),
+               label="tiny")
+    check_gemm(strict, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, strict_only=True, label="tiny strict")
 
 
 def _sample_pairs(rng, m, n, count):
@@ -172,24 +189,28 @@ def test_output_past_2_31_elements(hq):
     out = _gemm(hq, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws)
     edge = np.array([[r, c] for r in (0, 65535, 65536, 65537, m - 1) for c in (0, 255, 256, n - 1)])
     pairs = np.concatenate([_sample_pairs(rng, m, n, 6000), edge])
-    check_gemm(out, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, pairs=pairs)
+    check_gemm(out, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, pairs=pairs,
+               max_strict_frac=allowed_share("past_2_31", len(pairs)), label="past_2_31")
     del out
 
 
 def test_ptpc_square_full_size(hq):
     """4096^3 with per-token X and per-output-channel W, in the launch
-    configuration the benchmark times; sampled outputs against the oracle."""
+    configuration the benchmark times (the weight quantized straight into the
+    pre-shuffled layout); every output element against the oracle, for the
+    FP8 path and the strict path."""
     x, w = workloads.ptpc_square(1)
     gx, gxs, _ = hq.hq_quantize_fp8(dev_bf16(x), fp8.E4M3, Q.PER_TOKEN)
-    gw, gws, _ = hq.hq_quantize_fp8(dev_bf16(w), fp8.E4M3, Q.PER_TOKEN)
-    pre = hq.hq_preshuffle_weight(gw)
+    pre, gws, _, _ = hq.hq_quantize_fp8_preshuffled(dev_bf16(w), fp8.E4M3)
     out = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, 4096))
+    strict = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, 4096, strict=True))
     xq, xs, _ = Q.quantize_dynamic(x, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
     wq, ws, _ = Q.quantize_dynamic(w, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
-    assert np.array_equal(host(gx), xq) and np.array_equal(host(gw), wq)
-    rng = np.random.default_rng(0)
-    st = check_gemm(out, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, pairs=_sample_pairs(rng, 4096, 4096, 20000))
-    print("ptpc 4096^3:", st)
+    assert np.array_equal(host(gx), xq)
+    assert np.array_equal(host(gws).view(np.uint32), ws.view(np.uint32))
+    check_gemm(out, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, max_strict_frac=allowed_share("ptpc", 4096 * 4096),
+               label="ptpc 4096^3")
+    check_gemm(strict, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, strict_only=True, label="ptpc 4096^3 strict")
 
 
 @pytest.mark.parametrize("m", [1, 8, 32])
@@ -210,8 +231,14 @@ def test_decode_skinny_into_view(hq, m):
     assert np.all(allb[:off] == sentinel) and np.all(allb[off + m * n:] == sentinel)
     xq, xs, _ = Q.quantize_dynamic(x, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
     wq, ws, _ = Q.quantize_dynamic(w, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
-    st = check_gemm(allb[off:off + m * n].reshape(m, n), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
-    print(f"decode m={m}:", st)
+    check_gemm(allb[off:off + m * n].reshape(m, n), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws,
+               max_strict_frac=allowed_share(f"decode {m}", m * n), label=f"decode m={m}")
+    flat.view(torch.int16).fill_(sentinel)
+    hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, n, out=view, strict=True)
+    allb = host(flat)
+    assert np.all(allb[:off] == sentinel) and np.all(allb[off + m * n:] == sentinel)
+    check_gemm(allb[off:off + m * n].reshape(m, n), xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, strict_only=True,
+               label=f"decode m={m} strict")
 
 
 # shapes whose unsplit launch needs more than one chunk of loads per wavefront
@@ -246,7 +273,14 @@ def test_skinny_split_matches_unsplit_and_oracle(hq, shape):
     frags = -(-n // 32) * 2
     groups = frags if m <= 16 else -(-frags // 2)
     assert int(work[:4 * groups].count_nonzero()) == 0
-    check_gemm(plain, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, max_strict_frac=0.05)
+    key = f"split {shape}"
+    check_gemm(plain, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, max_strict_frac=allowed_share(key, m * n), label=key)
+    # the strict form splits the same way (M <= 32) or takes the tiles
+    for _ in range(2):
+        strict = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, n, workspace=work, strict=True))
+        check_gemm(strict, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, strict_only=True, label=key + " strict")
+    torch.cuda.synchronize()
+    assert int(work[:4 * groups].count_nonzero()) == 0
 
 
 def test_empty_output_is_noop(hq):
@@ -277,17 +311,17 @@ def test_invalid_gemm_leaves_out_untouched(hq):
 
 # ---- grouped -------------------------------------------------------------------
 
-def _grouped(hq, xq, xf, wq_e, wf, xs, ws, offsets, out=None):
+def _grouped(hq, xq, xf, wq_e, wf, xs, ws, offsets, out=None, strict=False):
     e, n, k = wq_e.shape
     pre = torch.cat([hq.hq_preshuffle_weight(dev_u8(wq_e[i])) for i in range(e)])
     off = torch.from_numpy(np.asarray(offsets, dtype=np.int32)).cuda()
     o = hq.hq_grouped_gemm_a8w8(dev_u8(xq), xf, pre, wf, dev_f32(np.atleast_1d(xs)), dev_f32(ws.reshape(-1)),
-                                off, e, n, out=out)
+                                off, e, n, out=out, strict=strict)
     torch.cuda.synchronize()
     return o
 
 
-def _check_grouped(out_bits, xq, xf, wq_e, wf, xs, ws, offsets, strict=False, pairs_per_expert=None):
+def _check_grouped(out_bits, xq, xf, wq_e, wf, xs, ws, offsets, strict=False, key=None):
     t = xq.shape[0]
     e = wq_e.shape[0]
     xsv = np.full(t, np.float32(xs)) if np.ndim(xs) == 0 or np.size(xs) == 1 else np.asarray(xs, np.float32)
@@ -296,11 +330,9 @@ def _check_grouped(out_bits, xq, xf, wq_e, wf, xs, ws, offsets, strict=False, pa
         if hi <= lo:
             continue
         wse = ws[i] if ws.ndim == 2 else np.full(wq_e.shape[1], ws[i], np.float32)
-        pairs = None
-        if pairs_per_expert:
-            rng = np.random.default_rng(i)
-            pairs = _sample_pairs(rng, hi - lo, wq_e.shape[1], pairs_per_expert)
-        check_gemm(out_bits[lo:hi], xq[lo:hi], xf, wq_e[i], wf, xsv[lo:hi], wse, pairs=pairs, strict_only=strict)
+        share = None if strict else allowed_share(f"{key} expert {i}", (hi - lo) * wq_e.shape[1])
+        check_gemm(out_bits[lo:hi], xq[lo:hi], xf, wq_e[i], wf, xsv[lo:hi], wse, strict_only=strict,
+                   max_strict_frac=share, label=None if key is None else f"{key} expert {i}")
 
 
 @pytest.mark.parametrize("pair", PAIRS[:2])
@@ -316,6 +348,7 @@ def test_grouped_narrow_strict_with_empty_experts(hq, pair):
     ws = rng.uniform(0.01, 1, (len(counts), n)).astype(np.float32)
     out = host(_grouped(hq, xq, xf, wq, wf, xs, ws, offsets))
     _check_grouped(out, xq, xf, wq, wf, xs, ws, offsets, strict=True)
+    assert np.array_equal(host(_grouped(hq, xq, xf, wq, wf, xs, ws, offsets, strict=True)), out)
 
 
 def test_grouped_per_expert_scalar_scale_and_uncovered_rows(hq):
@@ -356,7 +389,8 @@ def test_grouped_call_sequence_no_contamination(hq):
 
 def test_grouped_moe_full_size(hq):
     """8 experts, 8192 tokens, N=2048, K=1024 with two empty experts; GPU
-    quantization feeds the grouped GEMM; sampled outputs per expert."""
+    quantization feeds the grouped GEMM; every output element per expert, for
+    the FP8 path and the strict path."""
     x, w, offsets = workloads.grouped_moe(3)
     e, n, k = w.shape
     gx, gxs, _ = hq.hq_quantize_fp8(dev_bf16(x), fp8.E4M3, Q.PER_TOKEN)
@@ -371,8 +405,13 @@ def test_grouped_moe_full_size(hq):
     wq, ws, _ = Q.quantize_dynamic(w.reshape(-1, k), Q.BF16, fp8.E4M3, Q.PER_TOKEN)
     assert np.array_equal(host(gx), xq) and np.array_equal(host(gw), wq)
     assert not np.any(ob == sentinel)
-    _check_grouped(ob, xq, fp8.E4M3, wq.reshape(e, n, k), fp8.E4M3, xs, ws.reshape(e, n), offsets,
-                   pairs_per_expert=3000)
+    _check_grouped(ob, xq, fp8.E4M3, wq.reshape(e, n, k), fp8.E4M3, xs, ws.reshape(e, n), offsets, key="moe")
+    out.view(torch.int16).fill_(sentinel)
+    hq.hq_grouped_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, gxs, gws, off, e, n, out=out, strict=True)
+    ob = host(out)
+    assert not np.any(ob == sentinel)
+    _check_grouped(ob, xq, fp8.E4M3, wq.reshape(e, n, k), fp8.E4M3, xs, ws.reshape(e, n), offsets, strict=True,
+                   key="moe strict")
 
 
 def test_training_linear_gemm_shapes(hq):
@@ -395,8 +434,10 @@ def test_training_linear_gemm_shapes(hq):
     cases.append((gq, fp8.E5M2, np.ascontiguousarray(wq5.T), fp8.E5M2, gs, ws5))   # dgrad: G W
     xq5, xs5, _ = qt(xb, fp8.E5M2)
     cases.append((np.ascontiguousarray(gq.T), fp8.E5M2, np.ascontiguousarray(xq5.T), fp8.E5M2, gs, xs5))  # wgrad
-    for xq_, xf_, wq_, wf_, xs_, ws_ in cases:
+    for name, (xq_, xf_, wq_, wf_, xs_, ws_) in zip(("fwd", "dgrad", "wgrad"), cases):
         out = _gemm(hq, xq_, xf_, wq_, wf_, xs_, ws_)
-        st = check_gemm(out, xq_, xf_, wq_, wf_, xs_, ws_,
-                        pairs=_sample_pairs(rng, xq_.shape[0], wq_.shape[0], 6000))
-        print("training gemm", xq_.shape, wq_.shape, st)
+        n_el = xq_.shape[0] * wq_.shape[0]
+        check_gemm(out, xq_, xf_, wq_, wf_, xs_, ws_, max_strict_frac=allowed_share(f"training {name}", n_el),
+                   label=f"training {name}")
+        strict = _gemm(hq, xq_, xf_, wq_, wf_, xs_, ws_, strict=True)
+        check_gemm(strict, xq_, xf_, wq_, wf_, xs_, ws_, strict_only=True, label=f"training {name} strict")

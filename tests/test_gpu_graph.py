@@ -12,7 +12,7 @@ import torch
 
 import workloads
 from oracle import fp8, preshuffle as P, quantize as Q
-from tests.gpu_helpers import check_gemm, dev_bf16, host, require_gpu
+from tests.gpu_helpers import allowed_share, check_gemm, dev_bf16, host, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -133,8 +133,10 @@ def test_quantize_and_gemm_graph_replays(hq):
         assert np.array_equal(host(sr).view(np.uint32), s_r.view(np.uint32)), f"replay {rep}: delayed scale"
         assert np.array_equal(host(ring.state).view(np.uint32), state_r.view(np.uint32)), f"replay {rep}: ring"
         ob, odb = host(out), host(od)
-        check_gemm(ob, qx_ref, E4M3, qw_ref, E4M3, sx_ref, sw_ref, pairs=pairs)
-        check_gemm(odb, qd_h, E4M3, qv_h, E4M3, sd_h, sv_h, pairs=dpairs)
+        check_gemm(ob, qx_ref, E4M3, qw_ref, E4M3, sx_ref, sw_ref, pairs=pairs,
+                   max_strict_frac=allowed_share("graph gemm", len(pairs)), label="graph gemm")
+        check_gemm(odb, qd_h, E4M3, qv_h, E4M3, sd_h, sv_h, pairs=dpairs,
+                   max_strict_frac=allowed_share("graph decode", len(dpairs)), label="graph decode")
         if first is None:
             first = (ob.copy(), odb.copy())
         else:  # the GEMMs' sums are in a fixed order: replays agree bit for bit

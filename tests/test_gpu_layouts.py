@@ -8,7 +8,7 @@ import torch
 
 import workloads
 from oracle import fp8, gemm as G, preshuffle as P, quantize as Q
-from tests.gpu_helpers import check_gemm, dev_bf16, dev_f32, host, require_gpu
+from tests.gpu_helpers import allowed_share, check_gemm, dev_bf16, dev_f32, host, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -146,9 +146,11 @@ def test_training_backward_operands_fused(hq):
     rng = np.random.default_rng(4)
     wt, xt, gt = (np.ascontiguousarray(a.T) for a in (wq, xq, gq))
     pairs = np.stack([rng.integers(0, m, 4000), rng.integers(0, k, 4000)], axis=1)
-    check_gemm(host(dx), gq, fp8.E5M2, wt, fp8.E5M2, gs, sw, pairs=pairs)
+    check_gemm(host(dx), gq, fp8.E5M2, wt, fp8.E5M2, gs, sw, pairs=pairs,
+               max_strict_frac=allowed_share("layouts dgrad", len(pairs)), label="layouts dgrad")
     pairs = np.stack([rng.integers(0, n, 4000), rng.integers(0, k, 4000)], axis=1)
-    check_gemm(host(dw), gt, fp8.E5M2, xt, fp8.E5M2, gs, sx, pairs=pairs)
+    check_gemm(host(dw), gt, fp8.E5M2, xt, fp8.E5M2, gs, sx, pairs=pairs,
+               max_strict_frac=allowed_share("layouts wgrad", len(pairs)), label="layouts wgrad")
 
 
 # ---- stochastic rounding (E5M2) -----------------------------------------------------
