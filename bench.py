@@ -12,8 +12,10 @@ nor a single kernel's timing loop finds its data in the 256 MB Infinity Cache.
 
 Prints one JSON line (stdout). ``value`` = 2*M*N*K / step time (TFLOP/s of the
 whole step). ``roofline`` refers to the dominant kernel (the GEMM), timed with
-HIP events on the stream it runs on. ``cpu_baseline`` times the CPU oracle on a
-bounded sample (see --cpu-rows) and scales it to the same unit.
+HIP events on the stream it runs on. ``cpu_baseline`` times the CPU oracle on
+the same workload for a bounded time (see --cpu-seconds): the whole step at
+full size with the quantizations on a process pool over row blocks and the
+float64 GEMM on the BLAS threads, plus the quantize oracle on one core.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 200]
 
@@ -39,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "a8w8 GEMM TFLOP/s + quantize GB/s (% of MI355X roofline), PTPC 4096³"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA (the strict GEMM's instruction)
 M = N = K = 4096
 COPY_PROBE_BYTES = 1 << 30
 COPY_PROBE_KERNEL = "bitwise_not"
@@ -140,37 +143,91 @@ def traffic_from_profile(name):
     return d.get("bytes_per_launch")
 
 
+_POOL_X = None
+
+
+def _pool_init():
+    """Worker set-up (untimed): the seeded PTPC inputs, made by the generator."""
+    global _POOL_X
+    import workloads
+    _POOL_X = workloads.ptpc_square(1)
+
+
+def _pool_quant(task):
+    """Oracle per-token quantization of rows [lo, hi) of X (which = 0) or W (1)."""
+    from oracle import fp8, quantize as Q
+    which, lo, hi = task
+    q, s, _ = Q.quantize_dynamic(_POOL_X[which][lo:hi], Q.BF16, fp8.E4M3, Q.PER_TOKEN)
+    return which, lo, q, s
+
+
 def cpu_baseline(min_seconds: float):
-    """Time the CPU oracle on the whole 4096^3 step (per-token quantization of X
-    and W, pre-shuffle of WQ, float64 GEMM), repeated until at least
-    `min_seconds` have passed; reports the mean over the repetitions."""
-    import numpy as np  # noqa: F401
+    """Time the CPU oracle on the PTPC 4096^3 workload:
+      * the quantize oracle (per-token E4M3 of X bf16 [4096, 4096]) on one core,
+        in GB/s of the same algorithmic bytes as the GPU quantize;
+      * the whole step: per-token quantization of X and W on a process pool
+        over 64-row blocks (min(16, cpu count) workers), the pre-shuffle of WQ,
+        and the float64 GEMM on the BLAS threads, repeated for at least
+        `min_seconds`; `value` is 2*M*N*K / step time."""
+    import multiprocessing as mp
+
+    import numpy as np
 
     import workloads
     from oracle import fp8, gemm as G, preshuffle as P, quantize as Q
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        blas = 1
     x, w = workloads.ptpc_square(1)
-    reps, t_all = 0, 0.0
-    while reps == 0 or t_all < min_seconds:
+    quant_bytes = M * K * 3 + M * 8
+    # one core: 1024 rows at a time, repeated for about 2 s
+    rows, reps, t1 = 1024, 0, 0.0
+    while reps == 0 or t1 < 2.0:
         t0 = time.perf_counter()
-        xq, xsc, _ = Q.quantize_dynamic(x, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
-        wq, wsc, _ = Q.quantize_dynamic(w, Q.BF16, fp8.E4M3, Q.PER_TOKEN)
-        P.preshuffle(wq)
-        G.gemm_a8w8(xq, fp8.E4M3, wq, fp8.E4M3, xsc, wsc)
-        t_all += time.perf_counter() - t0
+        Q.quantize_dynamic(x[:rows], Q.BF16, fp8.E4M3, Q.PER_TOKEN)
+        t1 += time.perf_counter() - t0
         reps += 1
-    per = t_all / reps
+    gbs_1 = quant_bytes * rows / M / (t1 / reps) / 1e9
+    workers = max(1, min(16, os.cpu_count() or 1))
+    ctx = mp.get_context("spawn")  # fresh interpreters: no GPU state in the workers
+    with ctx.Pool(workers, initializer=_pool_init) as pool:
+        pool.map(_pool_quant, [(0, 0, 1)] * workers)  # workers up (untimed)
+        tasks = [(which, lo, lo + 64) for which in (0, 1) for lo in range(0, M, 64)]
+        steps, t_all, t_quant, t_gemm = 0, 0.0, 0.0, 0.0
+        while steps == 0 or t_all < min_seconds:
+            t0 = time.perf_counter()
+            xq = np.empty((M, K), np.uint8)
+            wq = np.empty((N, K), np.uint8)
+            xs = np.empty(M, np.float32)
+            ws = np.empty(N, np.float32)
+            for which, lo, q, sc in pool.imap_unordered(_pool_quant, tasks, chunksize=4):
+                (xq if which == 0 else wq)[lo:lo + len(q)] = q
+                (xs if which == 0 else ws)[lo:lo + len(sc)] = sc
+            t_q = time.perf_counter()
+            P.preshuffle(wq)
+            G.gemm_a8w8(xq, fp8.E4M3, wq, fp8.E4M3, xs, ws)
+            t_e = time.perf_counter()
+            t_quant += t_q - t0
+            t_gemm += t_e - t_q
+            t_all += t_e - t0
+            steps += 1
+    per = t_all / steps
     return {
         "value": round(2.0 * M * N * K / per / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(max(workers, blas)),
         "kind": "oracle",
-        "sample": (f"the whole step at full size (oracle per-token quantization of X and W, pre-shuffle of WQ, "
-                   f"float64 {M}x{N}x{K} GEMM), {reps} repetitions, {t_all:.1f} s in total, {per:.2f} s each"),
+        "sample": (f"the whole step at full size: oracle per-token quantization of X and W on {workers} worker "
+                   f"processes (64-row blocks), pre-shuffle of WQ, float64 {M}x{N}x{K} GEMM on {blas} BLAS threads; "
+                   f"{steps} steps, {t_all:.1f} s in total, {per:.2f} s each; plus the quantize oracle on one core "
+                   f"over {rows} rows x {reps}"),
+        "os_cpu_count": os.cpu_count(),
+        "quantize_x": {"gbs_1core": round(gbs_1, 4),
+                       "gbs_all_workers": round(2 * quant_bytes / (t_quant / steps) / 1e9, 4),
+                       "workers": workers, "algorithmic_bytes": quant_bytes},
+        "gemm_float64": {"tflops": round(2.0 * M * N * K / (t_gemm / steps) / 1e12, 6), "blas_threads": blas},
     }
 
 
@@ -228,8 +285,16 @@ def other_workloads(torch, hq, lib, reps):
             assert st == 0, hq.hq_last_error()
         ms = time_graph(torch, launch, 2 * copies)
         alg = dn * dk + m * dk + 2 * m * dn + 4 * (m + dn)
+
+        def slaunch(i, h, gx=gx, gxs=gxs, out=out, m=m, work=work, wsb=wsb):
+            st = lib.hq_gemm_a8w8_strict(P(gx.data_ptr()), E4M3, P(pres[i % copies].data_ptr()), E4M3,
+                                         P(gxs.data_ptr()), m, P(gws.data_ptr()), dn, m, dn, dk, None,
+                                         P(out.data_ptr()), P(work.data_ptr()), wsb, h)
+            assert st == 0, hq.hq_last_error()
+        sms = time_graph(torch, slaunch, 2 * copies)
         dec[f"m{m}"] = {"us": round(ms * 1e3, 3), "gbs": round(alg / (ms * 1e-3) / 1e9, 1),
-                        "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg}
+                        "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg,
+                        "strict_us": round(sms * 1e3, 3)}
     res["decode_skinny"] = {"shape": "M in {1,8,32}, N=2048, K=7168, per-token x per-channel E4M3",
                             "rotating_weight_copies": copies, **dec}
     del pres
@@ -254,13 +319,22 @@ def other_workloads(torch, hq, lib, reps):
                                       P(o.data_ptr()), h)
         assert st == 0, hq.hq_last_error()
     ms = time_graph(torch, glaunch, 10)
+
+    def gslaunch(i, h):
+        a, b, o = gsets[i % len(gsets)]
+        st = lib.hq_grouped_gemm_a8w8_strict(P(a.data_ptr()), E4M3, P(b.data_ptr()), E4M3, P(gxs.data_ptr()), t,
+                                             P(gws.data_ptr()), e_ * gn, P(off_d.data_ptr()), e_, t, gn, gk, None,
+                                             P(o.data_ptr()), h)
+        assert st == 0, hq.hq_last_error()
+    strict_ms = time_graph(torch, gslaunch, 10)
     nonempty = int(np.count_nonzero(np.diff(offs)))
     flops = 2.0 * t * gn * gk
     alg = t * gk + nonempty * gn * gk + 2 * t * gn + 4 * (t + e_ * gn)
     res["grouped_moe"] = {"shape": f"{e_} experts ({nonempty} non-empty), N={gn}, K={gk}, {t} rows",
                           "us": round(ms * 1e3, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                           "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                          "gbs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg}
+                          "gbs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg,
+                          "strict_us": round(strict_ms * 1e3, 3)}
     del gsets, gw, pre
 
     # GEMM epilogue variants on the PTPC 4096^3 operands: bf16 bias, and FP8 E4M3 output with an output scale
@@ -287,6 +361,20 @@ def other_workloads(torch, hq, lib, reps):
         ms = time_graph(torch, elaunch, 8)
         ep_res[name] = {"us": round(ms * 1e3, 3), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
     res["gemm_epilogue_ptpc4096"] = ep_res
+    # the strict GEMM (exact products on the float16 matrix cores) on the same operands
+    souts = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+
+    def slaunch4096(i, h):
+        a_, p_ = esets[i % 4]
+        st = lib.hq_gemm_a8w8_strict(P(a_.data_ptr()), E4M3, P(p_.data_ptr()), E4M3, P(gxs.data_ptr()), M,
+                                     P(gws.data_ptr()), N, M, N, K, None, P(souts[i % 4].data_ptr()), None, 0, h)
+        assert st == 0, hq.hq_last_error()
+    ms = time_graph(torch, slaunch4096, 8)
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    res["gemm_strict_ptpc4096"] = {"us": round(ms * 1e3, 3), "tflops": round(tf, 1),
+                                   "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                                   "frac_f16_peak": round(tf / F16_PEAK_TFLOPS, 4)}
+    del souts
     del esets, gx, gw, pre
 
     # quantize of the PTPC X [4096, 4096] bf16 at the other two granularities
@@ -312,9 +400,44 @@ def other_workloads(torch, hq, lib, reps):
     res["quantize_x_other_granularities"] = {"shape": "X bf16 [4096,4096] -> E4M3", **qv}
     del xs_, q
 
+    res["tiny_per_tensor"] = tiny_timings(torch, hq, lib)
     res["blockwise_ptpc4096"] = blockwise_timings(torch, hq, lib)
     res["training_linear"] = training_linear_timings(torch, hq, lib)
     return res
+
+
+def tiny_timings(torch, hq, lib):
+    """The tiny per-tensor workload as one step: per-tensor E4M3 quantization of
+    X fp32 [16, 128] and W fp32 [64, 128] (one pass each, scale reduced on the
+    device), the pre-shuffle of WQ and the GEMM 16 x 64 x 128 into bf16;
+    latency-bound, so reported in microseconds per step (HIP graph)."""
+    import workloads
+    P = ctypes.c_void_p
+    E4M3, F32, TEN = hq.HQ_E4M3, hq.HQ_F32, hq.HQ_PER_TENSOR
+    x, w = workloads.tiny_per_tensor(0)
+    gx, gw = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    xq = torch.empty((16, 128), dtype=torch.uint8, device="cuda")
+    wq = torch.empty((64, 128), dtype=torch.uint8, device="cuda")
+    pre = torch.empty(hq.hq_preshuffled_bytes(64, 128), dtype=torch.uint8, device="cuda")
+    xs, ws = torch.empty(1, device="cuda"), torch.empty(1, device="cuda")
+    out = torch.empty((16, 64), dtype=torch.bfloat16, device="cuda")
+    wsb = int(lib.hq_quantize_workspace_bytes(TEN, 64, 128))
+    wx = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    ww = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+
+    def step(i, h):
+        for src, q, s, work, rows in ((gx, xq, xs, wx, 16), (gw, wq, ws, ww, 64)):
+            st = lib.hq_quantize_fp8(P(src.data_ptr()), F32, rows, 128, E4M3, TEN, P(q.data_ptr()), P(s.data_ptr()),
+                                     None, None, P(work.data_ptr()), wsb, h)
+            assert st == 0, hq.hq_last_error()
+        st = lib.hq_preshuffle_weight(P(wq.data_ptr()), 64, 128, P(pre.data_ptr()), h)
+        assert st == 0, hq.hq_last_error()
+        st = lib.hq_gemm_a8w8(P(xq.data_ptr()), E4M3, P(pre.data_ptr()), E4M3, P(xs.data_ptr()), 1,
+                              P(ws.data_ptr()), 1, 16, 64, 128, P(out.data_ptr()), None, 0, h)
+        assert st == 0, hq.hq_last_error()
+    ms = time_graph(torch, step, 32)
+    return {"shape": "X fp32 [16,128], W fp32 [64,128], per-tensor E4M3, GEMM 16x64x128 -> bf16",
+            "us_per_step": round(ms * 1e3, 3), "launches_per_step": 4}
 
 
 def blockwise_timings(torch, hq, lib):

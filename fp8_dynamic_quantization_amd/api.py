@@ -27,6 +27,7 @@ __all__ = [
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error",
     "hq_gemm_a8w8_strict", "hq_grouped_gemm_a8w8_strict",
+    "hq_quantize_workspace_status",
 ]
 
 _XT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16}
@@ -390,6 +391,17 @@ def hq_gemm_a8w8(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_sca
                            _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(xq.device, stream)))
     return out
+
+
+@_on_stream
+def hq_quantize_workspace_status(workspace: torch.Tensor, stream=None) -> bool:
+    """True if a one-pass per-tensor / per-channel call on this quantize
+    workspace gave up its grid wait since the workspace was zero-filled (its
+    scales are NaN). Synchronises with the stream."""
+    flag = ctypes.c_int32(0)
+    check(load().hq_quantize_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              ctypes.byref(flag), _stream(workspace.device, stream)))
+    return bool(flag.value)
 
 
 def hq_gemm_a8w8_strict(*args, **kwargs) -> torch.Tensor:

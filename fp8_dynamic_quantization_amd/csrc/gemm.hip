@@ -630,6 +630,12 @@ __global__ __launch_bounds__(256 * WM) void grouped_gemm_kernel(GemmArgs a, cons
 // (device-scope counter, reset by that workgroup) adds the S partials in split
 // order and runs the epilogue, so results do not depend on arrival order.
 constexpr int kSkWaves = 16;
+// Workspace of a split launch: the column groups' arrival counters in a fixed
+// leading region (a launch splits only below 256 groups, so 1 KB holds them
+// all), then the partial sums. The region does not depend on the shape, so a
+// workspace shared by launches of different shapes never finds partial sums
+// where another shape's counters are.
+constexpr size_t kSkCounterBytes = 1024;
 
 SkinnyPlan skinny_plan(int m, int n, int k) {
   SkinnyPlan p{};
@@ -642,13 +648,11 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
   // more latency than the extra workgroups save.
   p.splits = 1;
   const int nkb = (k + kBK - 1) / kBK;
-  if (nkb > kSkWaves * p.kpw) {
+  if (nkb > kSkWaves * p.kpw && p.groups < (int)(kSkCounterBytes / 4)) {
     while (p.splits < 8 && p.groups * p.splits < 256) p.splits *= 2;
     while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;  // at least 2 K blocks per workgroup
   }
-  p.workspace_bytes = p.splits == 1 ? 0
-                                    : ((size_t)p.groups * 4 + 255) / 256 * 256 +
-                                          (size_t)p.groups * p.splits * p.f * p.mb * 1024;
+  p.workspace_bytes = p.splits == 1 ? 0 : kSkCounterBytes + (size_t)p.groups * p.splits * p.f * p.mb * 1024;
   return p;
 }
 
@@ -875,7 +879,7 @@ static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t works
   if (p.splits > 1 && (workspace == nullptr || workspace_bytes < p.workspace_bytes)) p.splits = 1;
   uint32_t* counters = static_cast<uint32_t*>(workspace);
   float* partials = p.splits > 1
-                        ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ((size_t)p.groups * 4 + 255) / 256 * 256)
+                        ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSkCounterBytes)
                         : nullptr;
   const dim3 grid(p.groups * p.splits), block(64 * (kSkWaves / p.splits));
   if (p.mb == 1)

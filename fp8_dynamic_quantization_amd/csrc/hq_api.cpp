@@ -523,6 +523,25 @@ static hq_status gemm_impl(const uint8_t* xq, int xf, const uint8_t* wq_pre, int
   return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), name);
 }
 
+hq_status hq_quantize_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* gave_up,
+                                       hipStream_t stream) {
+  if (!gave_up) return fail(HQ_ERR_INVALID_ARGUMENT, "gave_up must be non-NULL");
+  if (!workspace) return fail(HQ_ERR_INVALID_ARGUMENT, "workspace must be non-NULL");
+  if (workspace_bytes < hq::kTensorWorkspaceBytes)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "workspace_bytes %zu is less than the %zu of a quantize workspace",
+                workspace_bytes, hq::kTensorWorkspaceBytes);
+  if (!aligned(workspace, 16)) return fail(HQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  uint32_t word = 0;
+  const uint8_t* src = static_cast<const uint8_t*>(workspace) + (hq::kBarrierOffsetWords + hq::kBarStatus) * 4;
+  hipError_t e = hipMemcpyAsync(&word, src, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(HQ_ERR_LAUNCH, "hq_quantize_workspace_status: %s", hipGetErrorString(e));
+  *gave_up = (word & hq::kGaveUpBit) ? 1 : 0;
+  return ok();
+}
+
 hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
                                 int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m,
                                 int64_t n, int64_t k, const hq_epilogue* ep, void* out, void* workspace,

@@ -18,9 +18,12 @@ constexpr int kArrivalGroups = 32;
 constexpr int kArrivalStride = 32;        // uint32 words between arrival counters (128 bytes)
 // The single-pass per-tensor kernel's grid barrier follows the arrival
 // counters, one 128-byte line each: a 64-bit word (generation in the high
-// half, the last call's tensor amax bits in the low half) and the top arrival
-// counter.
-constexpr int kBarGen = 0, kBarTop = kArrivalStride, kBarWords = 2 * kArrivalStride;
+// half, the last call's tensor amax bits in the low half), the top arrival
+// counter, and a sticky status word whose bit 0 a single-pass kernel sets when
+// one of its blocks gave up its bounded wait (the call's scales are then NaN;
+// the bit stays set until the workspace is zero-filled again).
+constexpr int kBarGen = 0, kBarTop = kArrivalStride, kBarStatus = 2 * kArrivalStride, kBarWords = 3 * kArrivalStride;
+constexpr uint32_t kGaveUpBit = 1u;
 constexpr size_t kArrivalOffsetWords = kMaxTensorPartials;
 constexpr size_t kBarrierOffsetWords = kArrivalOffsetWords + (size_t)kArrivalGroups * kArrivalStride;
 constexpr size_t kTensorWorkspaceBytes = (kBarrierOffsetWords + kBarWords) * 4;
@@ -109,6 +112,7 @@ SkinnyPlan skinny_plan(int m, int n, int k);
 // are left zero by every launch.
 size_t gemm_workspace_bytes(int m, int n, int k);
 hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_t workspace_bytes, hipStream_t st);
+
 
 // Block-wise quantization: scales [rows, ceil(cols / bs)], bs in {16, 32, 64, 128}.
 hipError_t launch_quant_blocks(const void* x, int xt, int rows, int cols, int fmt, int bs, bool sr, uint64_t seed,

@@ -299,8 +299,14 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
 // block casts its registers. The launcher only uses this kernel when the whole
 // grid fits on the device at once (occupancy query), so every block is
 // resident and the wait ends; as a guard the poll gives up after
-// kBarrierSpinTicks of the 100 MHz real-time clock and the block then reports
-// a NaN scale instead of waiting further.
+// kBarrierSpinTicks of the 100 MHz real-time clock (a co-scheduled kernel
+// holding CUs could keep blocks off the device). A block that gives up sets the
+// workspace's sticky status bit (hq_quantize_workspace_status reports it) and
+// writes a NaN scale; the block that writes the valid scale re-reads the bit
+// after its write and overwrites the scale with NaN when it is set. Scale
+// writes are device-scope atomic stores, so of two writes the later one in the
+// coherence order stays: either the writer of the valid scale sees the bit, or
+// the NaN write comes after it. NaN wins either way.
 constexpr uint64_t kBarrierSpinTicks = 50000000;  // 0.5 s
 constexpr int kFusedBlocks = 512;  // two per CU (measured: 12.8 us for bf16 [4096, 4096], 13.7 at 1024)
 
@@ -372,7 +378,11 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_fused_kernel(const uint4*
         got = (uint32_t)w;
         break;
       }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierSpinTicks) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierSpinTicks) {
+        __hip_atomic_fetch_or(bar + kBarStatus, kGaveUpBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     sh[2] = got;
@@ -384,8 +394,13 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_fused_kernel(const uint4*
   const float s = gave_up ? __uint_as_float(0x7fc00000u) : scale_from_amax<FMT>(amax);
   const float r = 1.0f / s;
   if (threadIdx.x == 0 && (blockIdx.x == 0 || gave_up)) {
-    scale[0] = s;
-    if (amax_out) amax_out[0] = amax;
+    __hip_atomic_store(scale, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (amax_out) __hip_atomic_store(amax_out, amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!gave_up) {
+      __builtin_amdgcn_s_waitcnt(0);
+      if (__hip_atomic_load(bar + kBarStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kGaveUpBit)
+        __hip_atomic_store(scale, __uint_as_float(0x7fc00000u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   // (the codes need no tensor-wide non-finite flag: the cast patches NaN per vector)
 #pragma unroll
@@ -533,8 +548,13 @@ __device__ __forceinline__ void col_tile_scales(const uint32_t* partial, int nch
       const float s = scale_from_amax<FMT>(amax);
       rcp[c] = 1.0f / s;
       if (blockIdx.y == 0) {
-        scale[col] = s;
-        if (amax_out) amax_out[col] = amax;
+        if constexpr (ATOMIC) {
+          __hip_atomic_store(scale + col, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (amax_out) __hip_atomic_store(amax_out + col, amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          scale[col] = s;
+          if (amax_out) amax_out[col] = amax;
+        }
       }
     } else {
       rcp[c] = 0.0f;
@@ -672,6 +692,8 @@ __global__ __launch_bounds__(kBlock) void quant_cols_fused_kernel(const uint4* _
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       while ((uint32_t)(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) == g0) {
         if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierSpinTicks) {
+          __hip_atomic_fetch_or(bar + kBarStatus, kGaveUpBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(0);
           gave_up = 1u;
           break;
         }
@@ -682,14 +704,32 @@ __global__ __launch_bounds__(kBlock) void quant_cols_fused_kernel(const uint4* _
   }
   __syncthreads();
   if (sh[1]) {
-    // the wait gave up: report NaN scales for this tile's columns instead of codes
+    // the wait gave up (status bit set above): NaN scales for this tile's
+    // columns instead of codes
     for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
       const int col = blockIdx.x * kColVecs * E + c;
-      if (col < cols) scale[col] = __uint_as_float(0x7fc00000u);
+      if (col < cols) __hip_atomic_store(scale + col, __uint_as_float(0x7fc00000u), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
   col_tile_scales<FMT, E, true>(partial, gridDim.y, cols, scale, amax_out, rcp, flags);
+  if (blockIdx.y == 0) {
+    // the writer of these columns' scales: once every thread's scale store has
+    // completed, if any block gave up, NaN wins
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      sh[1] = __hip_atomic_load(bar + kBarStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kGaveUpBit;
+    __syncthreads();
+    if (sh[1]) {
+      for (int c = threadIdx.x; c < kColVecs * E; c += kBlock) {
+        const int col = blockIdx.x * kColVecs * E + c;
+        if (col < cols) __hip_atomic_store(scale + col, __uint_as_float(0x7fc00000u), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
   if (vc >= vpr) return;
   col_tile_cast<XT, FMT, SR>(v, rows, vpr, r0, vc, tx, ty, rcp, flags, q, sd);
 }

@@ -84,8 +84,8 @@ int64_t hq_scale_count(int gran, int64_t rows, int64_t cols);
 
 /* Bytes of device workspace hq_quantize_fp8 needs for this granularity and
  * shape: 0 for HQ_PER_TOKEN; for HQ_PER_TENSOR (dynamic or delayed) a fixed
- * 8448-byte region of block partials, arrival counters and the single-pass
- * grid barrier; for HQ_PER_CHANNEL that region plus ceil(rows/128) * cols * 4 bytes
+ * 8576-byte region of block partials, arrival counters, the single-pass grid
+ * barrier and its status word; for HQ_PER_CHANNEL that region plus ceil(rows/128) * cols * 4 bytes
  * of column partials after it (so one workspace sized for the largest call
  * serves every granularity). Returns 0 for invalid arguments (hq_quantize_fp8
  * then reports the error). */
@@ -125,7 +125,12 @@ size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
  *              per-channel quantization whose tiles of 128 rows x 256 bf16
  *              (128 float32) columns number at most 512, run as one pass over
  *              x whose blocks agree on the maxima through the workspace;
- *              other sizes take a partial-max pass first.
+ *              other sizes take a partial-max pass first. The one-pass form
+ *              needs its whole grid resident at once (checked by an occupancy
+ *              query before the launch); a block that still waits longer than
+ *              0.5 s (other work holding the device) gives up, the call's
+ *              affected scales come out NaN, and a sticky bit in the workspace
+ *              records it (hq_quantize_workspace_status).
  * Requires cols % 16 == 0 (16-byte vector rows), 1 <= rows, cols < 2^31,
  * rows * cols < 2^40. rows == 0 returns HQ_OK without a launch. Outputs must not
  * overlap inputs. */
@@ -134,6 +139,18 @@ hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols,
                           float* amax_out, const hq_ring* ring,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* Whether any one-pass per-tensor or per-channel call on this quantize
+ * workspace (since it was last zero-filled) gave up its grid wait: *gave_up = 1
+ * if so (that call's scales, or those of the columns it covered, are NaN and
+ * the call should be repeated after zero-filling the workspace), else 0. Reads
+ * the workspace's status word after the work already on `stream` (a
+ * synchronous device-to-host copy: not for the hot path).
+ *   workspace  device, a quantize workspace of workspace_bytes >=
+ *              hq_quantize_workspace_bytes(HQ_PER_TENSOR, 1, 16) bytes
+ *   gave_up    host pointer */
+hq_status hq_quantize_workspace_status(const void* workspace, size_t workspace_bytes, int32_t* gave_up,
+                                       hipStream_t stream);
 
 /* hq_quantize_fp8 to E5M2 with stochastic rounding (hip-quant README,
  * "Stochastic E5M2 Backward Gradients": each value rounds to one of the two
@@ -322,9 +339,10 @@ int64_t hq_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *             overlap any input. Written in full; nothing else is touched.
  *   workspace device scratch of workspace_bytes bytes, 16-byte aligned, or NULL
  *             with workspace_bytes == 0. Zero-fill it once before its first
- *             use: its leading words are per-column-group arrival counters that
- *             every call leaves at zero again (the rest holds partial sums and
- *             needs no reset). With at least
+ *             use: its first 1024 bytes are per-column-group arrival counters
+ *             that every call leaves at zero again, the rest holds partial sums
+ *             and needs no reset (the layout does not depend on the shape, so
+ *             one workspace serves calls of any shapes). With at least
  *             hq_gemm_workspace_bytes(m, n, k) bytes the decode shapes split
  *             their weight stream over more workgroups; with less they run
  *             unsplit, slower but with the same output bits (the order of the

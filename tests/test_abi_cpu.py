@@ -84,6 +84,9 @@ def test_workspace_bytes(hq):
     assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_TOKEN, 4096, 4096) == 0
     assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 4096, 4096) > 0
     region = hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 1, 16)
+    # 1024 partial words, 32 arrival-counter lines, 3 barrier lines (generation
+    # word, top counter, sticky status)
+    assert region == 1024 * 4 + 32 * 128 + 3 * 128
     assert region == hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 4096, 4096)
     # per-channel: the per-tensor region, then ceil(rows/128) * cols column partials
     assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 4096, 4096) == region + 32 * 4096 * 4
@@ -246,20 +249,20 @@ def test_gemm_valid_call_reaches_device_gate(hq):
 
 
 def test_gemm_workspace_bytes(hq):
-    """Split plan of the weight-streaming kernel: one 4-byte counter per column
-    group (padded to 256 bytes) + 1 KB of fp32 partials per (group, split,
-    fragment, 16-row block)."""
+    """Split plan of the weight-streaming kernel: a fixed 1 KB region of 4-byte
+    column-group counters + 1 KB of fp32 partials per (group, split, fragment,
+    16-row block)."""
     # m <= 16 splits only past 64 K blocks (16 wavefronts x 4 blocks per chunk)
     assert hq.hq_gemm_workspace_bytes(1, 2048, 7168) == 0
     assert hq.hq_gemm_workspace_bytes(16, 2048, 8192) == 0
     # m=1, n=2048, k=14336: 128 one-fragment groups, split 2 -> 256 workgroups
-    assert hq.hq_gemm_workspace_bytes(1, 2048, 14336) == 512 + 128 * 2 * 1024
-    assert hq.hq_gemm_workspace_bytes(16, 2048, 8208) == 512 + 128 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(1, 2048, 14336) == 1024 + 128 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(16, 2048, 8208) == 1024 + 128 * 2 * 1024
     # m=32 (past 32 K blocks): 64 two-fragment groups of 2 row blocks, split 4
-    assert hq.hq_gemm_workspace_bytes(32, 2048, 7168) == 256 + 64 * 4 * 2 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(32, 2048, 7168) == 1024 + 64 * 4 * 2 * 2 * 1024
     assert hq.hq_gemm_workspace_bytes(32, 2048, 4096) == 0
     # m=64 (past 16 K blocks): 4 row blocks
-    assert hq.hq_gemm_workspace_bytes(64, 2048, 7168) == 256 + 64 * 4 * 2 * 4 * 1024
+    assert hq.hq_gemm_workspace_bytes(64, 2048, 7168) == 1024 + 64 * 4 * 2 * 4 * 1024
     assert hq.hq_gemm_workspace_bytes(64, 2048, 2048) == 0
     # enough column groups already (n=7168: 448 fragments) -> no split
     assert hq.hq_gemm_workspace_bytes(4, 7168, 2048) == 0
@@ -530,3 +533,57 @@ def test_layouts_stochastic_validation(hq):
     if not _gpu_visible():
         assert call() == hq.HQ_ERR_UNSUPPORTED_DEVICE
         assert call(scale_in=fake(5), ws=None, wsb=0) == hq.HQ_ERR_UNSUPPORTED_DEVICE
+
+
+# ---- strict GEMMs, the workspace status query ----------------------------------
+
+def _gemm_strict(hq, xf=0, m=64, n=128, k=256, xsc=64, out=fake(4), ep=None):
+    return hq.load().hq_gemm_a8w8_strict(fake(0), xf, fake(1), 0, fake(2), xsc, fake(3), n, m, n, k,
+                                         ctypes.byref(ep) if ep is not None else None, out, None, 0, None)
+
+
+def _grouped_strict(hq, e=8, t=512, n=128, k=256, out=fake(4)):
+    return hq.load().hq_grouped_gemm_a8w8_strict(fake(0), 0, fake(1), 0, fake(2), t, fake(3), e * n, fake(5), e,
+                                                 t, n, k, None, out, None)
+
+
+def test_strict_validation(hq):
+    """The strict GEMMs validate exactly as hq_gemm_a8w8."""
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    for call in (_gemm_strict,):
+        assert call(hq, xf=3) == E
+        assert call(hq, k=100) == E
+        assert call(hq, xsc=7) == E
+        assert call(hq, out=fake(4, 8)) == E
+        assert call(hq, out=fake(0, 16)) == E  # out overlaps xq
+        assert "overlaps" in hq.hq_last_error()
+        assert call(hq, m=0, xsc=1) == hq.HQ_OK
+    assert _grouped_strict(hq, e=0) == E
+    assert _grouped_strict(hq, out=fake(0, 16)) == E
+    assert _grouped_strict(hq, t=0) == hq.HQ_OK
+
+
+@no_gpu
+def test_strict_valid_calls_reach_device_gate(hq):
+    D = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    assert _gemm_strict(hq) == D
+    assert _grouped_strict(hq) == D
+
+
+def test_workspace_status_validation(hq):
+    lib = hq.load()
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    region = hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 1, 16)
+    flag = ctypes.c_int32(0)
+    assert lib.hq_quantize_workspace_status(fake(4), region, None, None) == E
+    assert lib.hq_quantize_workspace_status(None, region, ctypes.byref(flag), None) == E
+    assert lib.hq_quantize_workspace_status(fake(4), region - 4, ctypes.byref(flag), None) == E
+    assert lib.hq_quantize_workspace_status(fake(4, 8), region, ctypes.byref(flag), None) == E
+
+
+@no_gpu
+def test_workspace_status_valid_call_reaches_device_gate(hq):
+    region = hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 1, 16)
+    flag = ctypes.c_int32(0)
+    assert hq.load().hq_quantize_workspace_status(fake(4), region, ctypes.byref(flag), None) == \
+        hq.HQ_ERR_UNSUPPORTED_DEVICE

@@ -283,6 +283,28 @@ def test_skinny_split_matches_unsplit_and_oracle(hq, shape):
     assert int(work[:4 * groups].count_nonzero()) == 0
 
 
+def test_workspace_shared_across_decode_shapes(hq):
+    """One workspace serves split launches of different shapes in turn: a
+    shape with few column groups (its partial sums right after the counter
+    region), then one with many (whose counters must not land on those
+    partials), then the first again; each bit-identical to its unsplit launch."""
+    shapes = [(1, 320, 14336), (1, 2048, 14336), (1, 320, 14336), (16, 1024, 9216)]
+    need = max(hq.hq_gemm_workspace_bytes(*s) for s in shapes)
+    work = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(99)
+    for m, n, k in shapes:
+        assert hq.hq_gemm_workspace_bytes(m, n, k) > 0
+        xq = _finite_codes(rng, (m, k), fp8.E4M3)
+        wq = _finite_codes(rng, (n, k), fp8.E4M3)
+        gx, pre = dev_u8(xq), hq.hq_preshuffle_weight(dev_u8(wq))
+        xs, ws = dev_f32(rng.uniform(1e-3, 1e-2, m)), dev_f32(rng.uniform(1e-3, 1e-2, n))
+        plain = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, xs, ws, n, workspace=False))
+        split = host(hq.hq_gemm_a8w8(gx, fp8.E4M3, pre, fp8.E4M3, xs, ws, n, workspace=work))
+        assert np.array_equal(split, plain), (m, n, k)
+    torch.cuda.synchronize()
+    assert int(work[:1024].count_nonzero()) == 0
+
+
 def test_empty_output_is_noop(hq):
     xq = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
     wq = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")

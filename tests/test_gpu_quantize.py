@@ -244,6 +244,32 @@ def test_single_pass_barrier_state(hq):
         assert (int(w[word_hi]), int(w[word_lo])) == (gen, last_amax), (t, sh)
 
 
+def test_single_pass_give_up_is_reported(hq):
+    """A one-pass per-tensor or per-channel call whose blocks cannot all meet
+    (forced from the host: the workspace filled with 0x40 bytes, so no arrival
+    counter ever reaches its last member and no block releases the others)
+    has every block give up its bounded wait (0.5 s) and exit: every scale it
+    writes is NaN and the workspace's sticky status bit reports it. After a
+    zero fill the same workspace serves a normal call again, status clear."""
+    rng = np.random.default_rng(31)
+    bits = workloads.random_bf16(rng, (1024, 2048))
+    ws = torch.zeros(hq.hq_quantize_workspace_bytes(Q.PER_CHANNEL, 1024, 2048), dtype=torch.uint8, device="cuda")
+    assert not hq.hq_quantize_workspace_status(ws)
+    for gran in (Q.PER_TENSOR, Q.PER_CHANNEL):
+        ws.fill_(0x40)
+        assert not hq.hq_quantize_workspace_status(ws)  # bit 0 of 0x40404040 is clear
+        _, s, _ = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, gran, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.all(np.isnan(host(s))), gran
+        assert hq.hq_quantize_workspace_status(ws), gran
+        ws.zero_()
+        q, s, a = hq.hq_quantize_fp8(dev_bf16(bits), fp8.E4M3, gran, workspace=ws)
+        q_ref, s_ref, a_ref = Q.quantize_dynamic(bits, Q.BF16, fp8.E4M3, gran)
+        assert np.array_equal(host(q), q_ref)
+        assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+        assert not hq.hq_quantize_workspace_status(ws)
+
+
 # ---- delayed scaling ---------------------------------------------------------------
 
 def test_delayed_shared_workspace_varying_grids(hq):
