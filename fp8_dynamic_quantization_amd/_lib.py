@@ -94,6 +94,7 @@ SIGNATURES = {
     "hq_grouped_gemm_a8w8_epilogue": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,
                                            ctypes.POINTER(hq_epilogue), _P, _P]),
     "hq_quantize_workspace_status": (_I, [_P, _SZ, ctypes.POINTER(_I32), _P]),
+    "hq_gemm_a8w8_noalloc": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P]),
     "hq_gemm_a8w8_strict": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _I64, _I64, _I64, ctypes.POINTER(hq_epilogue),
                                  _P, _P, _SZ, _P]),
     "hq_grouped_gemm_a8w8_strict": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,

@@ -26,7 +26,7 @@ __all__ = [
     "hq_gemm_a8w8_blockscaled", "hq_gemm_a8w8_blockscaled_preshuffled", "hq_scale_ring_update", "hq_preshuffle_weight", "hq_gemm_a8w8",
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error",
-    "hq_gemm_a8w8_strict", "hq_grouped_gemm_a8w8_strict",
+    "hq_gemm_a8w8_strict", "hq_grouped_gemm_a8w8_strict", "hq_gemm_a8w8_noalloc",
     "hq_quantize_workspace_status",
 ]
 
@@ -402,6 +402,22 @@ def hq_quantize_workspace_status(workspace: torch.Tensor, stream=None) -> bool:
     check(load().hq_quantize_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                               ctypes.byref(flag), _stream(workspace.device, stream)))
     return bool(flag.value)
+
+
+@_on_stream
+def hq_gemm_a8w8_noalloc(xq: torch.Tensor, xf: int, wq_pre: torch.Tensor, wf: int, x_scale: torch.Tensor,
+                         w_scale: torch.Tensor, n: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """hq_gemm_a8w8 with the library's own device scratch (no workspace, no
+    allocation in the call; `out` is required). Calls that overlap on one GPU
+    race on that scratch."""
+    for t in (xq, wq_pre, x_scale, w_scale, out):
+        if not t.is_contiguous():
+            raise ValueError("hq_gemm_a8w8_noalloc takes contiguous tensors (it makes no copies)")
+    m, k = xq.shape
+    check(load().hq_gemm_a8w8_noalloc(_ptr(xq), xf, _ptr(wq_pre), wf, _ptr(x_scale), x_scale.numel(),
+                                      _ptr(w_scale), w_scale.numel(), m, n, k, _ptr(out),
+                                      _stream(xq.device, stream)))
+    return out
 
 
 def hq_gemm_a8w8_strict(*args, **kwargs) -> torch.Tensor:

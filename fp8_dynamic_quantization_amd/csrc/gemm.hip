@@ -33,6 +33,8 @@
 #include "hq_device.h"
 #include "hq_launch.h"
 
+#include <mutex>
+
 namespace hq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -1045,6 +1047,47 @@ static hipError_t launch_grouped_t(const GemmArgs& a, const int32_t* offsets, in
     else if ((WF) == kE4M3) { CALL(kE5M2, kE4M3); }               \
     else { CALL(kE5M2, kE5M2); }                                  \
   } while (0)
+
+// ---------------------------------------------------------------------------
+// library-held scratch (hq_gemm_a8w8_noalloc)
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops), split decode launches take their workspace
+// from this file-scope device array instead of a caller buffer. Each GPU holds
+// its own copy until the process ends; host code reaches it only through the
+// per-device address from hipGetSymbolAddress (the array's name in host code is
+// a host-side stand-in, not a device address). The counter region is zeroed
+// once per device at set-up, by a small kernel on the caller's stream, and every
+// launch leaves it at zero; the partial sums need no reset. Every call on a GPU
+// shares that GPU's array, so calls that overlap on one GPU race on it.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t noalloc_scratch(hipStream_t st, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    constexpr int words = (int)(kSkCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st, static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t gemm_workspace_bytes(int m, int n, int k) {
   return m >= 1 && m <= kSkinnyMaxM ? skinny_plan(m, n, k).workspace_bytes : 0;

@@ -15,7 +15,6 @@
 
 #include <mutex>
 #include <string>
-#include <unordered_map>
 
 #include "hq_launch.h"
 
@@ -65,20 +64,21 @@ const char* find_overlap(const Range* r, int n, const char** other) {
   return nullptr;
 }
 
-// gfx950 gate for the current device, cached per device.
+// gfx950 gate for the current device, cached per device in a fixed table (no
+// allocation on any call).
 hq_status check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return fail(HQ_ERR_UNSUPPORTED_DEVICE, "no HIP device is available (libhq requires an MI355X / gfx950)");
   }
+  if (dev < 0 || dev >= hq::kMaxDevices) return fail(HQ_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
   static std::mutex mu;
-  static std::unordered_map<int, bool> cache;
+  static int8_t cache[hq::kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
   {
     std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(dev);
-    if (it != cache.end()) {
-      if (!it->second) return fail(HQ_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+    if (cache[dev] != 0) {
+      if (cache[dev] < 0) return fail(HQ_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
       return HQ_OK;
     }
   }
@@ -91,7 +91,7 @@ hq_status check_device() {
                      (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
   {
     std::lock_guard<std::mutex> lk(mu);
-    cache.emplace(dev, is950);
+    cache[dev] = is950 ? 1 : -1;
   }
   if (!is950) return fail(HQ_ERR_UNSUPPORTED_DEVICE, "device %d is %s, libhq requires gfx950", dev, prop.gcnArchName);
   return HQ_OK;
@@ -471,10 +471,12 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                                out, workspace, workspace_bytes, stream);
 }
 
+// library_scratch: take the split workspace from the library's device array
+// (hq_gemm_a8w8_noalloc) instead of `workspace`, which is then NULL / 0.
 static hq_status gemm_impl(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
                            int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m, int64_t n,
                            int64_t k, const hq_epilogue* ep, void* out, void* workspace, size_t workspace_bytes,
-                           bool strict, const char* name, hipStream_t stream) {
+                           bool strict, const char* name, hipStream_t stream, bool library_scratch = false) {
   hq_status st = check_gemm_common(xf, wf, m, n, k);
   if (st != HQ_OK) return st;
   if (workspace_bytes > 0 && workspace == nullptr)
@@ -514,12 +516,28 @@ static hq_status gemm_impl(const uint8_t* xq, int xf, const uint8_t* wq_pre, int
   const char* a = find_overlap(rg, 9, &other);
   if (a && (strcmp(a, "out") == 0 || strcmp(a, "workspace") == 0))
     return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  size_t scratch_need = 0;
+  if (library_scratch) {
+    scratch_need = hq::gemm_workspace_bytes((int)m, (int)n, (int)k);
+    if (scratch_need > hq::kNoAllocScratchBytes)
+      return fail(HQ_ERR_INVALID_ARGUMENT, "%s: m=%lld n=%lld k=%lld needs %zu bytes of scratch, more than the %zu the "
+                  "library holds", name, (long long)m, (long long)n, (long long)k, scratch_need,
+                  hq::kNoAllocScratchBytes);
+  }
   st = check_device();
   if (st != HQ_OK) return st;
   hq::GemmArgs g{xq, wq_pre, x_scale, w_scale, out, (int)m, (int)n, (int)k, x_scale_count != 1, w_scale_count != 1,
                  bias, bias_kind, bias_scale, out_scale, out_fmt};
   g.strict = strict;
   (void)hipGetLastError();
+  if (library_scratch) {
+    void* scratch = nullptr;
+    if (scratch_need > 0) {
+      const hipError_t e = hq::noalloc_scratch(stream, &scratch);
+      if (e != hipSuccess) return fail(HQ_ERR_LAUNCH, "%s: library scratch: %s", name, hipGetErrorString(e));
+    }
+    return launched(hq::launch_gemm(g, xf, wf, scratch, scratch_need, stream), name);
+  }
   return launched(hq::launch_gemm(g, xf, wf, ws_used ? workspace : nullptr, ws_used, stream), name);
 }
 
@@ -540,6 +558,13 @@ hq_status hq_quantize_workspace_status(const void* workspace, size_t workspace_b
   if (e != hipSuccess) return fail(HQ_ERR_LAUNCH, "hq_quantize_workspace_status: %s", hipGetErrorString(e));
   *gave_up = (word & hq::kGaveUpBit) ? 1 : 0;
   return ok();
+}
+
+hq_status hq_gemm_a8w8_noalloc(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,
+                               int64_t x_scale_count, const float* w_scale, int64_t w_scale_count, int64_t m,
+                               int64_t n, int64_t k, uint16_t* out, hipStream_t stream) {
+  return gemm_impl(xq, xf, wq_pre, wf, x_scale, x_scale_count, w_scale, w_scale_count, m, n, k, nullptr, out, nullptr,
+                   0, false, "hq_gemm_a8w8_noalloc", stream, true);
 }
 
 hq_status hq_gemm_a8w8_epilogue(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf, const float* x_scale,

@@ -113,6 +113,14 @@ SkinnyPlan skinny_plan(int m, int n, int k);
 size_t gemm_workspace_bytes(int m, int n, int k);
 hipError_t launch_gemm(const GemmArgs& a, int xf, int wf, void* workspace, size_t workspace_bytes, hipStream_t st);
 
+// Library-held GEMM scratch for callers that cannot allocate: a file-scope
+// device array of kNoAllocScratchBytes per GPU (the largest split plan needs
+// under 4.1 MiB). noalloc_scratch returns the current device's address of it,
+// looked up once per device with hipGetSymbolAddress, whose counter region is
+// zeroed at that first lookup by a kernel on `st`.
+constexpr size_t kNoAllocScratchBytes = (size_t)4352 << 10;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(hipStream_t st, void** ptr);
 
 // Block-wise quantization: scales [rows, ceil(cols / bs)], bs in {16, 32, 64, 128}.
 hipError_t launch_quant_blocks(const void* x, int xt, int rows, int cols, int fmt, int bs, bool sr, uint64_t seed,

@@ -356,6 +356,25 @@ hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                        int64_t m, int64_t n, int64_t k, uint16_t* out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* hq_gemm_a8w8 for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, arguments, requirements and output bits, with no workspace
+ * argument. The split decode launches (1 <= m <= 64) take their scratch from
+ * a device array the library holds for each GPU (4.25 MiB, kept until the
+ * process ends; its address is looked up once per device, and the first call
+ * on a device also enqueues a small kernel on `stream` that zeroes the
+ * array's counters). The call allocates nothing: no hipMalloc, no hipFree. A
+ * shape whose split plan needs more scratch than that is rejected with
+ * HQ_ERR_INVALID_ARGUMENT (no valid shape does today: the largest plan needs
+ * under 4.1 MiB). Every call on a GPU shares that GPU's array, which keeps the
+ * last call's partial sums: calls that overlap on one GPU (concurrent
+ * streams, host threads) race and must not be made. */
+hq_status hq_gemm_a8w8_noalloc(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
+                               const float* x_scale, int64_t x_scale_count,
+                               const float* w_scale, int64_t w_scale_count,
+                               int64_t m, int64_t n, int64_t k, uint16_t* out,
+                               hipStream_t stream);
+
 /* Kinds of GEMM epilogue bias (AstrAI ops.cu, linear_forward_fp8: a bf16 bias
  * as is, or a pre-quantized FP8 bias with its bias_scale). */
 typedef enum hq_bias { HQ_BIAS_BF16 = 0, HQ_BIAS_E4M3 = 1, HQ_BIAS_E5M2 = 2 } hq_bias;

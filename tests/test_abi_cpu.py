@@ -535,7 +535,7 @@ def test_layouts_stochastic_validation(hq):
         assert call(scale_in=fake(5), ws=None, wsb=0) == hq.HQ_ERR_UNSUPPORTED_DEVICE
 
 
-# ---- strict GEMMs, the workspace status query ----------------------------------
+# ---- strict GEMMs, the no-allocation GEMM, the workspace status query ----------
 
 def _gemm_strict(hq, xf=0, m=64, n=128, k=256, xsc=64, out=fake(4), ep=None):
     return hq.load().hq_gemm_a8w8_strict(fake(0), xf, fake(1), 0, fake(2), xsc, fake(3), n, m, n, k,
@@ -547,10 +547,14 @@ def _grouped_strict(hq, e=8, t=512, n=128, k=256, out=fake(4)):
                                                  t, n, k, None, out, None)
 
 
-def test_strict_validation(hq):
-    """The strict GEMMs validate exactly as hq_gemm_a8w8."""
+def _gemm_noalloc(hq, xf=0, m=64, n=128, k=256, xsc=64, out=fake(4)):
+    return hq.load().hq_gemm_a8w8_noalloc(fake(0), xf, fake(1), 0, fake(2), xsc, fake(3), n, m, n, k, out, None)
+
+
+def test_strict_and_noalloc_validation(hq):
+    """The strict and no-allocation GEMMs validate exactly as hq_gemm_a8w8."""
     E = hq.HQ_ERR_INVALID_ARGUMENT
-    for call in (_gemm_strict,):
+    for call in (_gemm_strict, _gemm_noalloc):
         assert call(hq, xf=3) == E
         assert call(hq, k=100) == E
         assert call(hq, xsc=7) == E
@@ -564,10 +568,12 @@ def test_strict_validation(hq):
 
 
 @no_gpu
-def test_strict_valid_calls_reach_device_gate(hq):
+def test_strict_and_noalloc_valid_calls_reach_device_gate(hq):
     D = hq.HQ_ERR_UNSUPPORTED_DEVICE
     assert _gemm_strict(hq) == D
     assert _grouped_strict(hq) == D
+    assert _gemm_noalloc(hq) == D
+    assert _gemm_noalloc(hq, m=16, xsc=16, n=2048, k=14336) == D  # a split decode plan
 
 
 def test_workspace_status_validation(hq):
