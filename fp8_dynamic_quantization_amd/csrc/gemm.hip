@@ -250,26 +250,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   const int b_vo0 = NB > 1 ? (kg & 1) * 1024 + (kg >> 1) * 256 + slot16 : lane * 16;
   const int b_vo1 = NB > 1 ? (kg & 1) * 1024 + (2 + (kg >> 1)) * 256 + slot16 : lane * 16 + 1024;
 
-  // The epilogue's scales go to LDS (after the two A stages) at the start, so
-  // their load latency hides behind the K loop: x_scale of the tile's BM rows,
-  // w_scale of its 4*TN columns (clamped at the edges; masked on store).
+  // The epilogue's scales go to LDS (after the two A stages) during the
+  // prologue: x_scale of the tile's BM rows, w_scale of its 4*TN columns
+  // (clamped at the edges; masked on store), one of each per thread at most.
+  // Their loads are issued after the first operand loads and written to LDS
+  // just before the prologue's barrier, so no operand load waits for them.
+  static_assert(BM <= C::kThreads && C::kBN <= C::kThreads, "one epilogue scale of each kind per thread");
   float* s_xs = reinterpret_cast<float*>(lds + 2 * C::kABytes);
   float* s_ws = s_xs + BM;
-  if constexpr (!BSF) {
-    for (int t = tid; t < BM; t += C::kThreads) {
-      const int row = min(m0 + t, row_end - 1);
-      s_xs[t] = a.x_scale_per_row ? a.x_scale[row] : a.x_scale[0];
-    }
-    for (int t = tid; t < C::kBN; t += C::kThreads) {
-      const int col = min(n0 + t, a.n - 1);
-      s_ws[t] = a.w_scale_per_col ? ws[col] : ws[0];
-    }
-  }
   float* s_bias = s_ws + C::kBN;
-  if (a.bias_kind != kBiasNone) {
-    const float bsc = a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0];
-    for (int t = tid; t < C::kBN; t += C::kThreads) s_bias[t] = bias_at(a, min(n0 + t, a.n - 1), bsc);
-  }
 
   // Block scales (BSZ > 0): thread t < BM holds the NB scales of tile row t,
   // thread BM + c those of tile column c, for one K step; a step's values sit in
@@ -444,6 +433,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   ra_valid = a_c * 16 < K;
 #pragma unroll
   for (int h = 0; h < 2 * C::kIN; ++h) HQ_LOAD_B_HALF(0, fb0, h);
+  float xs_v = 0.0f, ws_v = 0.0f;
+  if constexpr (!BSF) {
+    if (tid < BM) xs_v = a.x_scale[a.x_scale_per_row ? min(m0 + tid, row_end - 1) : 0];
+    if (tid < C::kBN) ws_v = ws[a.w_scale_per_col ? min(n0 + tid, a.n - 1) : 0];
+  }
 #pragma unroll
   for (int v = 0; v < C::kAVec; ++v) HQ_STORE_A_PIECE(0, v);
   {
@@ -451,6 +445,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #pragma unroll
     for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(nb1, v);
     ra_valid = nb1 * kBK + a_c * 16 < K;
+  }
+  if constexpr (!BSF) {
+    if (tid < BM) s_xs[tid] = xs_v;
+    if (tid < C::kBN) s_ws[tid] = ws_v;
+  }
+  if (a.bias_kind != kBiasNone) {
+    const float bsc = a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0];
+    if (tid < C::kBN) s_bias[tid] = bias_at(a, min(n0 + tid, a.n - 1), bsc);
   }
   __syncthreads();
   // Two unconditional steps per iteration (LDS buffers and B register sets both
@@ -645,12 +647,28 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
   p.f = p.mb == 1 ? 1 : 2;
   p.kpw = p.mb == 1 ? 4 : (p.mb == 2 ? 2 : 1);  // loads in flight within the 128-VGPR budget
   p.groups = (frag_rows(n) + p.f - 1) / p.f;
+  p.halves = 1;
+#ifndef HQ_SK_NOHALVES
+  // One 16-row activation block and fewer fragments than CUs: each fragment's
+  // two slot halves go to two workgroups (the other half's lanes load zeros),
+  // so every CU streams weight with no cross-workgroup sum.
+  if (p.mb == 1 && p.groups < 256) {
+    p.halves = 2;
+    p.groups *= 2;
+  }
+#endif
   // Split only when one workgroup per group would take its wavefronts through
   // more than one chunk of loads: below that the cross-workgroup step costs
   // more latency than the extra workgroups save.
   p.splits = 1;
   const int nkb = (k + kBK - 1) / kBK;
-  if (nkb > kSkWaves * p.kpw && p.groups < (int)(kSkCounterBytes / 4)) {
+#ifdef HQ_SK_MINWG
+  if (p.groups < (int)(kSkCounterBytes / 4) && nkb >= 4) {
+    while (p.splits < 8 && p.groups * p.splits < HQ_SK_MINWG) p.splits *= 2;
+    while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;
+  }
+#endif
+  if (p.splits == 1 && nkb > kSkWaves * p.kpw && p.groups < (int)(kSkCounterBytes / 4)) {
     while (p.splits < 8 && p.groups * p.splits < 256) p.splits *= 2;
     while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;  // at least 2 K blocks per workgroup
   }
@@ -659,7 +677,7 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
 }
 
 template <int XF, int WF, int MB, int F, int KPW, bool STRICT>
-__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, int splits, int chunk,
+__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, int splits, int chunk, int halves,
                                                                   uint32_t* counters, float* partials) {
   __shared__ __attribute__((aligned(16))) float red[kSkWaves][64][4];
   __shared__ int s_last;
@@ -668,11 +686,16 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fg = blockIdx.x / splits, split = blockIdx.x % splits;
   const int g = split * waves + wave;  // wavefront index within the fragment group
+  // with halves == 2 (F == 1): this group is slot half `half` of fragment fg / 2;
+  // lanes of the other half load zeros and store nothing
+  const int half = fg % halves;
+  const bool my_slots = halves == 1 || ((lane & 15) >> 3) == half;
+  const bool my_rows = halves == 1 || ((lane >> 4) >> 1) == half;
   const int K = a.k, nkb = (K + kBK - 1) / kBK;
   const int nfrag = frag_rows(a.n);
   // B: the group's fragment rows (F * nkb * 2048 contiguous bytes); fragments
   // past the padded N and blocks past nkb read zero.
-  const int nb0 = fg * F;
+  const int nb0 = fg / halves * F;
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.wq_pre + (size_t)nb0 * nkb * kFragBytes), (short)0, min(F, nfrag - nb0) * nkb * kFragBytes,
       kRsrcFlags);
@@ -682,25 +705,22 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
       __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, a.m * K, kRsrcFlags);
   const int xr = lane & 15, xc = 32 * (lane >> 4);
 
-  // Epilogue scales of every slice this lane may store, fetched before the K
-  // loop so their latency hides behind it (indices clamped; masked on store).
-  // Slice (f, i): row 16*i + l%16, columns col0(f) .. +3 (see the epilogue).
-  float xs_r[MB], ws_r[F][4], b_r[F][4];
+  // Epilogue scales of every slice this lane may store (indices clamped;
+  // masked on store). Slice (f, i): row 16*i + l%16, columns col0(f) .. +3 (see
+  // the epilogue). They are loaded after the first chunk's operand loads are
+  // issued, so no operand load waits for them; a bias is read in the epilogue.
+  float xs_r[MB], ws_r[F][4];
+  auto load_scales = [&]() {
 #pragma unroll
-  for (int i = 0; i < MB; ++i) xs_r[i] = a.x_scale[a.x_scale_per_row ? min(i * 16 + xr, a.m - 1) : 0];
+    for (int i = 0; i < MB; ++i) xs_r[i] = a.x_scale[a.x_scale_per_row ? min(i * 16 + xr, a.m - 1) : 0];
 #pragma unroll
-  for (int f = 0; f < F; ++f) {
-    const int nb = nb0 + f;
-    const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
+    for (int f = 0; f < F; ++f) {
+      const int nb = nb0 + f;
+      const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ws_r[f][e] = a.w_scale[a.w_scale_per_col ? min(col0 + e, a.n - 1) : 0];
-      b_r[f][e] = a.bias_kind == kBiasNone
-                      ? 0.0f
-                      : bias_at(a, min(col0 + e, a.n - 1), a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0]);
+      for (int e = 0; e < 4; ++e) ws_r[f][e] = a.w_scale[a.w_scale_per_col ? min(col0 + e, a.n - 1) : 0];
     }
-  }
-  const float r_out = a.out_scale ? 1.0f / a.out_scale[0] : 0.0f;
+  };
 
   v4f acc[F][MB];
 #pragma unroll
@@ -715,7 +735,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
     for (int j = 0; j < KPW; ++j) {
       const int kb = (c * KPW + j) * kSkWaves + g;
       // a block past nkb would land in the next fragment's row: send it past the extent
-      const int bvo = kb < nkb ? lane * 16 : kBadOffset;
+      const int bvo = kb < nkb && my_slots ? lane * 16 : kBadOffset;
 #pragma unroll
       for (int f = 0; f < F; ++f)
 #pragma unroll
@@ -731,6 +751,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
           fx[j][i][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(x_rsrc, vo, 0, 0));
         }
     }
+    if (!STRICT && c == 0) load_scales();
     // keep every load of the chunk ahead of its first MFMA
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -765,6 +786,10 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
     }
   }
 
+  // (the strict form's float16 conversions leave no registers for the scales
+  // during the loop)
+  if (STRICT) load_scales();
+
   // Epilogue of slice (f, i): lane l holds activation row 16*i + l%16 and weight
   // slots 4*(l/16) .. +3 of fragment nb0 + f, i.e. 4 consecutive output columns.
   // Scale, round to bf16, one 8-byte store.
@@ -772,18 +797,20 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
     const int nb = nb0 + f;
     const int row = i * 16 + xr;
     const int col0 = 32 * (nb >> 1) + 8 * (lane >> 4) + 4 * (nb & 1);
-    if (row >= a.m || col0 >= a.n) return;
+    if (row >= a.m || col0 >= a.n || !my_rows) return;
     const float xsc = xs_r[i];
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = t[e] * xsc * ws_r[f][e];
     if (a.bias_kind != kBiasNone) {
+      const float bsc = a.bias_kind == kBiasBF16 ? 0.0f : a.bias_scale[0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += b_r[f][e];
+      for (int e = 0; e < 4; ++e) v[e] += bias_at(a, min(col0 + e, a.n - 1), bsc);
     }
     const size_t off = (size_t)row * a.n + col0;
     const bool full = (a.n & 3) == 0;
     if (a.out_scale) {
+      const float r_out = 1.0f / a.out_scale[0];
       store_fp8_out<4>(static_cast<uint8_t*>(a.out) + off, v, r_out, a.out_fmt, full, a.n - col0);
       return;
     }
@@ -884,14 +911,15 @@ static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t works
                         ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSkCounterBytes)
                         : nullptr;
   const dim3 grid(p.groups * p.splits), block(64 * (kSkWaves / p.splits));
+  const int halves = p.halves;
   if (p.mb == 1)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 4, STRICT>), grid, block, 0, st, a, p.splits, chunk, counters,
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 4, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
                        partials);
   else if (p.mb == 2)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 2, 2, STRICT>), grid, block, 0, st, a, p.splits, chunk, counters,
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 2, 2, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
                        partials);
   else if constexpr (!STRICT)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2, 1, STRICT>), grid, block, 0, st, a, p.splits, chunk, counters,
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2, 1, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
                        partials);
   return hipGetLastError();
 }
@@ -913,6 +941,9 @@ static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t works
 enum TileCfg { kTile256, kTile128x256, kTile128, kTile64x128 };
 
 static TileCfg pick_tile(long rows, long n, int experts, bool strict) {
+#ifdef HQ_FORCE_TILE
+  if (!strict && !experts) return (TileCfg)HQ_FORCE_TILE;
+#endif
   struct Cand {
     TileCfg cfg;
     int bm, bn;

@@ -101,8 +101,10 @@ struct GemmArgs {
 // fragments per group, KPW K blocks per wavefront chunk, `groups` fragment
 // groups, each split over `splits` workgroups; workspace_bytes is what the
 // split needs (0 when splits == 1).
+// halves = 2: each group is one half (8 of the 16 slots) of a weight fragment,
+// so a narrow N still gives every CU a group without splitting K.
 struct SkinnyPlan {
-  int mb, f, kpw, groups, splits;
+  int mb, f, kpw, groups, splits, halves;
   size_t workspace_bytes;
 };
 SkinnyPlan skinny_plan(int m, int n, int k);

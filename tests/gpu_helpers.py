@@ -20,6 +20,8 @@ the test, with its margin).
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -167,7 +169,7 @@ MEASURED_SHARE = {k: v / n for k, (v, n) in {
     'full_range (64, 96, 1024) (0, 1)': (14, 6144),
     'full_range (64, 96, 1024) (1, 0)': (14, 6144),
     'full_range (64, 96, 1024) (1, 1)': (10, 6144),
-    'graph decode': (1, 2000),
+    'graph decode': (0, 2000),
     'graph gemm': (4, 3000),
     'layouts dgrad': (0, 4000),
     'layouts wgrad': (0, 4000),
@@ -179,8 +181,8 @@ MEASURED_SHARE = {k: v / n for k, (v, n) in {
     'moe expert 7': (884, 1595392),
     'past_2_31': (8, 6024),
     'ptpc 4096^3': (19414, 16777216),
-    'split (1, 2048, 14336)': (6, 2048),
-    'split (16, 2048, 9216)': (95, 32768),
+    'split (1, 1024, 14336)': (2, 1024),
+    'split (16, 1024, 9216)': (50, 16384),
     'split (32, 2048, 7168)': (216, 65536),
     'split (33, 96, 2304)': (10, 3168),
     'split (64, 520, 4096)': (98, 33280),
@@ -193,9 +195,16 @@ MEASURED_SHARE = {k: v / n for k, (v, n) in {
 
 
 def allowed_share(key, n):
-    """The share of n outputs a check may have outside the method's bound."""
-    measured = MEASURED_SHARE.get(key, 1.0)
-    return min(1.0, measured * 1.5 + 10.0 / n)
+    """The share of n outputs a check may have outside the method's bound
+    (every FP8-path check needs a measured entry). With HQ_MEASURE_SHARES=1 in
+    the environment no share is enforced (the per-element bound still is) and
+    each labelled check prints its share, for re-measuring after a kernel
+    change."""
+    if os.environ.get("HQ_MEASURE_SHARES") == "1":
+        return 1.0
+    if key not in MEASURED_SHARE:
+        raise KeyError(f"no measured strict-bound share for the check {key!r}; measure it and add it")
+    return min(1.0, MEASURED_SHARE[key] * 1.5 + 10.0 / n)
 
 
 def _scale_vec(s, count):

@@ -252,12 +252,15 @@ def test_gemm_workspace_bytes(hq):
     """Split plan of the weight-streaming kernel: a fixed 1 KB region of 4-byte
     column-group counters + 1 KB of fp32 partials per (group, split, fragment,
     16-row block)."""
-    # m <= 16 splits only past 64 K blocks (16 wavefronts x 4 blocks per chunk)
+    # m <= 16: each fragment's two slot halves are groups of their own, so
+    # n = 2048 (128 fragments) already gives 256 groups and never splits
     assert hq.hq_gemm_workspace_bytes(1, 2048, 7168) == 0
-    assert hq.hq_gemm_workspace_bytes(16, 2048, 8192) == 0
-    # m=1, n=2048, k=14336: 128 one-fragment groups, split 2 -> 256 workgroups
-    assert hq.hq_gemm_workspace_bytes(1, 2048, 14336) == 1024 + 128 * 2 * 1024
-    assert hq.hq_gemm_workspace_bytes(16, 2048, 8208) == 1024 + 128 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(1, 2048, 14336) == 0
+    # narrower n splits past 64 K blocks (16 wavefronts x 4 blocks per chunk):
+    # n=1024, k=14336: 64 fragments, 128 half groups, split 2 -> 256 workgroups
+    assert hq.hq_gemm_workspace_bytes(16, 1024, 8192) == 0
+    assert hq.hq_gemm_workspace_bytes(1, 1024, 14336) == 1024 + 128 * 2 * 1024
+    assert hq.hq_gemm_workspace_bytes(16, 1024, 8208) == 1024 + 128 * 2 * 1024
     # m=32 (past 32 K blocks): 64 two-fragment groups of 2 row blocks, split 4
     assert hq.hq_gemm_workspace_bytes(32, 2048, 7168) == 1024 + 64 * 4 * 2 * 2 * 1024
     assert hq.hq_gemm_workspace_bytes(32, 2048, 4096) == 0
@@ -573,7 +576,7 @@ def test_strict_and_noalloc_valid_calls_reach_device_gate(hq):
     assert _gemm_strict(hq) == D
     assert _grouped_strict(hq) == D
     assert _gemm_noalloc(hq) == D
-    assert _gemm_noalloc(hq, m=16, xsc=16, n=2048, k=14336) == D  # a split decode plan
+    assert _gemm_noalloc(hq, m=16, xsc=16, n=1024, k=14336) == D  # a split decode plan
 
 
 def test_workspace_status_validation(hq):

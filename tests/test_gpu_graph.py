@@ -40,7 +40,7 @@ def test_quantize_and_gemm_graph_replays(hq):
     cb, c = _bf16(rng, (1024, 512))
     # decode GEMM with a split-K workspace
     db, d = _bf16(rng, (8, 14336))
-    vb, v = _bf16(rng, (2048, 14336), 0.02)
+    vb, v = _bf16(rng, (1024, 14336), 0.02)
     # delayed scaling
     rb, rx = _bf16(rng, (256, 1024))
 
@@ -64,9 +64,9 @@ def test_quantize_and_gemm_graph_replays(hq):
     # decode operands are quantized once, eagerly; the graph holds the decode GEMM
     qd, sd, _ = hq.hq_quantize_fp8(d, E4M3, Q.PER_TOKEN)
     vpre, sv, _, qv = hq.hq_quantize_fp8_preshuffled(v, E4M3, row_major=True)
-    ws_g = torch.zeros(int(lib.hq_gemm_workspace_bytes(8, 2048, 14336)), dtype=torch.uint8, device=dev)
+    ws_g = torch.zeros(int(lib.hq_gemm_workspace_bytes(8, 1024, 14336)), dtype=torch.uint8, device=dev)
     assert ws_g.numel() > 0, "the decode shape is meant to run split"
-    od = torch.empty((8, 2048), dtype=torch.bfloat16, device=dev)
+    od = torch.empty((8, 1024), dtype=torch.bfloat16, device=dev)
     ring = hq.Ring(16)
     qr = torch.empty((256, 1024), dtype=torch.uint8, device=dev)
     sr = torch.empty(1, dtype=torch.float32, device=dev)
@@ -79,7 +79,7 @@ def test_quantize_and_gemm_graph_replays(hq):
         hq.hq_gemm_a8w8(qx, E4M3, wpre, E4M3, sx, sw, 768, out=out)
         hq.hq_quantize_fp8(t, E4M3, Q.PER_TENSOR, q=qt, scale_out=st_, amax_out=at_, workspace=ws_t)
         hq.hq_quantize_fp8(c, E4M3, Q.PER_CHANNEL, q=qc, scale_out=sc, amax_out=ac, workspace=ws_c)
-        hq.hq_gemm_a8w8(qd, E4M3, vpre, E4M3, sd, sv, 2048, out=od, workspace=ws_g)
+        hq.hq_gemm_a8w8(qd, E4M3, vpre, E4M3, sd, sv, 1024, out=od, workspace=ws_g)
         hq.hq_quantize_fp8(rx, E4M3, Q.PER_TENSOR, ring=ring, ring_idx=3, q=qr, scale_out=sr, amax_out=ar,
                            workspace=ws_t)
 
@@ -111,7 +111,7 @@ def test_quantize_and_gemm_graph_replays(hq):
     qd_h, sd_h, qv_h, sv_h = host(qd), host(sd), host(qv), host(sv)
     prng = np.random.default_rng(5)
     pairs = np.stack([prng.integers(0, 640, 3000), prng.integers(0, 768, 3000)], axis=1)
-    dpairs = np.stack([prng.integers(0, 8, 2000), prng.integers(0, 2048, 2000)], axis=1)
+    dpairs = np.stack([prng.integers(0, 8, 2000), prng.integers(0, 1024, 2000)], axis=1)
 
     first = None
     for rep in range(REPLAYS):
@@ -143,6 +143,6 @@ def test_quantize_and_gemm_graph_replays(hq):
             assert np.array_equal(ob, first[0]) and np.array_equal(odb, first[1])
     # the workspaces are left ready for eager calls after the replays
     q2, s2, _ = hq.hq_quantize_fp8(t, E4M3, Q.PER_TENSOR, workspace=ws_t)
-    o2 = hq.hq_gemm_a8w8(qd, E4M3, vpre, E4M3, sd, sv, 2048, workspace=ws_g)
+    o2 = hq.hq_gemm_a8w8(qd, E4M3, vpre, E4M3, sd, sv, 1024, workspace=ws_g)
     torch.cuda.synchronize()
     assert np.array_equal(host(q2), qt_ref) and np.array_equal(host(o2), first[1])
