@@ -65,11 +65,13 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint4* __restri
   // a chunk's scales and maxima, gathered per wavefront for coalesced stores
   __shared__ float sb[4][2][CB];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int W = gridDim.x * 4;
+  // row indices step in 64 bits: rows up to 2^31 - 1 would overflow row + W
+  const int64_t W = (int64_t)gridDim.x * 4;
   const int cpr = (vpr + 64 * U - 1) / (64 * U);  // chunks per row
-  int row = blockIdx.x * 4 + (threadIdx.x >> 6), c = 0;
+  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int c = 0;
   if (row >= rows) return;
-  auto load = [&](uint4 (&v)[U], int r, int ch) {
+  auto load = [&](uint4 (&v)[U], int64_t r, int ch) {
     const uint4* xr = x + (size_t)r * vpr;
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = xr[min(lane + 64 * (ch * U + u), vpr - 1)];
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint4* __restri
   uint4 cur[U];
   load(cur, row, 0);
   while (row < rows) {
-    int nrow = row, nc = c + 1;
+    int64_t nrow = row;
+    int nc = c + 1;
     if (nc == cpr) {
       nc = 0;
       nrow += W;
@@ -141,7 +144,7 @@ hipError_t launch_quant_blocks(const void* x, int xt, int rows, int cols, int fm
   const int nb = (cols + bs - 1) / bs;
   const SrSeed sd{(uint32_t)seed, (uint32_t)(seed >> 32)};
   // 16 wavefronts per CU (measured best for [4096, 4096]: one row each)
-  const dim3 grid(min((rows + 3) / 4, kNumCUs * 4)), block(256);
+  const dim3 grid((int)std::min<int64_t>(((int64_t)rows + 3) / 4, kNumCUs * 4)), block(256);
   const uint4* xv = static_cast<const uint4*>(x);
 #define HQ_BLK(XT_, FMT_, BS_, SR_)                                                                            \
   hipLaunchKernelGGL((quant_blocks_kernel<XT_, FMT_, BS_, SR_>), grid, block, 0, st, xv, q, scale, amax, rows, vpr, \
@@ -393,10 +396,10 @@ __global__ __launch_bounds__(bsg::threads<NJ>()) __attribute__((amdgpu_waves_per
       const int col = n0 + wcol + 16 * j;
       uint16_t* o = a.out + (size_t)row * a.n + col;
       if (vec && col + 3 < a.n) {
-        uint2 pk;
-        pk.x = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-        pk.y = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(o) = pk;
+        // non-temporal: the output is written once and never read here
+        const hq_u2v pk = {f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16),
+                           f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16)};
+        __builtin_nontemporal_store(pk, reinterpret_cast<hq_u2v*>(o));
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)

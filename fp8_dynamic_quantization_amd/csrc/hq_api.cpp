@@ -38,6 +38,9 @@ hq_status ok() {
 }
 
 constexpr int64_t kI32Max = 2147483647;
+// Largest row or column count a launch accepts: grid sizes and tile bounds
+// round a dimension up to a multiple of at most 1024 in 32-bit arithmetic.
+constexpr int64_t kMaxDim = kI32Max - 1023;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -177,9 +180,11 @@ static hq_status quantize_impl(const void* x, int xt, int64_t rows, int64_t cols
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
   if (gran != HQ_PER_TENSOR && gran != HQ_PER_TOKEN && gran != HQ_PER_CHANNEL)
     return fail(HQ_ERR_INVALID_ARGUMENT, "unknown granularity %d", gran);
-  if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
-  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if (rows < 0 || rows > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1024], got %lld", (long long)rows);
+  if (cols < 16 || cols > kMaxDim || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16, at most 2^31 - 1024, got %lld",
+                (long long)cols);
   if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
   if (ring) {
     if (gran != HQ_PER_TENSOR) return fail(HQ_ERR_INVALID_ARGUMENT, "a delayed-scaling ring requires HQ_PER_TENSOR");
@@ -236,9 +241,11 @@ static hq_status layouts_impl(const void* x, int xt, int64_t rows, int64_t cols,
                               uint64_t seed, hipStream_t stream, const char* name) {
   if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
-  if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
-  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if (rows < 0 || rows > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1024], got %lld", (long long)rows);
+  if (cols < 16 || cols > kMaxDim || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16, at most 2^31 - 1024, got %lld",
+                (long long)cols);
   if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
   if (scale_in && ring) return fail(HQ_ERR_INVALID_ARGUMENT, "give scale_in or ring, not both");
   if (ring) {
@@ -322,9 +329,11 @@ hq_status hq_quantize_fp8_blockwise(const void* x, int xt, int64_t rows, int64_t
   if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
     return fail(HQ_ERR_INVALID_ARGUMENT, "block_size must be 16, 32, 64 or 128, got %d", block_size);
   if (stochastic && fmt != HQ_E5M2) return fail(HQ_ERR_INVALID_ARGUMENT, "stochastic rounding produces E5M2");
-  if (rows < 0 || rows > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31), got %lld", (long long)rows);
-  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if (rows < 0 || rows > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1024], got %lld", (long long)rows);
+  if (cols < 16 || cols > kMaxDim || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16, at most 2^31 - 1024, got %lld",
+                (long long)cols);
   if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
   if (rows == 0) return ok();
   if (!x || !q || !scales) return fail(HQ_ERR_INVALID_ARGUMENT, "x, q and scales must be non-NULL");
@@ -374,10 +383,11 @@ hq_status hq_quantize_fp8_preshuffled(const void* x, int xt, int64_t rows, int64
                                       uint8_t* q_pre, float* scale_out, float* amax_out, hipStream_t stream) {
   if (xt != HQ_F32 && xt != HQ_BF16) return fail(HQ_ERR_INVALID_ARGUMENT, "xt must be HQ_F32 or HQ_BF16, got %d", xt);
   if (!valid_fmt(fmt)) return fail(HQ_ERR_INVALID_ARGUMENT, "fmt must be HQ_E4M3 or HQ_E5M2, got %d", fmt);
-  if (rows < 0 || rows > kI32Max - 31)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 32), got %lld", (long long)rows);
-  if (cols < 16 || cols > kI32Max || cols % 16 != 0)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16 below 2^31, got %lld", (long long)cols);
+  if (rows < 0 || rows > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1024], got %lld", (long long)rows);
+  if (cols < 16 || cols > kMaxDim || cols % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 16, at most 2^31 - 1024, got %lld",
+                (long long)cols);
   if ((double)rows * (double)cols > 1099511627776.0) return fail(HQ_ERR_INVALID_ARGUMENT, "rows * cols exceeds 2^40");
   if (rows == 0) return ok();
   if (!x || !q_pre || !scale_out) return fail(HQ_ERR_INVALID_ARGUMENT, "x, q_pre and scale_out must be non-NULL");
@@ -403,9 +413,10 @@ hq_status hq_quantize_fp8_preshuffled(const void* x, int xt, int64_t rows, int64
 }
 
 hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k, uint8_t* wq_pre, hipStream_t stream) {
-  if (n < 0 || n > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31), got %lld", (long long)n);
-  if (k < 16 || k > kI32Max || k % 16 != 0)
-    return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16 below 2^31, got %lld", (long long)k);
+  if (n < 0 || n > kMaxDim) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31 - 1024], got %lld", (long long)n);
+  if (k < 16 || k > kMaxDim || k % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16, at most 2^31 - 1024, got %lld",
+                (long long)k);
   if ((double)padded_bytes(n, k) / 16.0 / 256.0 > (double)kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "weight too large");
   if (n == 0) return ok();
   if (!wq || !wq_pre) return fail(HQ_ERR_INVALID_ARGUMENT, "wq and wq_pre must be non-NULL");
@@ -449,8 +460,8 @@ static hq_status epilogue_args(const hq_epilogue* ep, const void** bias, int* bi
 
 static hq_status check_gemm_common(int xf, int wf, int64_t m, int64_t n, int64_t k) {
   if (!valid_fmt(xf) || !valid_fmt(wf)) return fail(HQ_ERR_INVALID_ARGUMENT, "xf and wf must be HQ_E4M3 or HQ_E5M2");
-  if (m < 0 || m > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "m must be in [0, 2^31), got %lld", (long long)m);
-  if (n < 0 || n > kI32Max) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31), got %lld", (long long)n);
+  if (m < 0 || m > kMaxDim) return fail(HQ_ERR_INVALID_ARGUMENT, "m must be in [0, 2^31 - 1024], got %lld", (long long)m);
+  if (n < 0 || n > kMaxDim) return fail(HQ_ERR_INVALID_ARGUMENT, "n must be in [0, 2^31 - 1024], got %lld", (long long)n);
   if (k < 16 || k >= (1 << 24) || k % 16 != 0)
     return fail(HQ_ERR_INVALID_ARGUMENT, "k must be a positive multiple of 16 below 2^24, got %lld", (long long)k);
   if ((double)((m + 127) / 128) * (double)((n + 127) / 128) > 1.0e9)
@@ -459,7 +470,7 @@ static hq_status check_gemm_common(int xf, int wf, int64_t m, int64_t n, int64_t
 }
 
 int64_t hq_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m < 0 || n < 0 || k < 16 || k % 16 != 0 || k >= (int64_t(1) << 24) || m > INT32_MAX || n > INT32_MAX) return -1;
+  if (m < 0 || n < 0 || k < 16 || k % 16 != 0 || k >= (int64_t(1) << 24) || m > kMaxDim || n > kMaxDim) return -1;
   if (m == 0 || n == 0) return 0;
   return (int64_t)hq::gemm_workspace_bytes((int)m, (int)n, (int)k);
 }

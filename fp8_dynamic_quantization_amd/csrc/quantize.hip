@@ -113,7 +113,9 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
 // loads of its next row before it reduces, casts and stores the current one, so
 // code stores of one row overlap the input reads of the next.
 constexpr int kRowsPerBlock = 4;
-constexpr int kRowWavesPerCU = 12;  // measured best for 4096 x 4096 bf16 (9.2 vs 9.6 us at 16)
+// Measured on 4096 x 4096 bf16: 9.6 us at 12 wavefronts per CU, 10.0 at 8 (two
+// rows each, no tail) or 16, 11.6 at 4; non-temporal loads 10.0.
+constexpr int kRowWavesPerCU = 12;
 
 template <int XT, int FMT, int NV, bool SR>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
@@ -121,8 +123,9 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
     float* __restrict__ amax_out, int rows, int vpr, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   const int lane = threadIdx.x & 63;
-  const int W = gridDim.x * kRowsPerBlock;
-  int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  // row indices step in 64 bits: rows up to 2^31 - 1 would overflow row + W
+  const int64_t W = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wavefronts only
   // lanes past the row end reload the row's last vector (a real element, so it
   // cannot change the max) and skip the store
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
 #pragma unroll
   for (int j = 0; j < NV; ++j) cur[j] = x[(size_t)row * vpr + min(lane + 64 * j, vpr - 1)];
   for (; row < rows; row += W) {
-    const int nrow = row + W;
+    const int64_t nrow = row + W;
     uint4 nxt[NV];
     if (nrow < rows) {
 #pragma unroll
@@ -177,7 +180,8 @@ static hipError_t launch_rows_t(const void* x, int rows, int vpr, uint8_t* q, fl
                                 float* amax, SrSeed sd, hipStream_t st) {
   const uint4* xv = static_cast<const uint4*>(x);
   const dim3 grid(rows);
-  const int wblocks = min((rows + kRowsPerBlock - 1) / kRowsPerBlock, kNumCUs * kRowWavesPerCU / kRowsPerBlock);
+  const int wblocks = (int)std::min<int64_t>(((int64_t)rows + kRowsPerBlock - 1) / kRowsPerBlock,
+                                             kNumCUs * kRowWavesPerCU / kRowsPerBlock);
   const dim3 wgrid(wblocks), wblock(64 * kRowsPerBlock);
   if (vpr <= 64) {
     hipLaunchKernelGGL((quant_rows_wave_kernel<XT, FMT, 1, SR>), wgrid, wblock, 0, st, xv, q, scale, amax, rows, vpr, sd);

@@ -131,7 +131,7 @@ size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
  *              0.5 s (other work holding the device) gives up, the call's
  *              affected scales come out NaN, and a sticky bit in the workspace
  *              records it (hq_quantize_workspace_status).
- * Requires cols % 16 == 0 (16-byte vector rows), 1 <= rows, cols < 2^31,
+ * Requires cols % 16 == 0 (16-byte vector rows), 1 <= rows, cols <= 2^31 - 1024,
  * rows * cols < 2^40. rows == 0 returns HQ_OK without a launch. Outputs must not
  * overlap inputs. */
 hq_status hq_quantize_fp8(const void* x, int xt, int64_t rows, int64_t cols,
@@ -200,7 +200,8 @@ hq_status hq_quantize_fp8_stochastic(const void* x, int xt, int64_t rows, int64_
  * cols) bytes for the ring and dynamic forms, under the same zero-fill-once
  * rule as hq_quantize_fp8 (may be NULL with scale_in).
  * Requires cols % 16 == 0, and rows % 16 == 0 when q_t or q_t_pre is asked
- * for; 16-byte aligned x and code buffers; no output may overlap another
+ * for; rows, cols <= 2^31 - 1024, rows * cols < 2^40; 16-byte aligned x and
+ * code buffers; no output may overlap another
  * buffer. rows == 0 returns HQ_OK without a launch. */
 hq_status hq_quantize_fp8_layouts(const void* x, int xt, int64_t rows, int64_t cols, int fmt,
                                   const float* scale_in, const hq_ring* ring,
@@ -236,7 +237,7 @@ hq_status hq_quantize_fp8_layouts_stochastic(const void* x, int xt, int64_t rows
  *   scales    device, float32 [rows, ceil(cols / block_size)] row-major
  *   amax_out  device, optional, float32 of the same shape: the block amax
  * Requires block_size in {16, 32, 64, 128}, cols % 16 == 0, 1 <= rows,
- * cols < 2^31, rows * cols < 2^40; no output may overlap an input. rows == 0
+ * cols <= 2^31 - 1024, rows * cols < 2^40; no output may overlap an input. rows == 0
  * returns HQ_OK without a launch. */
 hq_status hq_quantize_fp8_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int fmt,
                                     int block_size, int stochastic, uint64_t seed,
@@ -315,7 +316,7 @@ hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k,
  *   q          device uint8 [rows, cols] row-major codes, or NULL for none
  *   q_pre      device, hq_preshuffled_bytes(rows, cols) bytes, 16-byte aligned
  *   scale_out  device float32 [rows]; amax_out device float32 [rows] or NULL
- * Requires cols % 16 == 0, rows < 2^31 - 32; no output may overlap another
+ * Requires cols % 16 == 0, rows, cols <= 2^31 - 1024; no output may overlap another
  * buffer. rows == 0 returns HQ_OK without a launch. */
 hq_status hq_quantize_fp8_preshuffled(const void* x, int xt, int64_t rows, int64_t cols, int fmt,
                                       uint8_t* q, uint8_t* q_pre, float* scale_out, float* amax_out,
@@ -348,7 +349,7 @@ int64_t hq_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *             unsplit, slower but with the same output bits (the order of the
  *             sums depends only on m, n and k).
  *             Calls that share a workspace must not run concurrently.
- * Requires k % 16 == 0, 16 <= k < 2^24, m, n < 2^31. m == 0 or n == 0 returns HQ_OK
+ * Requires k % 16 == 0, 16 <= k < 2^24, m, n <= 2^31 - 1024. m == 0 or n == 0 returns HQ_OK
  * without a launch (aiter PR: an empty out is a no-op). */
 hq_status hq_gemm_a8w8(const uint8_t* xq, int xf, const uint8_t* wq_pre, int wf,
                        const float* x_scale, int64_t x_scale_count,

@@ -596,3 +596,52 @@ def test_workspace_status_valid_call_reaches_device_gate(hq):
     flag = ctypes.c_int32(0)
     assert hq.load().hq_quantize_workspace_status(fake(4), region, ctypes.byref(flag), None) == \
         hq.HQ_ERR_UNSUPPORTED_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# dimension cap: tile rounding of a dimension stays inside 32-bit arithmetic
+# ---------------------------------------------------------------------------
+MAX_DIM = (1 << 31) - 1024
+
+
+def far(i):
+    """Fake device pointers 2^38 bytes apart: no overlap at the largest sizes."""
+    return ctypes.c_void_p(BASE + i * (1 << 38))
+
+
+def test_dimensions_above_the_cap_are_rejected(hq):
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    lib = hq.load()
+    big = MAX_DIM + 16
+    for gran in (hq.HQ_PER_TENSOR, hq.HQ_PER_TOKEN):
+        assert _quant(hq, rows=MAX_DIM + 1, cols=16, gran=gran) == E
+        assert "2^31 - 1024" in hq.hq_last_error()
+        assert _quant(hq, rows=16, cols=big, gran=gran) == E
+    assert _layouts(hq, rows=MAX_DIM + 1, cols=16) == E
+    assert _layouts(hq, rows=16, cols=big) == E
+    assert _blockwise(hq, rows=MAX_DIM + 1, cols=16) == E
+    assert _blockwise(hq, rows=16, cols=big) == E
+    assert _qpre(hq, rows=MAX_DIM + 1, cols=16) == E
+    assert _qpre(hq, rows=16, cols=big) == E
+    assert _gemm(hq, m=MAX_DIM + 1, n=16, k=16, xsc=1, wsc=1) == E
+    assert _gemm(hq, m=16, n=MAX_DIM + 1, k=16, xsc=1, wsc=1) == E
+    assert lib.hq_gemm_workspace_bytes(MAX_DIM + 1, 16, 16) == -1
+    assert lib.hq_gemm_workspace_bytes(16, MAX_DIM + 1, 16) == -1
+    assert lib.hq_preshuffle_weight(fake(0), MAX_DIM + 1, 16, fake(1), None) == E
+    assert lib.hq_preshuffle_weight(fake(0), 16, big, fake(1), None) == E
+
+
+@no_gpu
+def test_dimensions_at_the_cap_reach_the_device_gate(hq):
+    """The largest accepted row counts pass every host check (the call then
+    stops at the device gate on a host without a GPU)."""
+    U = hq.HQ_ERR_UNSUPPORTED_DEVICE
+    lib = hq.load()
+    for gran in (hq.HQ_PER_TENSOR, hq.HQ_PER_TOKEN):
+        assert _quant(hq, x=far(0), q=far(1), s=far(2), a=far(3), ws=far(4), rows=MAX_DIM, cols=16,
+                      gran=gran) == U, hq.hq_last_error()
+    assert _blockwise(hq, x=far(0), q=far(1), s=far(2), a=far(3), rows=MAX_DIM, cols=16) == U, hq.hq_last_error()
+    assert _qpre(hq, x=far(0), qp=far(1), s=far(2), rows=MAX_DIM, cols=16) == U, hq.hq_last_error()
+    assert lib.hq_gemm_workspace_bytes(MAX_DIM, 16, 16) >= 0
+    assert _gemm(hq, xq=far(0), wq=far(1), xs=far(2), xsc=1, ws=far(3), wsc=1, out=far(4), m=MAX_DIM, n=16,
+                 k=16) == U, hq.hq_last_error()
