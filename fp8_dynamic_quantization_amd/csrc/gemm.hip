@@ -480,7 +480,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // once and never read by the kernel, and streaming it past the L2 keeps the
   // operand lines other tiles still read there and leaves no dirty output to
   // write back when the kernel ends (4096^3: 66 -> 58-60 us; MoE 33 -> 28 us).
+  // In the 256 x 256 tile (64 columns per wavefront) a 16-row block's two
+  // fragment pairs hold whole 128-byte output lines (bf16, N % 64 == 0), but
+  // each store instruction would cover only half of 16 lines, and streamed
+  // half lines reach HBM as extra write traffic (1.33x the output at 4096^3). Lanes l and l ^ 8 (DPP
+  // row_ror:8 within each 16-lane row) swap one 16-byte piece first: lanes of
+  // rows 0-7 keep pair 0 of their row and take pair 0 of row r + 8, lanes of
+  // rows 8-15 keep pair 1 of their row and take pair 1 of row r - 8, so each
+  // of the two stores writes 8 complete lines (no partial-line writes to HBM).
+  constexpr int kRowRor8 = 0x128;
   const bool vec_ok = (a.n & 7) == 0;
+  const bool lines_ok = C::kIN == 4 && WM == 2 && !BSF && (a.n & 63) == 0 && !a.out_scale && n0 + wave * TN + TN <= a.n;
   const float r_out = a.out_scale ? 1.0f / a.out_scale[0] : 0.0f;
   const int ccol = 8 * (lane >> 4);
   float wsc[C::kIN / 2][8];
@@ -491,8 +501,44 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #pragma unroll
   for (int i = 0; i < C::kIM; ++i) {
     const int row = m0 + wrow * C::kWR + i * 16 + (lane & 15);
-    if (row >= row_end) continue;
     const float xsc = BSF ? 1.0f : s_xs[wrow * C::kWR + i * 16 + (lane & 15)];
+    if constexpr (C::kIN == 4 && WM == 2 && !BSF) {
+      if (lines_ok && m0 + wrow * C::kWR + i * 16 + 16 <= row_end) {  // wavefront-uniform
+        uint32_t w[2][4];
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+          const v4f p0 = acc[i][2 * jp], p1 = acc[i][2 * jp + 1];
+          float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * wsc[jp][e];
+          if (a.bias_kind != kBiasNone) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += s_bias[wave * TN + 32 * jp + ccol + e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f2v pr = {v[2 * e], v[2 * e + 1]};
+            w[jp][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
+          }
+        }
+        const bool lo = (lane & 15) < 8;
+        uint32_t got[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          got[e] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(lo ? w[1][e] : w[0][e]), kRowRor8, 0xF, 0xF, false);
+        // store 0: rows 0-7 of the block; store 1: rows 8-15
+        const int r0 = m0 + wrow * C::kWR + i * 16 + (lane & 7);
+        const int col = n0 + wave * TN + (lo ? 0 : 32) + ccol;
+        uint16_t* d0 = static_cast<uint16_t*>(a.out) + (size_t)r0 * a.n + col;
+        uint16_t* d1 = d0 + (size_t)8 * a.n;
+        const uint32_t* s0 = lo ? w[0] : got;
+        const uint32_t* s1 = lo ? got : w[1];
+        __builtin_nontemporal_store(hq_u4v{s0[0], s0[1], s0[2], s0[3]}, reinterpret_cast<hq_u4v*>(d0));
+        __builtin_nontemporal_store(hq_u4v{s1[0], s1[1], s1[2], s1[3]}, reinterpret_cast<hq_u4v*>(d1));
+        continue;
+      }
+    }
+    if (row >= row_end) continue;
 #pragma unroll
     for (int jp = 0; jp < C::kIN / 2; ++jp) {
       const int col0 = n0 + wave * TN + 32 * jp + ccol;

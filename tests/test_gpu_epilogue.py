@@ -250,3 +250,27 @@ def test_grouped_plain_epilogue_equals_hq_grouped_gemm_a8w8(hq):
     b = hq.hq_grouped_gemm_a8w8_epilogue(xq, fp8.E4M3, pre, fp8.E4M3, xs, ws, offsets, len(counts), n)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("bias_kind", ["none", "bf16"])
+def test_full_line_stores_every_element(hq, bias_kind):
+    """The 256 x 256 tile writes whole 128-byte output lines (a lane swap
+    between rows r and r + 8 of each 16-row block) when N % 64 == 0 and the
+    block's 16 rows all exist; M = 3601 ends in a block with one valid row
+    (per-lane stores), N = 3648 leaves three of the last tile's four wavefront
+    columns empty. Every element is compared with the oracle's epilogue on
+    exact accumulators."""
+    m, n, k = 3601, 3648, 400
+    rng = np.random.default_rng(zlib.crc32(repr(("full lines", bias_kind)).encode()))
+    xq = narrow_codes(rng, (m, k), fp8.E4M3)
+    wq = narrow_codes(rng, (n, k), fp8.E4M3)
+    xs = rng.uniform(1e-3, 2.0, m).astype(np.float32)
+    ws = rng.uniform(1e-3, 2.0, n).astype(np.float32)
+    got, bvals = _run(hq, xq, fp8.E4M3, wq, fp8.E4M3, xs, ws, bias_kind, "bf16", rng, 1.0)
+    acc = fp8.decode(xq, fp8.E4M3) @ fp8.decode(wq, fp8.E4M3).T
+    acc32 = acc.astype(np.float32)
+    assert np.array_equal(acc32.astype(np.float64), acc)  # exact in float32
+    want = G.epilogue_f32(acc32, xs[:, None], ws[None, :],
+                          None if bvals is None else bvals[None, :].astype(np.float32), None, None)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} differ; first at {tuple(bad[0])}: got {got[tuple(bad[0])]:#x}"

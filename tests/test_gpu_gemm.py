@@ -97,6 +97,7 @@ def _edge_pairs(rng, m, n, count):
 # N and K): 256 x 256 (eight wavefronts), 128 x 256, 128 x 128 and
 # 64 x 128 (the small test shapes above all take 64 x 128 as well).
 @pytest.mark.parametrize("shape", [(3600, 3700, 400), (3841, 3330, 1024),   # 256 x 256
+                                   (3601, 3648, 400),                       # 256 x 256, whole-line stores
                                    (2000, 4000, 272),                       # 128 x 256
                                    (4000, 1000, 272),                       # 128 x 128
                                    (1000, 1000, 400)])                      # 64 x 128
