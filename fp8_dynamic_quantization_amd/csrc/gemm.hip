@@ -498,6 +498,51 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   for (int jp = 0; jp < C::kIN / 2; ++jp)
 #pragma unroll
     for (int e = 0; e < 8; ++e) wsc[jp][e] = BSF ? 1.0f : s_ws[wave * TN + 32 * jp + ccol + e];
+  // With 32 columns per wavefront (kIN == 2) a line spans two wavefronts, so
+  // the bf16 tile goes through LDS: the K loop ended on a barrier, and its two
+  // A stages (2 x BM x 128 bytes) hold the BM x 256-byte output tile exactly.
+  // Each row's 16-byte chunks are stored at chunk ^ (row % 16), so the
+  // wavefronts' writes (16 rows, one chunk column) and the read-back (one row,
+  // 16 chunks) are both free of bank conflicts; each group of 16 lanes then
+  // stores one whole 256-byte row segment.
+  if constexpr (C::kIN == 2 && !BSF) {
+    static_assert(C::kThreads == 256 && BM * 256 <= 2 * C::kABytes, "staged epilogue layout");
+    if (!a.out_scale && (a.n & 63) == 0 && n0 + C::kBN <= a.n) {  // workgroup-uniform
+#pragma unroll
+      for (int i = 0; i < C::kIM; ++i) {
+        const int tr = wrow * C::kWR + i * 16 + (lane & 15);
+        const float xsc = s_xs[tr];
+        const v4f p0 = acc[i][0], p1 = acc[i][1];
+        float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * wsc[0][e];
+        if (a.bias_kind != kBiasNone) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += s_bias[wave * TN + ccol + e];
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f2v pr = {v[2 * e], v[2 * e + 1]};
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf2v));
+        }
+        const int chunk = 4 * wave + (lane >> 4);
+        *reinterpret_cast<uint4*>(lds + tr * 256 + ((chunk ^ (tr & 15)) << 4)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      __syncthreads();
+      const int c = tid & 15;
+#pragma unroll
+      for (int p = 0; p < BM / 16; ++p) {
+        const int tr = p * 16 + (tid >> 4);
+        const uint4 val = *reinterpret_cast<const uint4*>(lds + tr * 256 + ((c ^ (tr & 15)) << 4));
+        if (m0 + tr < row_end) {
+          uint16_t* dst = static_cast<uint16_t*>(a.out) + (size_t)(m0 + tr) * a.n + n0 + 8 * c;
+          __builtin_nontemporal_store(hq_u4v{val.x, val.y, val.z, val.w}, reinterpret_cast<hq_u4v*>(dst));
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < C::kIM; ++i) {
     const int row = m0 + wrow * C::kWR + i * 16 + (lane & 15);

@@ -252,16 +252,21 @@ def test_grouped_plain_epilogue_equals_hq_grouped_gemm_a8w8(hq):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [(3601, 3648, 400),    # 256 x 256
+                                   (2001, 1088, 272),    # 128 x 128
+                                   (1000, 1088, 400)])   # 64 x 128
 @pytest.mark.parametrize("bias_kind", ["none", "bf16"])
-def test_full_line_stores_every_element(hq, bias_kind):
-    """The 256 x 256 tile writes whole 128-byte output lines (a lane swap
-    between rows r and r + 8 of each 16-row block) when N % 64 == 0 and the
-    block's 16 rows all exist; M = 3601 ends in a block with one valid row
-    (per-lane stores), N = 3648 leaves three of the last tile's four wavefront
-    columns empty. Every element is compared with the oracle's epilogue on
-    exact accumulators."""
-    m, n, k = 3601, 3648, 400
-    rng = np.random.default_rng(zlib.crc32(repr(("full lines", bias_kind)).encode()))
+def test_full_line_stores_every_element(hq, shape, bias_kind):
+    """bf16 outputs go out as whole 128-byte lines when N % 64 == 0: the
+    256 x 256 tile swaps pieces between lanes of rows r and r + 8 of each
+    16-row block (blocks with all 16 rows present), the 32-column-per-wavefront
+    tiles stage the tile through LDS (tiles whose columns all exist). M = 3601,
+    2001, 1000 end in a partial row tile; N = 3648 leaves three of the last
+    256-column tile's wavefront columns empty, N = 1088 ends in a half 128-column
+    tile (per-lane stores). Every element is compared with the oracle's
+    epilogue on exact accumulators."""
+    m, n, k = shape
+    rng = np.random.default_rng(zlib.crc32(repr(("full lines", shape, bias_kind)).encode()))
     xq = narrow_codes(rng, (m, k), fp8.E4M3)
     wq = narrow_codes(rng, (n, k), fp8.E4M3)
     xs = rng.uniform(1e-3, 2.0, m).astype(np.float32)

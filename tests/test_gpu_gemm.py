@@ -100,7 +100,9 @@ def _edge_pairs(rng, m, n, count):
                                    (3601, 3648, 400),                       # 256 x 256, whole-line stores
                                    (2000, 4000, 272),                       # 128 x 256
                                    (4000, 1000, 272),                       # 128 x 128
-                                   (1000, 1000, 400)])                      # 64 x 128
+                                   (2001, 1088, 272),                       # 128 x 128, staged stores
+                                   (1000, 1000, 400),                       # 64 x 128
+                                   (1000, 1088, 400)])                      # 64 x 128, staged stores
 @pytest.mark.parametrize("pair", PAIRS)
 def test_gemm_tile_configs_narrow_strict(hq, shape, pair):
     m, n, k = shape
