@@ -658,6 +658,33 @@ def training_linear_timings(torch, hq, lib, copies=12):
     return out
 
 
+def vendor_yardstick(torch):
+    """Context only, not part of the step: the vendor FP8 GEMM behind
+    torch._scaled_mm (E4M3 operands, per-tensor scales of 1, bf16 output) on the
+    GEMM shapes of the bench, graph-timed like this library's kernels over
+    rotating operand and output sets larger than the Infinity Cache."""
+    res = {"what": "torch._scaled_mm, float8_e4m3fn x float8_e4m3fn^T, scalar scales, bf16 out"}
+    for (m, n, k) in [(4096, 4096, 4096), (8192, 2048, 1024), (2048, 4096, 1024), (2048, 1024, 4096),
+                      (4096, 1024, 2048), (8192, 8192, 8192)]:
+        nsets = max(2, min(8, int(600e6 // (m * k + n * k + 2 * m * n))))
+        sets = [(torch.randn(m, k, device="cuda").to(torch.float8_e4m3fn),
+                 torch.randn(n, k, device="cuda").to(torch.float8_e4m3fn),
+                 torch.empty(m, n, dtype=torch.bfloat16, device="cuda")) for _ in range(nsets)]
+        one = torch.ones((), device="cuda")
+
+        def launch(i, h, sets=sets, one=one):
+            a, b, o = sets[i % len(sets)]
+            torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16, out=o)
+        launch(0, None)  # the library's first call sets up state that graph capture does not allow
+        torch.cuda.synchronize()
+        ms = min(time_graph(torch, launch, 2 * nsets) for _ in range(3))
+        res[f"{m}x{n}x{k}"] = {"us": round(ms * 1e3, 2), "tflops": round(2 * m * n * k / ms / 1e9, 1),
+                               "rotating_sets": nsets}
+        log(f"vendor yardstick {m}x{n}x{k}: {res[f'{m}x{n}x{k}']}")
+        del sets
+    return res
+
+
 def _csv_rows(directory, suffix):
     import csv
     import glob
@@ -772,6 +799,9 @@ def main():
     ap.add_argument("--no-other", action="store_true", help="skip the decode / grouped / quantize-variant timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC calibration) and exit")
+    ap.add_argument("--vendor-yardstick", action="store_true",
+                    help="only time torch._scaled_mm (the vendor FP8 GEMM) on this library's GEMM shapes, as "
+                         "context, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (this build has no multi-GPU "
@@ -799,6 +829,10 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         log(f"copy probe: 3 x bitwise_not over {COPY_PROBE_BYTES} bytes")
+        return
+
+    if args.vendor_yardstick:
+        print(json.dumps(vendor_yardstick(torch)))
         return
 
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)

@@ -143,18 +143,24 @@ __device__ __forceinline__ float bias_at(const GemmArgs& a, int col, float bscal
 }
 
 // N (4 or 8) epilogue values to FP8 codes of fl32(v * r_out) (saturating RNE,
-// NaN -> 0x7F), stored as one N-byte write when `full`, else byte by byte up
-// to `left` columns.
+// NaN -> 0x7F), four to a word.
 template <int N>
-__device__ __forceinline__ void store_fp8_out(uint8_t* dst, const float* v, float r_out, int fmt, bool full,
-                                              int left) {
-  uint32_t w[N / 4];
+__device__ __forceinline__ void fp8_out_codes(const float* v, float r_out, int fmt, uint32_t* w) {
 #pragma unroll
   for (int d = 0; d < N / 4; ++d) {
     const float x0 = v[4 * d] * r_out, x1 = v[4 * d + 1] * r_out, x2 = v[4 * d + 2] * r_out, x3 = v[4 * d + 3] * r_out;
     w[d] = fmt == kE4M3 ? cvt4<kE4M3>(x0, x1, x2, x3) : cvt4<kE5M2>(x0, x1, x2, x3);
     w[d] = patch_nan4(w[d], x0, x1, x2, x3);
   }
+}
+
+// The codes of fp8_out_codes stored as one N-byte write when `full`, else byte
+// by byte up to `left` columns.
+template <int N>
+__device__ __forceinline__ void store_fp8_out(uint8_t* dst, const float* v, float r_out, int fmt, bool full,
+                                              int left) {
+  uint32_t w[N / 4];
+  fp8_out_codes<N>(v, r_out, fmt, w);
   if (full) {
     if constexpr (N == 8) __builtin_nontemporal_store(hq_u2v{w[0], w[1]}, reinterpret_cast<hq_u2v*>(dst));
     else __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(dst));
@@ -498,6 +504,51 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   for (int jp = 0; jp < C::kIN / 2; ++jp)
 #pragma unroll
     for (int e = 0; e < 8; ++e) wsc[jp][e] = BSF ? 1.0f : s_ws[wave * TN + 32 * jp + ccol + e];
+  // FP8 output codes of the 256 x 256 tile: the 64 KB code tile fits the two
+  // A stages (free once the K loop has ended on its barrier), so it is staged
+  // there (8-byte pieces, 16-byte chunks at chunk ^ (row % 16)) and stored as
+  // whole row segments, 16 bytes per lane: an 8-byte store per lane would
+  // stream half lines to HBM. (In the smaller tiles the same code pushed the
+  // register count past a workgroup-per-CU boundary.)
+  if constexpr (!BSF && WM == 2) {
+    constexpr int kChunksF = C::kBN / 16;
+    static_assert(BM * C::kBN <= 2 * C::kABytes && (BM * kChunksF) % C::kThreads == 0, "FP8 staging layout");
+    if (a.out_scale && (a.n & 15) == 0 && n0 + C::kBN <= a.n) {  // workgroup-uniform
+#pragma unroll
+      for (int i = 0; i < C::kIM; ++i) {
+        const int tr = wrow * C::kWR + i * 16 + (lane & 15);
+        const float xsc = s_xs[tr];
+#pragma unroll
+        for (int jp = 0; jp < C::kIN / 2; ++jp) {
+          const v4f p0 = acc[i][2 * jp], p1 = acc[i][2 * jp + 1];
+          float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * wsc[jp][e];
+          if (a.bias_kind != kBiasNone) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += s_bias[wave * TN + 32 * jp + ccol + e];
+          }
+          uint32_t w[2];
+          fp8_out_codes<8>(v, r_out, a.out_fmt, w);
+          const int cb = wave * TN + 32 * jp + ccol;  // byte column in the tile row
+          const int pc = (cb >> 4) ^ (tr & (kChunksF - 1));
+          *reinterpret_cast<uint2*>(lds + tr * C::kBN + pc * 16 + (cb & 8)) = make_uint2(w[0], w[1]);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < BM * kChunksF / C::kThreads; ++q) {
+        const int idx = q * C::kThreads + tid;
+        const int tr = idx / kChunksF, c = idx % kChunksF;
+        const uint4 val = *reinterpret_cast<const uint4*>(lds + tr * C::kBN + ((c ^ (tr & (kChunksF - 1))) << 4));
+        if (m0 + tr < row_end) {
+          uint8_t* dst = static_cast<uint8_t*>(a.out) + (size_t)(m0 + tr) * a.n + n0 + 16 * c;
+          __builtin_nontemporal_store(hq_u4v{val.x, val.y, val.z, val.w}, reinterpret_cast<hq_u4v*>(dst));
+        }
+      }
+      return;
+    }
+  }
   // With 32 columns per wavefront (kIN == 2) a line spans two wavefronts, so
   // the bf16 tile goes through LDS: the K loop ended on a barrier, and its two
   // A stages (2 x BM x 128 bytes) hold the BM x 256-byte output tile exactly.

@@ -279,3 +279,28 @@ def test_full_line_stores_every_element(hq, shape, bias_kind):
                           None if bvals is None else bvals[None, :].astype(np.float32), None, None)
     bad = np.argwhere(got != want)
     assert bad.size == 0, f"{len(bad)} differ; first at {tuple(bad[0])}: got {got[tuple(bad[0])]:#x}"
+
+
+@pytest.mark.parametrize("out_kind", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("bias_kind", ["none", "e4m3"])
+def test_fp8_output_staged_every_element(hq, out_kind, bias_kind):
+    """FP8 output codes of the 256 x 256 tile go through LDS and out as whole
+    row segments when N % 16 == 0 and the tile's 256 columns all exist; the
+    last column tile of N = 3648 (64 columns) and the ragged last row tile of
+    M = 3601 take the per-lane stores or the row mask. Every code is compared
+    with the oracle's epilogue on exact accumulators."""
+    m, n, k = 3601, 3648, 400
+    rng = np.random.default_rng(zlib.crc32(repr(("fp8 staged", out_kind, bias_kind)).encode()))
+    xq = narrow_codes(rng, (m, k), fp8.E4M3)
+    wq = narrow_codes(rng, (n, k), fp8.E5M2)
+    xs = rng.uniform(1e-3, 2.0, m).astype(np.float32)
+    ws = rng.uniform(1e-3, 2.0, n).astype(np.float32)
+    out_scale = np.float32(rng.uniform(0.5, 4.0))
+    got, bvals = _run(hq, xq, fp8.E4M3, wq, fp8.E5M2, xs, ws, bias_kind, out_kind, rng, out_scale)
+    acc = fp8.decode(xq, fp8.E4M3) @ fp8.decode(wq, fp8.E5M2).T
+    acc32 = acc.astype(np.float32)
+    assert np.array_equal(acc32.astype(np.float64), acc)  # exact in float32
+    want = G.epilogue_f32(acc32, xs[:, None], ws[None, :],
+                          None if bvals is None else bvals[None, :].astype(np.float32), out_scale, FMT[out_kind])
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} differ; first at {tuple(bad[0])}: got {got[tuple(bad[0])]:#x}"
