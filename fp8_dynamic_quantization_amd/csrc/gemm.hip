@@ -202,17 +202,27 @@ struct BsCfg {
 // take one MFMA per block, whose per-lane E8M0 operand scales are 2^0 for the
 // block's 32-element chunks and 2^-127 for the others: their products are then
 // scaled by 2^-254 and vanish below float32's range.
-template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, int BSZ, bool STRICT = false>
+// KS == 2: split K inside the workgroup. A second group of the tile's
+// wavefronts takes the odd K steps (with A stages of its own in LDS), the
+// first the even ones; at the end the second hands its sums to the first
+// through LDS and the first runs the epilogue. For launches of one tile per CU
+// this puts two wavefronts on each SIMD, so one's loads hide behind the
+// other's MFMAs. Both groups pass the same barriers: K is a multiple of 256.
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, int BSZ, bool STRICT = false, int KS = 1>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m0, int row_end, int n0,
                                           const uint8_t* __restrict__ wq, const float* __restrict__ ws) {
   using C = BsCfg<BM, TN, WM>;
+  static_assert(KS == 1 || (KS == 2 && !KTAIL && BSZ == 0 && !STRICT && WM == 1 && TN == 32), "split-K form");
   constexpr bool BSF = BSZ > 0;
   constexpr int NB = BSF ? kBK / BSZ : 1;  // scale blocks per K step
   static_assert(!BSF || BSZ == 32 || BSZ == 64 || BSZ == 128, "block size");
   static_assert(C::kAVec <= C::kIM && C::kIN <= C::kIM, "slot schedule: at most one A piece and two B halves per slot");
   static_assert(!BSF || BM + C::kBN <= C::kThreads, "block scales: one row or column per thread per step");
   static_assert(!(BSF && STRICT), "the strict form has no block scales");
-  const int tid = threadIdx.x;
+  const int tid_all = threadIdx.x;
+  const int ks = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid_all / C::kThreads);  // K group
+  const int tid = tid_all - ks * C::kThreads;                                        // thread in the group
+  uint8_t* const lds_g = lds + ks * 2 * C::kABytes;                                 // the group's A stages
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // wavefront column
   const int wrow = __builtin_amdgcn_readfirstlane(tid >> 8);        // wavefront row
@@ -262,7 +272,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // Their loads are issued after the first operand loads and written to LDS
   // just before the prologue's barrier, so no operand load waits for them.
   static_assert(BM <= C::kThreads && C::kBN <= C::kThreads, "one epilogue scale of each kind per thread");
-  float* s_xs = reinterpret_cast<float*>(lds + 2 * C::kABytes);
+  float* s_xs = reinterpret_cast<float*>(lds + KS * 2 * C::kABytes);
   float* s_ws = s_xs + BM;
   float* s_bias = s_ws + C::kBN;
 
@@ -313,10 +323,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #define HQ_LOAD_A_PIECE(KB, V) \
   ra[V] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_vo, (int)((uint32_t)((V) * C::kRowStep) * uK + (uint32_t)((KB) * kBK)), 0))
 #define HQ_STORE_A_PIECE(BUF, V)                                          \
-  *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
+  *reinterpret_cast<uint4*>(lds_g + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
       (!KTAIL || ra_valid) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
 #define HQ_STORE_A_PIECE_V(BUF, V, VALID)                                  \
-  *reinterpret_cast<uint4*>(lds + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
+  *reinterpret_cast<uint4*>(lds_g + (BUF) * C::kABytes + a_dst + (V) * C::kRowStep * kBK) = \
       (!KTAIL || (VALID)) ? ra[V] : make_uint4(0u, 0u, 0u, 0u)
 #define HQ_LOAD_B_HALF(KB, FB, H)                                                                 \
   FB[H] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(b_rsrc, ((H) & 1) ? b_vo1 : b_vo0,             \
@@ -349,9 +359,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // inserts stay exact; steps past the end reload the last one.
 #define HQ_STEP(KB, BUF, FBC, FBN)                                                                     \
   do {                                                                                                 \
-    const int nb1_ = min((KB) + 1, nkb - 1);                                                           \
-    const int nb2_ = min((KB) + 2, nkb - 1);                                                           \
-    const uint8_t* cur_ = lds + (BUF) * C::kABytes;                                                    \
+    const int nb1_ = min((KB) + KS, nkb - 1);                                                          \
+    const int nb2_ = min((KB) + 2 * KS, nkb - 1);                                                      \
+    const uint8_t* cur_ = lds_g + (BUF) * C::kABytes;                                                  \
     uint4 lo0_, hi0_, lo1_, hi1_, lo2_, hi2_;                                                          \
     bool st_valid_ = ra_valid;                                                                         \
     bsv_t bs_nx_{};                                                                                    \
@@ -435,10 +445,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   // prologue: A(0) to LDS buffer 0, B(0) to registers, A(1) in flight
   if constexpr (BSF) bsf_store(0, bsf_load(0));
 #pragma unroll
-  for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(0, v);
+  for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(ks, v);
   ra_valid = a_c * 16 < K;
 #pragma unroll
-  for (int h = 0; h < 2 * C::kIN; ++h) HQ_LOAD_B_HALF(0, fb0, h);
+  for (int h = 0; h < 2 * C::kIN; ++h) HQ_LOAD_B_HALF(ks, fb0, h);
   float xs_v = 0.0f, ws_v = 0.0f;
   if constexpr (!BSF) {
     if (tid < BM) xs_v = a.x_scale[a.x_scale_per_row ? min(m0 + tid, row_end - 1) : 0];
@@ -447,7 +457,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
 #pragma unroll
   for (int v = 0; v < C::kAVec; ++v) HQ_STORE_A_PIECE(0, v);
   {
-    const int nb1 = min(1, nkb - 1);
+    const int nb1 = min(ks + KS, nkb - 1);
 #pragma unroll
     for (int v = 0; v < C::kAVec; ++v) HQ_LOAD_A_PIECE(nb1, v);
     ra_valid = nb1 * kBK + a_c * 16 < K;
@@ -463,12 +473,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
   __syncthreads();
   // Two unconditional steps per iteration (LDS buffers and B register sets both
   // alternate); an odd last step follows the loop, so the loop body has no branch.
-  int kb = 0;
-  for (; kb + 2 <= nkb; kb += 2) {
-    HQ_STEP(kb, 0, fb0, fb1);
-    HQ_STEP(kb + 1, 1, fb1, fb0);
+  // The group's steps are ks, ks + KS, ks + 2 KS, ...
+  const int nsteps = nkb / KS;
+  int j = 0;
+  for (; j + 2 <= nsteps; j += 2) {
+    HQ_STEP(ks + KS * j, 0, fb0, fb1);
+    HQ_STEP(ks + KS * (j + 1), 1, fb1, fb0);
   }
-  if (kb < nkb) HQ_STEP(kb, 0, fb0, fb1);
+  if (j < nsteps) HQ_STEP(ks + KS * j, 0, fb0, fb1);
+  if constexpr (KS == 2) {
+    // the last step ended on a barrier: the A stages are free for the sums
+    static_assert(C::kIM * C::kIN * C::kThreads * 16 <= KS * 2 * C::kABytes, "split-K sums fit the A stages");
+    v4f* part = reinterpret_cast<v4f*>(lds);
+    if (ks == 1) {
+#pragma unroll
+      for (int i = 0; i < C::kIM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < C::kIN; ++jn) part[(i * C::kIN + jn) * C::kThreads + tid] = acc[i][jn];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int i = 0; i < C::kIM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < C::kIN; ++jn) acc[i][jn] += part[(i * C::kIN + jn) * C::kThreads + tid];
+    }
+    __syncthreads();
+  }
 #undef HQ_LOAD_A_PIECE
 #undef HQ_STORE_A_PIECE
 #undef HQ_STORE_A_PIECE_V
@@ -561,6 +592,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
     if (!a.out_scale && (a.n & 63) == 0 && n0 + C::kBN <= a.n) {  // workgroup-uniform
 #pragma unroll
       for (int i = 0; i < C::kIM; ++i) {
+        if (ks != 0) break;  // split K: the first group holds the sums
         const int tr = wrow * C::kWR + i * 16 + (lane & 15);
         const float xsc = s_xs[tr];
         const v4f p0 = acc[i][0], p1 = acc[i][1];
@@ -581,10 +613,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
         *reinterpret_cast<uint4*>(lds + tr * 256 + ((chunk ^ (tr & 15)) << 4)) = make_uint4(w[0], w[1], w[2], w[3]);
       }
       __syncthreads();
-      const int c = tid & 15;
+      const int c = tid_all & 15;
 #pragma unroll
-      for (int p = 0; p < BM / 16; ++p) {
-        const int tr = p * 16 + (tid >> 4);
+      for (int p = 0; p < BM * 16 / (KS * C::kThreads); ++p) {
+        const int tr = (p * KS * C::kThreads + tid_all) >> 4;
         const uint4 val = *reinterpret_cast<const uint4*>(lds + tr * 256 + ((c ^ (tr & 15)) << 4));
         if (m0 + tr < row_end) {
           uint16_t* dst = static_cast<uint16_t*>(a.out) + (size_t)(m0 + tr) * a.n + n0 + 8 * c;
@@ -594,6 +626,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* lds, int m
       return;
     }
   }
+  if (KS == 2 && ks != 0) return;  // split K: the first group stores
 #pragma unroll
   for (int i = 0; i < C::kIM; ++i) {
     const int row = m0 + wrow * C::kWR + i * 16 + (lane & 15);
@@ -697,14 +730,15 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   *tn = r / gm;
 }
 
-template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, bool STRICT>
-__global__ __launch_bounds__(256 * WM) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+template <int XF, int WF, int BM, int TN, int WM, bool KTAIL, bool STRICT, int KS = 1>
+__global__ __launch_bounds__(256 * WM * KS) void gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   using C = BsCfg<BM, TN, WM>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes + (KS - 1) * 2 * C::kABytes];
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM;
-  gemm_tile<XF, WF, BM, TN, WM, KTAIL, 0, STRICT>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre, a.w_scale);
+  gemm_tile<XF, WF, BM, TN, WM, KTAIL, 0, STRICT, KS>(a, lds, m0, min(a.m, m0 + BM), tn * C::kBN, a.wq_pre,
+                                                      a.w_scale);
 }
 
 // Block-scaled form (blocks of 128 along K) on the same data path.
@@ -1118,6 +1152,17 @@ template <int XF, int WF, int BM, int TN, int WM, bool STRICT>
 static hipError_t launch_plain(const GemmArgs& a, hipStream_t st) {
   using C = BsCfg<BM, TN, WM>;
   const int tiles_m = (a.m + BM - 1) / BM, tiles_n = (a.n + C::kBN - 1) / C::kBN;
+  if constexpr (BM == 64 && TN == 32 && WM == 1 && !STRICT) {
+    // one 64 x 128 tile per CU or fewer (8 MFMAs per wavefront per K step, too
+    // few to cover a load's latency): split K inside the workgroup (K % 256 ==
+    // 0). Measured on 2048 x 1024 x 4096: 14.2 -> 13.35 us; the 128 x 128 tile
+    // (16 MFMAs per step) got slower with it (4096 x 1024 x 2048: 11.8 -> 12.7).
+    if (a.k % (2 * kBK) == 0 && tiles_m * tiles_n <= kNumCUs) {
+      hipLaunchKernelGGL((gemm_kernel<XF, WF, BM, TN, WM, false, false, 2>), dim3(tiles_m * tiles_n),
+                         dim3(2 * C::kThreads), 0, st, a, tiles_m, tiles_n);
+      return hipGetLastError();
+    }
+  }
   if (a.k % kBK == 0)
     hipLaunchKernelGGL((gemm_kernel<XF, WF, BM, TN, WM, false, STRICT>), dim3(tiles_m * tiles_n), dim3(C::kThreads), 0,
                        st, a, tiles_m, tiles_n);

@@ -61,7 +61,8 @@ def _run(hq, xq, xf, wq, wf, xs, ws, bias_kind, out_kind, rng, out_scale_val):
 
 # (m, n, k): decode path (M <= 64, ragged N), and the 64x128, 128x256 and
 # 256x256 tile configurations
-SHAPES = [(1, 96, 256), (33, 200, 400), (300, 520, 1040), (2000, 4000, 272), (3600, 3700, 400)]
+SHAPES = [(1, 96, 256), (33, 200, 400), (300, 520, 1040), (2000, 4000, 272), (3600, 3700, 400),
+          (1000, 1088, 512)]  # 64 x 128 tiles with K split inside the workgroup
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -254,7 +255,8 @@ def test_grouped_plain_epilogue_equals_hq_grouped_gemm_a8w8(hq):
 
 @pytest.mark.parametrize("shape", [(3601, 3648, 400),    # 256 x 256
                                    (2001, 1088, 272),    # 128 x 128
-                                   (1000, 1088, 400)])   # 64 x 128
+                                   (1000, 1088, 400),    # 64 x 128
+                                   (1000, 1088, 512)])   # 64 x 128, K split inside the workgroup
 @pytest.mark.parametrize("bias_kind", ["none", "bf16"])
 def test_full_line_stores_every_element(hq, shape, bias_kind):
     """bf16 outputs go out as whole 128-byte lines when N % 64 == 0: the

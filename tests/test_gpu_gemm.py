@@ -102,7 +102,8 @@ def _edge_pairs(rng, m, n, count):
                                    (4000, 1000, 272),                       # 128 x 128
                                    (2001, 1088, 272),                       # 128 x 128, staged stores
                                    (1000, 1000, 400),                       # 64 x 128
-                                   (1000, 1088, 400)])                      # 64 x 128, staged stores
+                                   (1000, 1088, 400),                       # 64 x 128, staged stores
+                                   (1000, 1088, 512)])                      # 64 x 128, K split in the workgroup
 @pytest.mark.parametrize("pair", PAIRS)
 def test_gemm_tile_configs_narrow_strict(hq, shape, pair):
     m, n, k = shape
