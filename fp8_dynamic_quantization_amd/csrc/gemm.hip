@@ -827,7 +827,6 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
   p.kpw = p.mb == 1 ? 4 : (p.mb == 2 ? 2 : 1);  // loads in flight within the 128-VGPR budget
   p.groups = (frag_rows(n) + p.f - 1) / p.f;
   p.halves = 1;
-#ifndef HQ_SK_NOHALVES
   // One 16-row activation block and fewer fragments than CUs: each fragment's
   // two slot halves go to two workgroups (the other half's lanes load zeros),
   // so every CU streams weight with no cross-workgroup sum.
@@ -835,19 +834,12 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
     p.halves = 2;
     p.groups *= 2;
   }
-#endif
   // Split only when one workgroup per group would take its wavefronts through
   // more than one chunk of loads: below that the cross-workgroup step costs
   // more latency than the extra workgroups save.
   p.splits = 1;
   const int nkb = (k + kBK - 1) / kBK;
-#ifdef HQ_SK_MINWG
-  if (p.groups < (int)(kSkCounterBytes / 4) && nkb >= 4) {
-    while (p.splits < 8 && p.groups * p.splits < HQ_SK_MINWG) p.splits *= 2;
-    while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;
-  }
-#endif
-  if (p.splits == 1 && nkb > kSkWaves * p.kpw && p.groups < (int)(kSkCounterBytes / 4)) {
+  if (nkb > kSkWaves * p.kpw && p.groups < (int)(kSkCounterBytes / 4)) {
     while (p.splits < 8 && p.groups * p.splits < 256) p.splits *= 2;
     while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;  // at least 2 K blocks per workgroup
   }
@@ -1120,9 +1112,6 @@ static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t works
 enum TileCfg { kTile256, kTile128x256, kTile128, kTile64x128 };
 
 static TileCfg pick_tile(long rows, long n, int experts, bool strict) {
-#ifdef HQ_FORCE_TILE
-  if (!strict && !experts) return (TileCfg)HQ_FORCE_TILE;
-#endif
   struct Cand {
     TileCfg cfg;
     int bm, bn;
