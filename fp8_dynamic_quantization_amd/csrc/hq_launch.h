@@ -23,6 +23,10 @@ constexpr int kArrivalStride = 32;        // uint32 words between arrival counte
 // one of its blocks gave up its bounded wait (the call's scales are then NaN;
 // the bit stays set until the workspace is zero-filled again).
 constexpr int kBarGen = 0, kBarTop = kArrivalStride, kBarStatus = 2 * kArrivalStride, kBarWords = 3 * kArrivalStride;
+// Line 0, words 8-9: the one-pass per-channel kernel's tensor-wide non-finite
+// flag, a 64-bit word (generation in the high half, 1 in the low half when a
+// tile of that launch held an Inf or NaN).
+constexpr int kBarColFlag = 8;
 constexpr uint32_t kGaveUpBit = 1u;
 constexpr size_t kArrivalOffsetWords = kMaxTensorPartials;
 constexpr size_t kBarrierOffsetWords = kArrivalOffsetWords + (size_t)kArrivalGroups * kArrivalStride;

@@ -85,9 +85,9 @@ int64_t hq_scale_count(int gran, int64_t rows, int64_t cols);
 /* Bytes of device workspace hq_quantize_fp8 needs for this granularity and
  * shape: 0 for HQ_PER_TOKEN; for HQ_PER_TENSOR (dynamic or delayed) a fixed
  * 8576-byte region of block partials, arrival counters, the single-pass grid
- * barrier and its status word; for HQ_PER_CHANNEL that region plus ceil(rows/128) * cols * 4 bytes
- * of column partials after it (so one workspace sized for the largest call
- * serves every granularity). Returns 0 for invalid arguments (hq_quantize_fp8
+ * barrier and its status word; for HQ_PER_CHANNEL that region plus (ceil(rows/128) + 1) * cols * 8
+ * bytes of column partials and per-column words after it (so one workspace
+ * sized for the largest call serves every granularity). Returns 0 for invalid arguments (hq_quantize_fp8
  * then reports the error). */
 size_t hq_quantize_workspace_bytes(int gran, int64_t rows, int64_t cols);
 

@@ -88,9 +88,10 @@ def test_workspace_bytes(hq):
     # word, top counter, sticky status)
     assert region == 1024 * 4 + 32 * 128 + 3 * 128
     assert region == hq.hq_quantize_workspace_bytes(hq.HQ_PER_TENSOR, 4096, 4096)
-    # per-channel: the per-tensor region, then ceil(rows/128) * cols column partials
-    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 4096, 4096) == region + 32 * 4096 * 4
-    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 1, 64) == region + 64 * 4
+    # per-channel: the per-tensor region, then ceil(rows/128) * cols column partials and cols
+    # column words, 8 bytes each
+    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 4096, 4096) == region + (32 + 1) * 4096 * 8
+    assert hq.hq_quantize_workspace_bytes(hq.HQ_PER_CHANNEL, 1, 64) == region + 2 * 64 * 8
     assert hq.hq_quantize_workspace_bytes(9, 4, 4) == 0
 
 
