@@ -923,7 +923,7 @@ __device__ __forceinline__ size_t preshuffled_offset(int n, int k, int kblocks) 
 
 enum { kScaleGiven = 0, kScaleRing = 1, kScaleDynamic = 2 };
 
-template <int XT, int FMT, int MODE, bool SR>
+template <int XT, int FMT, int MODE, bool SR, bool STAGE_T>
 __global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
     const uint4* __restrict__ x, int rows, int cols, LayoutOut o, const float* __restrict__ scale_in,
     const uint32_t* __restrict__ dyn_partial, int ndyn, float* __restrict__ scale_out,
@@ -931,6 +931,20 @@ __global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
     uint32_t* arrivals, SrSeed sd) {
   constexpr int E = VecTraits<XT>::kElems;
   constexpr int VPC = 8 / E;  // 16-byte vectors per 8 columns
+  // A whole tile's transposed codes go through LDS (128 rows of the
+  // transposed tile, 136-byte pitch against bank conflicts) and out as whole
+  // 128-byte lines: stored straight from the threads, each line of the
+  // transposed output came in four 32-byte pieces from four wavefronts
+  // (15.0 -> 13.9 us for a bf16 [2048, 4096] gradient, row-major and
+  // transposed, with a ring). The transposed pre-shuffled output keeps the
+  // per-thread stores: staged in the same way (each 128 x 128 tile is one K
+  // block of 8 contiguous 2048-byte fragments) it was no faster on [4096,
+  // 1024] and slower on [2048, 1024] (5.5 -> 5.9 us, 128 tiles: one workgroup
+  // on half the CUs, whose extra barriers nothing overlaps).
+  // (STAGE_T: launched when the transposed row-major output is asked for; the
+  // other launches keep the registers of the plain form.)
+  constexpr int kQtPitch = 136;
+  __shared__ __align__(16) uint8_t qt_stage[STAGE_T ? 128 * kQtPitch : 16];
   __shared__ uint32_t red[kBlock / 64];
   float s;
   if (MODE == kScaleGiven) {
@@ -993,11 +1007,30 @@ __global__ __launch_bounds__(kBlock) void quant_layouts_kernel(
         }
         t[i] = make_uint2(lo, hi);
       }
+      const int tr0 = (tile / tiles_c) * 128, tc0 = (tile % tiles_c) * 128;
+      (void)tr0;
+      (void)tc0;
+      const bool stage_t = STAGE_T && o.qt && tr0 + 128 <= rows && tc0 + 128 <= cols;  // workgroup-uniform
+      if (stage_t) {
+        __syncthreads();  // the previous tile's read-back is done
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(qt_stage + (8 * cv + i) * kQtPitch + 8 * rg) = t[i];
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 128 * 8 / kBlock; ++p) {
+          const int idx = p * kBlock + threadIdx.x;  // 16-byte piece c16 of transposed row R
+          const int R = idx >> 3, c16 = idx & 7;
+          const uint2 lo = *reinterpret_cast<const uint2*>(qt_stage + R * kQtPitch + 16 * c16);
+          const uint2 hi = *reinterpret_cast<const uint2*>(qt_stage + R * kQtPitch + 16 * c16 + 8);
+          __builtin_nontemporal_store(hq_u4v{lo.x, lo.y, hi.x, hi.y},
+                                      reinterpret_cast<hq_u4v*>(o.qt + (size_t)(tc0 + R) * rows + tr0 + 16 * c16));
+        }
+      }
       // rows % 16 == 0 when a transposed output is asked for: an 8-row piece is all in or all out
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int col = c0 + i;
-        if (o.qt && col < cols && r0 < rows) *reinterpret_cast<uint2*>(o.qt + (size_t)col * rows + r0) = t[i];
+        if (o.qt && !stage_t && col < cols && r0 < rows) *reinterpret_cast<uint2*>(o.qt + (size_t)col * rows + r0) = t[i];
         if (o.qtp && col < o.np_t) *reinterpret_cast<uint2*>(o.qtp + preshuffled_offset(col, r0, o.kb_t)) = t[i];
       }
     }
@@ -1397,22 +1430,28 @@ hipError_t launch_quant_layouts(const void* x, int xt, int rows, int cols, int f
     else
       hipLaunchKernelGGL((amax_partials_kernel<kF32>), dim3(ndyn), dim3(kBlock), 0, st, xv, nvec, partial);
   }
-#define CALL(A, B, S)                                                                                  \
-  do {                                                                                                       \
-    if (mode == kScaleGiven)                                                                                 \
-      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleGiven, S>), grid, block, 0, st, xv, rows, cols, o,    \
+#define LAUNCH_MODE(A, B, S, T)                                                                            \
+  do {                                                                                                     \
+    if (mode == kScaleGiven)                                                                               \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleGiven, S, T>), grid, block, 0, st, xv, rows, cols, o, \
                          scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals, sd); \
-    else if (mode == kScaleRing)                                                                             \
-      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleRing, S>), grid, block, 0, st, xv, rows, cols, o,     \
+    else if (mode == kScaleRing)                                                                           \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleRing, S, T>), grid, block, 0, st, xv, rows, cols, o, \
                          scale_in, nullptr, 0, scale_out, amax, state, len, idx, margin, flag, partial, arrivals, sd); \
-    else                                                                                                     \
-      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleDynamic, S>), grid, block, 0, st, xv, rows, cols, o,  \
-                         scale_in, partial, ndyn, scale_out, amax, state, len, idx, margin, flag, partial,    \
-                         arrivals, sd);                                                                      \
-    return hipGetLastError();                                                                                \
+    else                                                                                                   \
+      hipLaunchKernelGGL((quant_layouts_kernel<A, B, kScaleDynamic, S, T>), grid, block, 0, st, xv, rows, cols, \
+                         o, scale_in, partial, ndyn, scale_out, amax, state, len, idx, margin, flag, partial,   \
+                         arrivals, sd);                                                                    \
+  } while (0)
+#define CALL(A, B, S)                        \
+  do {                                       \
+    if (o.qt) LAUNCH_MODE(A, B, S, true);    \
+    else LAUNCH_MODE(A, B, S, false);        \
+    return hipGetLastError();                \
   } while (0)
   HQ_DISPATCH_XT_FMT_SR(xt, fmt, sr, CALL);
 #undef CALL
+#undef LAUNCH_MODE
 }
 
 hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_t* flag, const float* amax,
