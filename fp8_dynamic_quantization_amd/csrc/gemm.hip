@@ -849,6 +849,17 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
     while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;  // at least 2 K blocks per workgroup
   }
   p.workspace_bytes = p.splits == 1 ? 0 : kSkCounterBytes + (size_t)p.groups * p.splits * p.f * p.mb * 1024;
+  // Wavefronts per fragment group: 16 for split plans; unsplit, the next power
+  // of two of ceil(nkb / 8), at least 2 (each wavefront then takes up to 8 K
+  // blocks, two chunks of loads). Smaller workgroups cost less to start and
+  // reduce: N = 7168, K = 768 / 2048, M = 1 (one weight copy): 7.9 / 8.2 us at
+  // 16 wavefronts, 3.1 / 3.9 us at 2; N = 2048, K = 7168: 6.7 us at 16, 6.55 at 8.
+  p.waves = kSkWaves;
+  if (p.splits == 1) {
+    int w = 2;
+    while (w < kSkWaves && w * 8 < nkb) w *= 2;
+    p.waves = w;
+  }
   return p;
 }
 
@@ -858,7 +869,8 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
   __shared__ __attribute__((aligned(16))) float red[kSkWaves][64][4];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int waves = blockDim.x >> 6;  // kSkWaves / splits
+  const int waves = blockDim.x >> 6;  // wavefronts of the group in this workgroup
+  const int wtot = waves * splits;     // wavefronts of the fragment group (K blocks are dealt over them)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fg = blockIdx.x / splits, split = blockIdx.x % splits;
   const int g = split * waves + wave;  // wavefront index within the fragment group
@@ -904,12 +916,12 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = (nkb + kSkWaves * KPW - 1) / (kSkWaves * KPW);
+  const int nchunks = (nkb + wtot * KPW - 1) / (wtot * KPW);
   for (int c = 0; c < nchunks; ++c) {
     uint4 fb[KPW][F][2], fx[KPW][MB][2];
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
-      const int kb = (c * KPW + j) * kSkWaves + g;
+      const int kb = (c * KPW + j) * wtot + g;
       // a block past nkb would land in the next fragment's row: send it past the extent
       const int bvo = kb < nkb && my_slots ? lane * 16 : kBadOffset;
 #pragma unroll
@@ -1080,13 +1092,13 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, 
 template <int XF, int WF, bool STRICT>
 static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t workspace_bytes, hipStream_t st) {
   SkinnyPlan p = skinny_plan(a.m, a.n, a.k);
-  const int chunk = kSkWaves / p.splits;  // the planned association, kept when run unsplit
+  const int chunk = p.waves / p.splits;  // the planned association, kept when run unsplit
   if (p.splits > 1 && (workspace == nullptr || workspace_bytes < p.workspace_bytes)) p.splits = 1;
   uint32_t* counters = static_cast<uint32_t*>(workspace);
   float* partials = p.splits > 1
                         ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSkCounterBytes)
                         : nullptr;
-  const dim3 grid(p.groups * p.splits), block(64 * (kSkWaves / p.splits));
+  const dim3 grid(p.groups * p.splits), block(64 * (p.waves / p.splits));
   const int halves = p.halves;
   if (p.mb == 1)
     hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 4, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
