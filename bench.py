@@ -44,6 +44,9 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA (the strict GEMM's instruction)
 M = N = K = 4096
 COPY_PROBE_BYTES = 1 << 30
+NUM_CUS = 256
+QUANT_ROW_WAVES_PER_CU = 12         # the per-token quantize's grid (wavefronts per compute unit)
+ROW_PROBE_WAVES_PER_CU = (4, 8, 12, 16)
 COPY_PROBE_KERNEL = "bitwise_not"
 KERNEL_SOURCES = ["fp8_dynamic_quantization_amd/csrc/gemm.hip", "fp8_dynamic_quantization_amd/csrc/quantize.hip",
                   "fp8_dynamic_quantization_amd/csrc/hq_device.h"]
@@ -252,6 +255,37 @@ def time_graph(torch, launch, reps, replays=5):
     return start.elapsed_time(end) / (replays * reps)
 
 
+class MoeSets:
+    """The grouped MoE workload on the device: 8 experts, N = 2048, K = 1024,
+    8192 rows, per-token x per-expert-channel E4M3; 5 rotating (codes,
+    pre-shuffled weights, output) sets, 141 MB together."""
+
+    def __init__(self, torch, hq, lib):
+        import workloads
+        x, w, offs = workloads.grouped_moe()
+        self.e, self.n, self.k = w.shape
+        self.t = x.shape[0]
+        self.offs = offs
+        e4 = hq.HQ_E4M3
+        gx, self.xs, _ = hq.hq_quantize_fp8(torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16), e4,
+                                            hq.HQ_PER_TOKEN)
+        gw, self.ws, _ = hq.hq_quantize_fp8(torch.from_numpy(w.reshape(self.e * self.n, self.k).view("int16"))
+                                            .cuda().view(torch.bfloat16), e4, hq.HQ_PER_TOKEN)
+        pre = torch.cat([hq.hq_preshuffle_weight(gw[i * self.n:(i + 1) * self.n]) for i in range(self.e)])
+        self.off = torch.from_numpy(offs).cuda()
+        self.sets = [(gx.clone(), pre.clone(), torch.empty((self.t, self.n), dtype=torch.bfloat16, device="cuda"))
+                     for _ in range(5)]
+        self.lib, self.hq = lib, hq
+
+    def launch(self, i, h):
+        P = ctypes.c_void_p
+        a, b, o = self.sets[i % len(self.sets)]
+        st = self.lib.hq_grouped_gemm_a8w8(P(a.data_ptr()), self.hq.HQ_E4M3, P(b.data_ptr()), self.hq.HQ_E4M3,
+                                           P(self.xs.data_ptr()), self.t, P(self.ws.data_ptr()), self.e * self.n,
+                                           P(self.off.data_ptr()), self.e, self.t, self.n, self.k, P(o.data_ptr()), h)
+        assert st == 0, self.hq.hq_last_error()
+
+
 def other_workloads(torch, hq, lib, reps):
     """Decode-skinny GEMM, grouped MoE GEMM and per-tensor / per-channel
     quantize, each timed on rotating buffers larger than the Infinity Cache."""
@@ -300,25 +334,10 @@ def other_workloads(torch, hq, lib, reps):
     del pres
 
     # grouped MoE: 8 experts, N=2048, K=1024, 8192 rows; 5 rotating sets
-    x, w, offs = workloads.grouped_moe()
-    e_, gn, gk = w.shape
-    t = x.shape[0]
-    gx, gxs, _ = hq.hq_quantize_fp8(torch.from_numpy(x.view("int16")).cuda().view(torch.bfloat16), E4M3,
-                                    hq.HQ_PER_TOKEN)
-    gw, gws, _ = hq.hq_quantize_fp8(torch.from_numpy(w.reshape(e_ * gn, gk).view("int16")).cuda()
-                                    .view(torch.bfloat16), E4M3, hq.HQ_PER_TOKEN)
-    pre = torch.cat([hq.hq_preshuffle_weight(gw[i * gn:(i + 1) * gn]) for i in range(e_)])
-    off_d = torch.from_numpy(offs).cuda()
-    gsets = [(gx.clone(), pre.clone(), torch.empty((t, gn), dtype=torch.bfloat16, device="cuda"))
-             for _ in range(5)]
-
-    def glaunch(i, h):
-        a, b, o = gsets[i % len(gsets)]
-        st = lib.hq_grouped_gemm_a8w8(P(a.data_ptr()), E4M3, P(b.data_ptr()), E4M3, P(gxs.data_ptr()), t,
-                                      P(gws.data_ptr()), e_ * gn, P(off_d.data_ptr()), e_, t, gn, gk,
-                                      P(o.data_ptr()), h)
-        assert st == 0, hq.hq_last_error()
-    ms = time_graph(torch, glaunch, 10)
+    moe = MoeSets(torch, hq, lib)
+    gsets, gxs, gws, off_d, offs = moe.sets, moe.xs, moe.ws, moe.off, moe.offs
+    e_, gn, gk, t = moe.e, moe.n, moe.k, moe.t
+    ms = time_graph(torch, moe.launch, 10)
 
     def gslaunch(i, h):
         a, b, o = gsets[i % len(gsets)]
@@ -334,8 +353,8 @@ def other_workloads(torch, hq, lib, reps):
                           "us": round(ms * 1e3, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                           "frac_mfma": round(flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                           "gbs": round(alg / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": alg,
-                          "strict_us": round(strict_ms * 1e3, 3)}
-    del gsets, gw, pre
+                          "strict_us": round(strict_ms * 1e3, 3), "traffic": traffic_from_profile("grouped_moe")}
+    del gsets, moe
 
     # GEMM epilogue variants on the PTPC 4096^3 operands: bf16 bias, and FP8 E4M3 output with an output scale
     x, w = workloads.ptpc_square(1)
@@ -799,6 +818,8 @@ def main():
     ap.add_argument("--no-other", action="store_true", help="skip the decode / grouped / quantize-variant timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (PMC calibration) and exit")
+    ap.add_argument("--grouped-only", action="store_true",
+                    help="only run 10 launches of the grouped MoE GEMM (for the PMC traffic summary) and exit")
     ap.add_argument("--vendor-yardstick", action="store_true",
                     help="only time torch._scaled_mm (the vendor FP8 GEMM) on this library's GEMM shapes, as "
                          "context, and exit")
@@ -829,6 +850,15 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         log(f"copy probe: 3 x bitwise_not over {COPY_PROBE_BYTES} bytes")
+        return
+
+    if args.grouped_only:
+        moe = MoeSets(torch, hq, lib)
+        h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(10):
+            moe.launch(i, h)
+        torch.cuda.synchronize()
+        log("grouped MoE: 10 launches of hq_grouped_gemm_a8w8 over 5 rotating sets")
         return
 
     if args.vendor_yardstick:
@@ -894,6 +924,19 @@ def main():
     same_ms = time_graph(torch, lambda i, h: same_traffic(sets[i % len(sets)], h), 2 * len(sets))
     same_gbs = (M * K * 3) / (same_ms * 1e-3) / 1e9
     log(f"  same-traffic probe: {same_ms * 1e3:.2f} us = {same_gbs:.0f} GB/s")
+    # the same bytes in the per-token kernel's own access pattern: the
+    # hand-written row-streaming probe (one wavefront per row, 16-byte loads,
+    # the next row's loads in flight, non-temporal 8-byte stores), at that
+    # kernel's grid and at three others
+    row_probe = {}
+    for wpc in ROW_PROBE_WAVES_PER_CU:
+        def plaunch(i, h, wpc=wpc):
+            b = sets[i % len(sets)]
+            st = lib.hq_stream_rows_probe(b.p["x"], M, 2 * K, wpc * NUM_CUS, b.p["xq"], h)
+            assert st == 0, hq.hq_last_error()
+        row_probe[wpc] = time_graph(torch, plaunch, 2 * len(sets))
+    probe_ms = row_probe[QUANT_ROW_WAVES_PER_CU]
+    log("  row-streaming probe: " + ", ".join(f"{w}/CU {v * 1e3:.2f} us" for w, v in row_probe.items()))
     other = None if args.no_other else other_workloads(torch, hq, lib, args.kernel_reps)
     if other:
         log(json.dumps(other))
@@ -947,6 +990,13 @@ def main():
                                    "what": "the 32 MiB of X read, 16 MiB written (torch elementwise xor of the "
                                            "two halves of X's bytes), same rotating sets",
                                    "quantize_frac_of_probe": round(same_ms / kms["quant_x"], 4)},
+            "row_probe": {"us": round(probe_ms * 1e3, 3),
+                          "gbs": round(M * K * 3 / (probe_ms * 1e-3) / 1e9, 1),
+                          "waves_per_cu": QUANT_ROW_WAVES_PER_CU,
+                          "what": "hq_stream_rows_probe: X's 32 MiB read and 16 MiB written with the per-token "
+                                  "kernel's access pattern and grid, without its arithmetic",
+                          "quantize_frac_of_probe": round(probe_ms / kms["quant_x"], 4),
+                          "us_by_waves_per_cu": {str(w): round(v * 1e3, 3) for w, v in row_probe.items()}},
         },
         "quant_w_pre": {
             "kernel": "per-output-channel quantize of W into the pre-shuffled layout (hq_quantize_fp8_preshuffled)",

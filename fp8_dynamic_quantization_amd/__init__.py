@@ -12,7 +12,7 @@ from .api import (Ring, gemm_workspace, hq_gemm_a8w8, hq_gemm_a8w8_blockscaled, 
                   hq_gemm_workspace_bytes, hq_quantize_fp8_blockwise, hq_grouped_gemm_a8w8,
                   hq_grouped_gemm_a8w8_epilogue, hq_quantize_fp8_preshuffled, hq_gemm_a8w8_strict,
                   hq_grouped_gemm_a8w8_strict, hq_gemm_a8w8_noalloc,
-                  hq_quantize_workspace_status,
+                  hq_quantize_workspace_status, hq_stream_rows_probe,
                   hq_last_error, hq_preshuffle_weight, hq_preshuffled_bytes, hq_quantize_fp8,
                   hq_quantize_fp8_layouts, hq_quantize_fp8_layouts_stochastic, hq_quantize_fp8_stochastic,
                   hq_quantize_workspace_bytes, hq_scale_count,
@@ -28,4 +28,5 @@ __all__ = [
     "hq_gemm_a8w8_epilogue", "hq_epilogue", "HQ_BIAS_BF16", "HQ_BIAS_E4M3", "HQ_BIAS_E5M2",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error", "gemm_workspace",
     "hq_gemm_a8w8_strict", "hq_grouped_gemm_a8w8_strict", "hq_gemm_a8w8_noalloc", "hq_quantize_workspace_status",
+    "hq_stream_rows_probe",
 ]

@@ -99,6 +99,7 @@ SIGNATURES = {
                                  _P, _P, _SZ, _P]),
     "hq_grouped_gemm_a8w8_strict": (_I, [_P, _I, _P, _I, _P, _I64, _P, _I64, _P, _I32, _I64, _I64, _I64,
                                          ctypes.POINTER(hq_epilogue), _P, _P]),
+    "hq_stream_rows_probe": (_I, [_P, _I64, _I64, _I32, _P, _P]),
     "hq_last_error": (ctypes.c_char_p, []),
 }
 

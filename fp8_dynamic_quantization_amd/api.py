@@ -27,7 +27,7 @@ __all__ = [
     "hq_gemm_a8w8_epilogue",
     "hq_grouped_gemm_a8w8", "hq_grouped_gemm_a8w8_epilogue", "hq_quantize_fp8_preshuffled", "hq_last_error",
     "hq_gemm_a8w8_strict", "hq_grouped_gemm_a8w8_strict", "hq_gemm_a8w8_noalloc",
-    "hq_quantize_workspace_status",
+    "hq_quantize_workspace_status", "hq_stream_rows_probe",
 ]
 
 _XT = {torch.float32: HQ_F32, torch.bfloat16: HQ_BF16}
@@ -309,6 +309,22 @@ def hq_preshuffle_weight(wq: torch.Tensor, out=None, stream=None) -> torch.Tenso
     if out is None:
         out = torch.empty(max(nbytes, 0), dtype=torch.uint8, device=wq.device)
     check(lib.hq_preshuffle_weight(_ptr(wq), n, k, _ptr(out), _stream(wq.device, stream)))
+    return out
+
+
+@_on_stream
+def hq_stream_rows_probe(x: torch.Tensor, waves: int, out=None, stream=None) -> torch.Tensor:
+    """Row-streaming probe over a 2-D 16-bit tensor X [rows, cols] (a
+    measurement aid): returns uint8 [rows, cols] holding the high byte of each
+    element, written with the per-token quantize's access pattern over a grid
+    of `waves` wavefronts."""
+    if x.dim() != 2 or x.element_size() != 2:
+        raise ValueError("x must be a 2-D tensor of 16-bit elements")
+    x = x.contiguous()
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    check(load().hq_stream_rows_probe(_ptr(x), rows, 2 * cols, waves, _ptr(out), _stream(x.device, stream)))
     return out
 
 

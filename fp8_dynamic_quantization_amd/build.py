@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhq.so")
 
-SOURCES = ["quantize.hip", "gemm.hip", "blockscaled.hip", "hq_api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "blockscaled.hip", "probe.hip", "hq_api.cpp"]
 
 # Per-source flags. The GEMM keeps its MFMA accumulators in VGPRs and the
 # operand fragments in AGPRs: with 256 accumulator registers per wavefront the

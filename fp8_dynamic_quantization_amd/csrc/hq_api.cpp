@@ -430,6 +430,24 @@ hq_status hq_preshuffle_weight(const uint8_t* wq, int64_t n, int64_t k, uint8_t*
   return launched(hq::launch_preshuffle(wq, (int)n, (int)k, wq_pre, stream), "hq_preshuffle_weight");
 }
 
+hq_status hq_stream_rows_probe(const void* x, int64_t rows, int64_t row_bytes, int32_t waves, uint8_t* out,
+                               hipStream_t stream) {
+  if (rows < 0 || rows > kMaxDim) return fail(HQ_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1024], got %lld", (long long)rows);
+  if (row_bytes < 16 || row_bytes > 8192 || row_bytes % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "row_bytes must be a multiple of 16 in [16, 8192], got %lld", (long long)row_bytes);
+  if (waves < 1 || waves > (1 << 20)) return fail(HQ_ERR_INVALID_ARGUMENT, "waves must be in [1, 2^20], got %d", waves);
+  if (rows == 0) return ok();
+  if (!x || !out) return fail(HQ_ERR_INVALID_ARGUMENT, "x and out must be non-NULL");
+  if (!aligned(x, 16) || !aligned(out, 8)) return fail(HQ_ERR_INVALID_ARGUMENT, "x must be 16-byte and out 8-byte aligned");
+  const Range rg[] = {{x, (size_t)rows * (size_t)row_bytes, "x"}, {out, (size_t)rows * (size_t)row_bytes / 2, "out"}};
+  const char* other = nullptr;
+  if (const char* a = find_overlap(rg, 2, &other)) return fail(HQ_ERR_INVALID_ARGUMENT, "%s overlaps %s", a, other);
+  hq_status st = check_device();
+  if (st != HQ_OK) return st;
+  (void)hipGetLastError();
+  return launched(hq::launch_stream_rows_probe(x, rows, (int)(row_bytes / 16), waves, out, stream), "hq_stream_rows_probe");
+}
+
 // Epilogue arguments shared by the plain and grouped forms: bias kind, pointers
 // and the validation of their combination. Returns HQ_OK and fills the outputs.
 static hq_status epilogue_args(const hq_epilogue* ep, const void** bias, int* bias_kind, const float** bias_scale,

@@ -71,6 +71,8 @@ hipError_t launch_ring_update(float* state, int len, int idx, int margin, int32_
                               int fmt, hipStream_t st);
 
 hipError_t launch_preshuffle(const uint8_t* wq, int n, int k, uint8_t* out, hipStream_t st);
+hipError_t launch_stream_rows_probe(const void* x, int64_t rows, int row_vecs, int waves, uint8_t* q,
+                                    hipStream_t st);
 
 // Epilogue bias kinds (GemmArgs::bias_kind).
 constexpr int kBiasNone = 0, kBiasBF16 = 1, kBiasE4M3 = 2, kBiasE5M2 = 3;

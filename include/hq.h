@@ -489,6 +489,23 @@ hq_status hq_grouped_gemm_a8w8_strict(const uint8_t* xq, int xf, const uint8_t* 
                                       int64_t total_rows, int64_t n, int64_t k,
                                       const hq_epilogue* ep, void* out, hipStream_t stream);
 
+/* Row-streaming probe: a measurement aid, not a step of the quantization (no
+ * page defines it). It moves the bytes of a per-token quantize pass without
+ * its arithmetic: for each of `rows` rows of 16-bit elements it writes the
+ * high byte of every element, out[r, i] = x[r, i] >> 8, with the per-token
+ * kernel's access pattern (one wavefront per row, 16-byte loads, the next
+ * row's loads in flight while the current row is stored, non-temporal 8-byte
+ * stores) over a grid of `waves` wavefronts. Timed at the per-token kernel's
+ * own grid (12 wavefronts per compute unit) it is the HBM ceiling of a pass of
+ * that size and shape.
+ *   x          device, 16-bit elements [rows, row_bytes / 2], 16-byte aligned
+ *   out        device, uint8 [rows, row_bytes / 2], 8-byte aligned, must not
+ *              overlap x
+ * Requires row_bytes % 16 == 0, 16 <= row_bytes <= 8192, 1 <= waves <= 2^20,
+ * 0 <= rows <= 2^31 - 1024. rows == 0 returns HQ_OK without a launch. */
+hq_status hq_stream_rows_probe(const void* x, int64_t rows, int64_t row_bytes, int32_t waves, uint8_t* out,
+                               hipStream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* hq_last_error(void);
 

@@ -599,6 +599,24 @@ def test_workspace_status_valid_call_reaches_device_gate(hq):
         hq.HQ_ERR_UNSUPPORTED_DEVICE
 
 
+def test_stream_rows_probe_validation(hq):
+    lib = hq.load()
+    E = hq.HQ_ERR_INVALID_ARGUMENT
+    assert lib.hq_stream_rows_probe(None, 0, 8192, 3072, None, None) == hq.HQ_OK   # empty: no launch
+    assert lib.hq_stream_rows_probe(fake(0), 4, 8200, 3072, fake(1), None) == E       # row_bytes > 8192
+    assert lib.hq_stream_rows_probe(fake(0), 4, 24, 3072, fake(1), None) == E         # not a multiple of 16
+    assert lib.hq_stream_rows_probe(fake(0), 4, 8192, 0, fake(1), None) == E          # no wavefronts
+    assert lib.hq_stream_rows_probe(fake(0), -1, 8192, 3072, fake(1), None) == E
+    assert lib.hq_stream_rows_probe(fake(0, 8), 4, 8192, 3072, fake(1), None) == E    # x not 16-byte aligned
+    assert lib.hq_stream_rows_probe(fake(0), 4, 8192, 3072, fake(0, 8192), None) == E  # out overlaps x
+    assert lib.hq_stream_rows_probe(None, 4, 8192, 3072, fake(1), None) == E
+
+
+@no_gpu
+def test_stream_rows_probe_valid_call_reaches_device_gate(hq):
+    assert hq.load().hq_stream_rows_probe(fake(0), 4096, 8192, 3072, fake(1), None) == hq.HQ_ERR_UNSUPPORTED_DEVICE
+
+
 # ---------------------------------------------------------------------------
 # dimension cap: tile rounding of a dimension stays inside 32-bit arithmetic
 # ---------------------------------------------------------------------------
