@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint4* __restri
           sb[wv][1][t] = am;
         }
         uint32_t w[E / 4];
-        cast_vec<XT, FMT, SR>(cur[u], r, own, w, sd, ((size_t)row * vpr + i) * E);
+        cast_vec<XT, FMT, SR, true>(cur[u], r, own, w, sd, ((size_t)row * vpr + i) * E);
         store_codes<E>(qr + (size_t)i * E, w);
       }
     }

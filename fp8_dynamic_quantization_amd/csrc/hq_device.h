@@ -33,20 +33,24 @@ __device__ __forceinline__ float clamp_fmax(float v, float fmax) {
   return __builtin_amdgcn_fmed3f(v, -fmax, fmax);
 }
 
-// Two saturating RNE casts packed into 16-bit half `hi` of `old`.
-template <int FMT, bool HI>
+// Two saturating RNE casts packed into 16-bit half `hi` of `old`. CLAMP = false
+// leaves out the clamp to +-fmax: only for finite values whose magnitude is at
+// most one float32 ulp above fmax, which the conversion's nearest-even rounding
+// takes to fmax by itself (the next magnitude either format encodes lies 2^-4
+// (E4M3) or 2^-3 (E5M2) of fmax above it; checked on the device).
+template <int FMT, bool HI, bool CLAMP = true>
 __device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
   constexpr float F = Fp8Fmt<FMT>::kMax;
-  const float ca = clamp_fmax(a, F), cb = clamp_fmax(b, F);
+  const float ca = CLAMP ? clamp_fmax(a, F) : a, cb = CLAMP ? clamp_fmax(b, F) : b;
   if (FMT == kE4M3) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, (int)old, HI);
   return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, (int)old, HI);
 }
 
 // Four floats -> four codes in one dword (element i in byte i).
-template <int FMT>
+template <int FMT, bool CLAMP = true>
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-  uint32_t w = cvt2<FMT, false>(a, b, 0u);
-  return cvt2<FMT, true>(c, d, w);
+  uint32_t w = cvt2<FMT, false, CLAMP>(a, b, 0u);
+  return cvt2<FMT, true, CLAMP>(c, d, w);
 }
 
 // Replace byte i of `codes` by 0x7F where element i is NaN.
@@ -107,8 +111,9 @@ __device__ __forceinline__ uint32_t vec_absmax_finite(const uint4& v) {
 }
 
 // Cast the vector's elements times r. Output: bytes in element order, in
-// `out[0 .. kElems/4 - 1]`. `patch` adds the NaN fix-up.
-template <int XT, int FMT>
+// `out[0 .. kElems/4 - 1]`. `patch` adds the NaN fix-up; CLAMP = false (see
+// cvt2) only for finite elements with |x * r| <= fmax * (1 + 2^-23).
+template <int XT, int FMT, bool CLAMP = true>
 __device__ __forceinline__ void vec_cast(const uint4& v, float r, bool patch, uint32_t* out) {
 #pragma unroll
   for (int d = 0; d < VecTraits<XT>::kElems / 4; ++d) {
@@ -116,7 +121,7 @@ __device__ __forceinline__ void vec_cast(const uint4& v, float r, bool patch, ui
     const float b = vec_elem<XT>(v, 4 * d + 1) * r;
     const float c = vec_elem<XT>(v, 4 * d + 2) * r;
     const float e = vec_elem<XT>(v, 4 * d + 3) * r;
-    uint32_t w = cvt4<FMT>(a, b, c, e);
+    uint32_t w = cvt4<FMT, CLAMP>(a, b, c, e);
     if (patch) w = patch_nan4(w, a, b, c, e);
     out[d] = w;
   }
@@ -124,10 +129,14 @@ __device__ __forceinline__ void vec_cast(const uint4& v, float r, bool patch, ui
 
 // Cast a whole vector; applies the NaN patch only when the vector holds a
 // non-finite element (raw >= kInfBits), so the common path is branch-free.
-template <int XT, int FMT>
+// OWN: r comes from the amax of a group the vector's elements belong to
+// (dynamic scaling), so every finite element has |x| <= amax and, with
+// s = fl32(amax / fmax) and r = fl32(1 / s), |fl32(x * r)| <= fmax * (1 + 2^-23):
+// a vector without Inf or NaN then needs no clamp.
+template <int XT, int FMT, bool OWN = false>
 __device__ __forceinline__ void vec_cast_checked(const uint4& v, float r, uint32_t raw, uint32_t* out) {
   if (raw >= kInfBits) vec_cast<XT, FMT>(v, r, true, out);
-  else vec_cast<XT, FMT>(v, r, false, out);
+  else vec_cast<XT, FMT, !OWN>(v, r, false, out);
 }
 
 // ---- stochastic rounding to E5M2 -------------------------------------------------
@@ -195,12 +204,12 @@ __device__ __forceinline__ uint32_t e5m2_sr4(float a, float b, float c, float d,
 }
 
 // Cast a whole vector whose first element has flat index `elem`: nearest-even
-// (SR = false, vec_cast_checked) or stochastic E5M2 (SR = true).
-template <int XT, int FMT, bool SR>
+// (SR = false, vec_cast_checked, OWN as there) or stochastic E5M2 (SR = true).
+template <int XT, int FMT, bool SR, bool OWN = false>
 __device__ __forceinline__ void cast_vec(const uint4& v, float r, uint32_t raw, uint32_t* out, SrSeed sd,
                                          size_t elem) {
   if constexpr (!SR) {
-    vec_cast_checked<XT, FMT>(v, r, raw, out);
+    vec_cast_checked<XT, FMT, OWN>(v, r, raw, out);
   } else {
     static_assert(FMT == kE5M2, "stochastic rounding produces E5M2");
 #pragma unroll

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
       const int i = threadIdx.x + j * BLOCK;
       if (i < vpr) {
         uint32_t w[E / 4];
-        cast_vec<XT, FMT, SR>(v[j], r, raw[j], w, sd, (row * vpr + i) * E);
+        cast_vec<XT, FMT, SR, true>(v[j], r, raw[j], w, sd, (row * vpr + i) * E);
         store_codes<E>(qr + (size_t)i * E, w);
       }
     }
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(BLOCK) void quant_rows_kernel(
     for (int i = threadIdx.x; i < vpr; i += BLOCK) {
       const uint4 vv = xr[i];
       uint32_t w[E / 4];
-      cast_vec<XT, FMT, SR>(vv, r, vec_absmax_raw<XT>(vv), w, sd, (row * vpr + i) * E);
+      cast_vec<XT, FMT, SR, true>(vv, r, vec_absmax_raw<XT>(vv), w, sd, (row * vpr + i) * E);
       store_codes<E>(qr + (size_t)i * E, w);
     }
   }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
       const int i = lane + 64 * j;
       if (i < vpr) {
         uint32_t w[E / 4];
-        cast_vec<XT, FMT, SR>(cur[j], r, raw[j], w, sd, ((size_t)row * vpr + i) * E);
+        cast_vec<XT, FMT, SR, true>(cur[j], r, raw[j], w, sd, ((size_t)row * vpr + i) * E);
         store_codes<E>(qr + (size_t)i * E, w);
       }
     }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const uint4* __res
         uint32_t w[E / 4];
         if constexpr (SR) cast_vec<XT, FMT, true>(v[u], r, 0u, w, sd, i * E);
         else if (nonfinite) vec_cast<XT, FMT>(v[u], r, true, w);
-        else vec_cast<XT, FMT>(v[u], r, false, w);
+        else vec_cast<XT, FMT, false>(v[u], r, false, w);
         store_codes<E>(q + i * E, w);
       }
     }
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_fused_kernel(const uint4*
     const size_t i = base + k * stride;
     if (i < nvec) {
       uint32_t w[E / 4];
-      cast_vec<XT, FMT, SR>(v[k], r, m[k], w, sd, i * E);
+      cast_vec<XT, FMT, SR, true>(v[k], r, m[k], w, sd, i * E);
       store_codes<E>(q + i * E, w);
     }
   }
@@ -587,8 +587,10 @@ __device__ __forceinline__ void col_tile_cast(const uint4 (&v)[kColPer], int row
       if constexpr (SR) {
         w[d] = e5m2_sr4(a, b, c, e, sd, ((size_t)row * vpr + vc) * E + 4 * d);
       } else {
-        w[d] = cvt4<FMT>(a, b, c, e);
-        if (patch) w[d] = patch_nan4(w[d], a, b, c, e);
+        // r comes from the column's own amax, so without a non-finite element in
+        // these columns no value needs the clamp (vec_cast_checked, OWN)
+        if (patch) w[d] = patch_nan4(cvt4<FMT>(a, b, c, e), a, b, c, e);
+        else w[d] = cvt4<FMT, false>(a, b, c, e);
       }
     }
     store_codes<E>(q + ((size_t)row * vpr + vc) * E, w);
@@ -1087,7 +1089,7 @@ __global__ __launch_bounds__(64 * kPreRows) void quant_rows_pre_long_kernel(
     uint32_t w[E / 4];
     if (valid && i < vpr) {
       const uint4 v = xr[i];
-      cast_vec<XT, FMT, false>(v, r, vec_absmax_raw<XT>(v), w, sd, 0);
+      cast_vec<XT, FMT, false, true>(v, r, vec_absmax_raw<XT>(v), w, sd, 0);
       if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
       store_codes_temporal<E>(qp + preshuffled_offset(row, i * E, kblocks), w);
     } else {
@@ -1163,7 +1165,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void quant_rows_pre_group_kernel(
     if (i < vpp) {
       uint32_t w[E / 4];
       if (valid && i < vpr) {
-        cast_vec<XT, FMT, false>(cur[j], r, raw[j], w, sd, 0);
+        cast_vec<XT, FMT, false, true>(cur[j], r, raw[j], w, sd, 0);
         if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
       } else {
 #pragma unroll

@@ -389,3 +389,74 @@ def test_invalid_arguments_leave_outputs_untouched(hq):
         hq.hq_quantize_fp8(x[:, :40], fp8.E4M3, Q.PER_TOKEN, q=q[:, :40], scale_out=s)
     torch.cuda.synchronize()
     assert bool((q == 0xAB).all()) and bool((s == -1.0).all())
+
+
+# ---- scaled values one float32 ulp above fmax ------------------------------------
+
+def _ulp_above_fmax_amaxes(fmt, dtype):
+    """Every positive normal amax a of the input type whose scaled value
+    fl32(a * fl32(1 / max(fl32(a / fmax), 2^-126))) lies above fmax (one float32
+    ulp above, at most). Found by enumerating the type's values (bf16: all of
+    them; float32: one in 2^7 of the mantissas, all exponents)."""
+    if dtype == Q.BF16:
+        bits = (np.arange(0x0080, 0x7F80, dtype=np.uint32) << np.uint32(16))
+    else:
+        bits = np.arange(0x00800000, 0x7F800000, 128, dtype=np.uint32)
+    a = bits.view(np.float32)
+    fmax = np.float32(fp8.fmax(fmt))
+    s = np.maximum((a / fmax).astype(np.float32), np.float32(2.0 ** -126))
+    r = (np.float32(1.0) / s).astype(np.float32)
+    v = (a * r).astype(np.float32)
+    assert np.all(v <= np.nextafter(fmax, np.float32(np.inf)))
+    return a[v > fmax]
+
+
+def _rows_with_amax(rng, amax, cols):
+    """One row per amax: +-amax planted at a random column (and its negation in
+    another), the other entries amax times factors in (-1, 1) rounded towards
+    zero to bf16, so the row's amax is the planted value."""
+    n = len(amax)
+    x = (amax[:, None] * rng.uniform(-1.0, 1.0, (n, cols))).astype(np.float32)
+    x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    c = rng.integers(0, cols, n)
+    x[np.arange(n), c] = amax * np.where(rng.random(n) < 0.5, 1, -1).astype(np.float32)
+    x[np.arange(n), (c + 1 + rng.integers(0, cols - 1, n)) % cols] = -x[np.arange(n), c]
+    return x
+
+
+@pytest.mark.parametrize("dtype", [Q.BF16, Q.F32])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_scaled_value_one_ulp_above_fmax(hq, fmt, dtype):
+    """With dynamic scales every finite element has |x| <= amax, and the kernels
+    cast such vectors without the clamp to +-fmax: the largest scaled value,
+    fl32(amax * r), can sit one float32 ulp above fmax, and the conversion's own
+    nearest-even rounding must give the fmax code there. Every group here has
+    such an amax (all of them for bf16, a sample for float32): per token, per
+    channel (the transpose), per tensor, per row into the pre-shuffled layout
+    and block-wise, each checked byte for byte against the oracle."""
+    from oracle import blockwise as B
+    from oracle import preshuffle as P
+    rng = np.random.default_rng(17 + fmt + 2 * dtype)
+    amax = _ulp_above_fmax_amaxes(fmt, dtype)
+    assert len(amax) > 1000
+    if len(amax) > 8192:
+        amax = rng.choice(amax, 8192, replace=False)
+    x = _rows_with_amax(rng, amax, 64)
+    x_in = workloads.to_bf16_bits(x) if dtype == Q.BF16 else x
+    if dtype == Q.BF16:
+        assert np.array_equal(workloads.to_bf16_bits(x), (x.view(np.uint32) >> 16).astype(np.uint16))
+    _assert_same(hq, x_in, dtype, fmt, Q.PER_TOKEN, "per token, amax*r above fmax")
+    _assert_same(hq, np.ascontiguousarray(x_in[:1024].T), dtype, fmt, Q.PER_CHANNEL, "per channel")
+    for i in rng.choice(len(amax), 8, replace=False):
+        t = _rows_with_amax(rng, np.full(32, amax[i], np.float32), 64)
+        _assert_same(hq, workloads.to_bf16_bits(t) if dtype == Q.BF16 else t, dtype, fmt, Q.PER_TENSOR,
+                     "per tensor")
+    xd = dev_bf16(x_in) if dtype == Q.BF16 else dev_f32(x_in)
+    q_pre, s, _, q = hq.hq_quantize_fp8_preshuffled(xd, fmt, row_major=True)
+    got = hq.hq_quantize_fp8_blockwise(xd, fmt, 64)
+    torch.cuda.synchronize()
+    q_ref, s_ref, _ = Q.quantize_dynamic(x_in, dtype, fmt, Q.PER_TOKEN)
+    assert np.array_equal(host(q), q_ref) and np.array_equal(host(q_pre), P.preshuffle(q_ref))
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    bq, bs, _ = B.quantize_blockwise(x_in, dtype, fmt, 64)
+    assert np.array_equal(host(got[0]), bq) and np.array_equal(host(got[1]).view(np.uint32), bs.view(np.uint32))
