@@ -844,6 +844,7 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
   // more latency than the extra workgroups save.
   p.splits = 1;
   const int nkb = (k + kBK - 1) / kBK;
+  p.kb = nkb;
   if (nkb > kSkWaves * p.kpw && p.groups < (int)(kSkCounterBytes / 4)) {
     while (p.splits < 8 && p.groups * p.splits < 256) p.splits *= 2;
     while (p.splits > 1 && nkb < p.splits * 2) p.splits /= 2;  // at least 2 K blocks per workgroup
@@ -863,8 +864,11 @@ SkinnyPlan skinny_plan(int m, int n, int k) {
   return p;
 }
 
-template <int XF, int WF, int MB, int F, int KPW, bool STRICT>
-__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs a, int splits, int chunk, int halves,
+// TPB: the largest workgroup the kernel is launched with; a plan whose
+// workgroups are smaller compiles with a smaller bound and gets the registers
+// for more K blocks per chunk of loads (KPW).
+template <int XF, int WF, int MB, int F, int KPW, bool STRICT, int TPB = 64 * kSkWaves>
+__global__ __launch_bounds__(TPB) void gemm_skinny_kernel(GemmArgs a, int splits, int chunk, int halves,
                                                                   uint32_t* counters, float* partials) {
   __shared__ __attribute__((aligned(16))) float red[kSkWaves][64][4];
   __shared__ int s_last;
@@ -1098,17 +1102,48 @@ static hipError_t launch_skinny(const GemmArgs& a, void* workspace, size_t works
   float* partials = p.splits > 1
                         ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kSkCounterBytes)
                         : nullptr;
-  const dim3 grid(p.groups * p.splits), block(64 * (p.waves / p.splits));
+  const int wg_waves = p.waves / p.splits;
+  const dim3 grid(p.groups * p.splits), block(64 * wg_waves);
   const int halves = p.halves;
-  if (p.mb == 1)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 4, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
-                       partials);
-  else if (p.mb == 2)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 2, 2, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
-                       partials);
-  else if constexpr (!STRICT)
-    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2, 1, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves, counters,
-                       partials);
+  // K blocks each wavefront takes (dealt over the group's p.waves wavefronts).
+  // Where the workgroup is small enough, the register budget it leaves holds
+  // all of them in one chunk of loads, so each wavefront waits for memory once
+  // (N = 2048, K = 7168: M = 1 and 8 take 7 blocks per wavefront in one chunk
+  // instead of two of 4; M = 32 takes 4 in one chunk instead of two of 2). The
+  // K order each wavefront adds its blocks in does not depend on the chunking,
+  // so the outputs are the same bits.
+  // (The strict form keeps the 1024-thread bound: its float16 conversions
+  // need the registers.)
+  const int bpw = (p.kb + p.waves - 1) / p.waves;
+  const bool deep1 = wg_waves <= 8 && bpw > 4, deep2 = wg_waves <= 4 && bpw > 2;
+  if (p.mb == 1) {
+    if constexpr (!STRICT) {
+      if (deep1) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 8, STRICT, 512>), grid, block, 0, st, a, p.splits, chunk,
+                           halves, counters, partials);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 1, 1, 4, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves,
+                       counters, partials);
+  } else if (p.mb == 2) {
+    if constexpr (!STRICT) {
+      if (deep2) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 2, 4, STRICT, 256>), grid, block, 0, st, a, p.splits, chunk,
+                           halves, counters, partials);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 2, 2, 2, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves,
+                       counters, partials);
+  } else if constexpr (!STRICT) {
+    if (wg_waves <= 4 && bpw > 1)
+      hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2, 4, STRICT, 256>), grid, block, 0, st, a, p.splits, chunk,
+                         halves, counters, partials);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<XF, WF, 4, 2, 1, STRICT>), grid, block, 0, st, a, p.splits, chunk, halves,
+                         counters, partials);
+  }
   return hipGetLastError();
 }
 

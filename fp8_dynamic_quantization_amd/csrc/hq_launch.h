@@ -110,7 +110,7 @@ struct GemmArgs {
 // halves = 2: each group is one half (8 of the 16 slots) of a weight fragment,
 // so a narrow N still gives every CU a group without splitting K.
 struct SkinnyPlan {
-  int mb, f, kpw, groups, splits, halves, waves;
+  int mb, f, kpw, groups, splits, halves, waves, kb;  // kb: 128-deep K blocks
   size_t workspace_bytes;
 };
 SkinnyPlan skinny_plan(int m, int n, int k);
