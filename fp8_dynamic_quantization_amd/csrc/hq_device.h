@@ -9,7 +9,10 @@
 // (every pattern from 2^-20 up to 2^18, zero, subnormals, Inf and NaN, compared on
 // the device with the CPU encoder; below and above those binades every value is a
 // signed zero or saturates); NaN inputs, which the clamp would turn into +-fmax,
-// are patched to the canonical code 0x7F.
+// are patched to the canonical code 0x7F. Casts whose scale comes from the amax
+// of the elements' own group, on vectors without Inf or NaN, leave the clamp
+// out: their scaled values are never more than one float32 ulp above fmax, which
+// the conversion rounds to fmax (vec_cast_checked, OWN).
 #pragma once
 
 #include <hip/hip_runtime.h>
