@@ -234,18 +234,36 @@ def cpu_baseline(min_seconds: float):
     }
 
 
-def time_graph(torch, launch, reps, replays=5):
+# Untimed replays before the timed ones: at least this much GPU time of the
+# same launches, so each kernel is timed at the clock it settles at under its
+# own load whatever ran before it (from a cold start the PTPC step takes about
+# 150 steps, 12 ms, to settle).
+GRAPH_WARM_MS = 25.0
+GRAPH_WARM_MAX_REPLAYS = 2000
+
+
+def time_graph(torch, launch, reps, replays=5, info=None):
     """Average duration (ms) of one launch: `reps` launches captured in a HIP
     graph (launch(i, stream_handle)), replayed back to back, so host launch
-    overhead does not hide short kernels."""
+    overhead does not hide short kernels. The graph is first replayed untimed
+    until GRAPH_WARM_MS have passed (the count goes to info["untimed_replays"]
+    when a dict is given)."""
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         for i in range(reps):
             launch(i, h)
-    g.replay()
-    torch.cuda.synchronize()
+    warm = 0
+    t_warm = time.perf_counter()
+    while True:
+        g.replay()
+        warm += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t_warm) * 1e3 >= GRAPH_WARM_MS or warm >= GRAPH_WARM_MAX_REPLAYS:
+            break
+    if info is not None:
+        info["untimed_replays"] = warm
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(replays):
@@ -897,11 +915,13 @@ def main():
     # Per-kernel durations: each kernel launched back to back over the rotating
     # sets inside a HIP graph on a side stream, bracketed by HIP events on that
     # stream (no host launch overhead, no event between launches).
-    kms = {}
+    kms, warm_replays = {}, {}
     for name, fn in {**ops, **two_launch}.items():
         def launch(i, h, fn=fn):
             fn(sets[i % len(sets)], h)
-        kms[name] = time_graph(torch, launch, 2 * len(sets))
+        info = {}
+        kms[name] = time_graph(torch, launch, 2 * len(sets), info=info)
+        warm_replays[name] = info["untimed_replays"]
     for name, ms in kms.items():
         log(f"  {name}: {ms * 1e3:.2f} us")
     quant_bytes = M * K * 2 + M * K + M * 4 * 2      # bf16 in, codes out, scale + amax out
@@ -975,7 +995,8 @@ def main():
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kms.items()},
         "kernel_timing": {"method": "HIP graph of launches over the rotating sets on torch's current stream, "
                                     "HIP events around the timed replays",
-                          "launches_per_replay": 2 * args.rotate, "untimed_replays": 1, "timed_replays": 5,
+                          "launches_per_replay": 2 * args.rotate,
+                          "untimed_replays": {"min_ms": GRAPH_WARM_MS, "count": warm_replays}, "timed_replays": 5,
                           "step_loop_launches_per_kernel": args.warmup + args.steps},
         "quantize": {
             "kernel": "per-token quantize of X (hq_quantize_fp8)",
