@@ -941,6 +941,15 @@ def main():
     # element read, one byte written (torch's vectorised elementwise xor of the
     # two halves of X's bytes into the code buffer), over the same rotating
     # sets; a practical ceiling for a pass of this size
+    # The whole step (quantize X, quantize W into the pre-shuffled layout, GEMM)
+    # as one graph of 16 steps over the rotating sets, timed like the kernels:
+    # its device time per step beside the eager loop's and the kernels' sum.
+    def step_launch(i, h):
+        b = sets[i % len(sets)]
+        for fn in ops.values():
+            fn(b, h)
+    step_graph_ms = time_graph(torch, step_launch, 2 * len(sets))
+    log(f"  step as one graph: {step_graph_ms * 1e3:.2f} us")
     same_ms = time_graph(torch, lambda i, h: same_traffic(sets[i % len(sets)], h), 2 * len(sets))
     same_gbs = (M * K * 3) / (same_ms * 1e-3) / 1e9
     log(f"  same-traffic probe: {same_ms * 1e3:.2f} us = {same_gbs:.0f} GB/s")
@@ -993,6 +1002,11 @@ def main():
             "traffic": traffic_from_profile("gemm_ptpc4096"),
         },
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kms.items()},
+        "step_graph": {"us": round(step_graph_ms * 1e3, 3),
+                       "tflops": round(flops / (step_graph_ms * 1e-3) / 1e12, 2),
+                       "sum_of_step_kernels_us": round(sum(kms[k] for k in ops) * 1e3, 3),
+                       "what": "the step's three launches captured as one HIP graph of 16 steps over the rotating "
+                               "sets, timed like the kernels (device time per step, no host launch overhead)"},
         "kernel_timing": {"method": "HIP graph of launches over the rotating sets on torch's current stream, "
                                     "HIP events around the timed replays",
                           "launches_per_replay": 2 * args.rotate,
