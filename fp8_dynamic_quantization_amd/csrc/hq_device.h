@@ -49,10 +49,13 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, (int)old, HI);
 }
 
-// Four floats -> four codes in one dword (element i in byte i).
+// Four floats -> four codes in one dword (element i in byte i). The two
+// conversions fill the low and then the high half of one register, so its
+// starting value never reaches the result; passing a register the caller no
+// longer needs (`dead`) saves the move that zeroes a fresh one.
 template <int FMT, bool CLAMP = true>
-__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-  uint32_t w = cvt2<FMT, false, CLAMP>(a, b, 0u);
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d, uint32_t dead = 0u) {
+  uint32_t w = cvt2<FMT, false, CLAMP>(a, b, dead);
   return cvt2<FMT, true, CLAMP>(c, d, w);
 }
 
@@ -124,7 +127,8 @@ __device__ __forceinline__ void vec_cast(const uint4& v, float r, bool patch, ui
     const float b = vec_elem<XT>(v, 4 * d + 1) * r;
     const float c = vec_elem<XT>(v, 4 * d + 2) * r;
     const float e = vec_elem<XT>(v, 4 * d + 3) * r;
-    uint32_t w = cvt4<FMT, CLAMP>(a, b, c, e);
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};  // element 4d's input word, dead after the widening
+    uint32_t w = cvt4<FMT, CLAMP>(a, b, c, e, in[d]);
     if (patch) w = patch_nan4(w, a, b, c, e);
     out[d] = w;
   }
