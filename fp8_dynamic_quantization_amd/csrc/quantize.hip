@@ -147,6 +147,10 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
       mx = max(mx, raw[j]);
     }
     mx = wave_max_u32(mx);
+    // a full row (every lane holds NV whole vectors) without Inf or NaN, scaled
+    // by its own amax: no bounds check, no NaN patch and no clamp per vector
+    // (bf16 [4096, 4096]: 9.335 -> 9.135 us in interleaved rounds on one box)
+    const bool full_finite = !SR && mx < kInfBits && vpr == 64 * NV;  // wavefront-uniform
     if (mx >= kInfBits) {  // the row holds an Inf/NaN: recompute over finite elements
       uint32_t f = 0;
 #pragma unroll
@@ -161,13 +165,22 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quant_rows_wave_kernel(
       if (amax_out) amax_out[row] = amax;
     }
     uint8_t* qr = q + (size_t)row * vpr * E;
+    if (full_finite) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int i = lane + 64 * j;
-      if (i < vpr) {
+      for (int j = 0; j < NV; ++j) {
         uint32_t w[E / 4];
-        cast_vec<XT, FMT, SR, true>(cur[j], r, raw[j], w, sd, ((size_t)row * vpr + i) * E);
-        store_codes<E>(qr + (size_t)i * E, w);
+        vec_cast<XT, FMT, false>(cur[j], r, false, w);
+        store_codes<E>(qr + (size_t)(lane + 64 * j) * E, w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int i = lane + 64 * j;
+        if (i < vpr) {
+          uint32_t w[E / 4];
+          cast_vec<XT, FMT, SR, true>(cur[j], r, raw[j], w, sd, ((size_t)row * vpr + i) * E);
+          store_codes<E>(qr + (size_t)i * E, w);
+        }
       }
     }
 #pragma unroll
@@ -1146,6 +1159,9 @@ __global__ __launch_bounds__(64 * kPreWaves) void quant_rows_pre_group_kernel(
     mx = max(mx, raw[j]);
   }
   mx = wave_max_u32(mx);
+  // a valid, full row (NV whole vectors per lane, K a multiple of 128) without
+  // Inf or NaN: no bounds checks, no NaN patch and no clamp per vector
+  const bool full_finite = valid && mx < kInfBits && vpr == 64 * NV && vpp == vpr;  // wavefront-uniform
   if (mx >= kInfBits) {  // the row holds an Inf/NaN: recompute over finite elements
     uint32_t f = 0;
 #pragma unroll
@@ -1159,21 +1175,35 @@ __global__ __launch_bounds__(64 * kPreWaves) void quant_rows_pre_group_kernel(
     scale[row] = s;
     if (amax_out) amax_out[row] = amax;
   }
+  auto stage_codes = [&](int i, const uint32_t* w) {
+    const int c0 = i * E, kin = c0 & 127;
+    const int L = ((c0 >> 7) * 2 + ((kin >> 4) & 1)) * 4 + (kin >> 5);
+    store_codes_temporal<E>(stage + L * 128 + (((s8 + L) & 7) << 4) + (kin & 15), w);
+  };
+  if (full_finite) {
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int i = lane + 64 * j;
-    if (i < vpp) {
+    for (int j = 0; j < NV; ++j) {
+      const int i = lane + 64 * j;
       uint32_t w[E / 4];
-      if (valid && i < vpr) {
-        cast_vec<XT, FMT, false, true>(cur[j], r, raw[j], w, sd, 0);
-        if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
-      } else {
+      vec_cast<XT, FMT, false>(cur[j], r, false, w);
+      if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
+      stage_codes(i, w);
+    }
+  } else {
 #pragma unroll
-        for (int d = 0; d < E / 4; ++d) w[d] = 0u;
+    for (int j = 0; j < NV; ++j) {
+      const int i = lane + 64 * j;
+      if (i < vpp) {
+        uint32_t w[E / 4];
+        if (valid && i < vpr) {
+          cast_vec<XT, FMT, false, true>(cur[j], r, raw[j], w, sd, 0);
+          if (q) store_codes<E>(q + ((size_t)row * vpr + i) * E, w);
+        } else {
+#pragma unroll
+          for (int d = 0; d < E / 4; ++d) w[d] = 0u;
+        }
+        stage_codes(i, w);
       }
-      const int c0 = i * E, kin = c0 & 127;
-      const int L = ((c0 >> 7) * 2 + ((kin >> 4) & 1)) * 4 + (kin >> 5);
-      store_codes_temporal<E>(stage + L * 128 + (((s8 + L) & 7) << 4) + (kin & 15), w);
     }
   }
   __syncthreads();
