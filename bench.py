@@ -843,7 +843,7 @@ def main():
                          "context, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (this build has no multi-GPU "
+        print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (this library has no multi-GPU "
               "path; run it with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
